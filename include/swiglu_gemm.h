@@ -1,0 +1,142 @@
+/*
+ * swiglu_gemm.h -- C ABI of the MI355X (gfx950) GEMM / fused SwiGLU-GEMM library
+ * (libswiglu_gemm.so).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All matrix pointers are DEVICE pointers owned by the caller; the library keeps
+ *   no pointer after the enqueued work has finished.  Matrices are row-major with
+ *   a leading dimension (the distance, in elements, between the starts of two
+ *   consecutive stored rows).
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *   call is asynchronous: it enqueues kernels on `stream` and returns without
+ *   synchronising.
+ * - Return value: 0 on success; -i when argument i (1-based) is invalid, checked
+ *   before any HIP call; a positive hipError_t when a HIP call failed.  Nothing is
+ *   printed and nothing aborts.
+ * - Output buffers must not overlap input buffers.
+ * - dtype codes: SG_F32 = 0, SG_F16 = 1, SG_BF16 = 2, SG_F8E4M3 = 3 (OCP e4m3fn:
+ *   bias 7, largest magnitude 448, no infinities).  Every product is accumulated
+ *   in fp32 and rounded to the output type (nearest-even) once, at the end.
+ * - Split-K workspace (fp32 partial sums) is owned by the library: one buffer per
+ *   device, grown on first need, released by sg_release().  Calls that need it and
+ *   run concurrently on different streams of one device are serialised by the
+ *   caller (the library does not order streams).
+ */
+#ifndef SWIGLU_GEMM_H
+#define SWIGLU_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SG_F32 = 0,
+    SG_F16 = 1,
+    SG_BF16 = 2,
+    SG_F8E4M3 = 3
+} sg_dtype;
+
+/*
+ * sg_gemm: C = alpha * op(A) * op(B) + beta * C_old.
+ *
+ * The BLAS update of "GEMM o Coração Matemático" §1 (op is the identity or the
+ * transpose; alpha and beta scalars), row-major as in its §2.
+ *
+ *  1 transA  'N'/'n': op(A) = A, A stored M x K (lda >= max(1,K));
+ *            'T'/'t': op(A) = A^T, A stored K x M (lda >= max(1,M)).
+ *  2 transB  'N'/'n': op(B) = B, B stored K x N (ldb >= max(1,N));
+ *            'T'/'t': op(B) = B^T, B stored N x K (ldb >= max(1,K)).
+ *  3 M, 4 N, 5 K   sizes of op(A) (M x K), op(B) (K x N) and C (M x N); >= 0.
+ *  6 alpha   fp32 scalar.
+ *  7 A, 8 lda, 9 B, 10 ldb   operands (see above).
+ *  11 beta   fp32 scalar.  beta == 0: C is write-only (C_old is never read, so
+ *            NaN/Inf there cannot propagate).
+ *  12 C, 13 ldc   M x N output, ldc >= max(1,N).  Elements outside the logical
+ *            M x N block (the ld padding) are never written.
+ *  14 dtype  SG_F32: A, B, C fp32.  SG_F16 / SG_BF16: A, B, C in that type.
+ *            SG_F8E4M3: A, B e4m3 codes, C bf16; per-tensor scales are folded
+ *            into alpha by the caller (alpha = s_A * s_B * alpha').
+ *  15 stream hipStream_t (void*).
+ * Quick returns: M == 0 or N == 0 does nothing; K == 0 or alpha == 0 computes
+ * C = beta * C_old without reading A or B.
+ * Invalid: trans flag (-1/-2), negative size (-3/-4/-5), NULL A/B when they are
+ * read (-7/-9), ld too small (-8/-10/-13), NULL C (-12), unknown dtype (-14).
+ */
+int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K,
+            float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+            float beta, void* C, int64_t ldc, int dtype, void* stream);
+
+/*
+ * sg_swiglu_gemm: Y = SiLU(s * A * W1) ⊙ (s * A * W2), s = scale_a * scale_w.
+ *
+ * The gated MLP of "Resumo Técnico: Sobreposição de Ativação em Nível de Tile para
+ * Inferência Eficiente de LLM" (Definição do Problema), computed as ONE GEMM over
+ * [M, 2N, K] on the column-interleaved W_fused of its Metodologia / Kernel-2 (even
+ * columns gate = W1, odd columns up = W2); the epilogue pairs columns (2n, 2n+1)
+ * in registers, so the gate and up intermediates never reach memory.
+ * SiLU(x) = x / (1 + e^-x).  The scales are the per-tensor dequantisation factors
+ * (value = s * code, zero point 0) of "GEMM o Coração Matemático" §12.4, applied
+ * to the fp32 sums before SiLU.
+ *
+ *  1 A       M x K, contiguous (ld = K).
+ *  2 Wfused  K x 2N, contiguous (ld = 2N).
+ *  3 Y       M x N, contiguous (ld = N).
+ *  4 M, 5 N, 6 K   >= 0.
+ *  7 dtype   SG_BF16: A, W bf16, Y bf16.  SG_F16: A, W fp16, Y fp16.
+ *            SG_F8E4M3: A, W e4m3 codes, Y bf16.
+ *  8 scale_a, 9 scale_w   fp32 per-tensor scales; finite and > 0; must be 1.0
+ *            unless dtype is SG_F8E4M3.
+ *  10 stream hipStream_t (void*).
+ * Quick returns: M == 0 or N == 0 does nothing; K == 0 writes Y = 0.
+ * Invalid: NULL pointer (-1/-2/-3), negative size (-4/-5/-6), unsupported dtype
+ * (-7), bad scale (-8/-9).
+ */
+int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y,
+                   int64_t M, int64_t N, int64_t K, int dtype,
+                   float scale_a, float scale_w, void* stream);
+
+/*
+ * sg_interleave_gate_up: Wfused[k, 2n] = W1[k, n], Wfused[k, 2n+1] = W2[k, n]
+ * (the W_fused layout of the same page's Kernel-2).  Bit-exact copy.
+ *  1 W1, 2 W2   K x N contiguous; 3 Wfused  K x 2N contiguous;
+ *  4 K, 5 N >= 0; 6 dtype any sg_dtype (element size 4, 2, 2 or 1 bytes);
+ *  7 stream.
+ * Invalid: NULL pointer (-1/-2/-3), negative size (-4/-5), unknown dtype (-6).
+ */
+int sg_interleave_gate_up(const void* W1, const void* W2, void* Wfused,
+                          int64_t K, int64_t N, int dtype, void* stream);
+
+/*
+ * sg_silu_mul: Y = SiLU(G) ⊙ U, elementwise over M x N contiguous matrices (the
+ * separate activation step of the unfused MLP that the same page's Definição do
+ * Problema describes: two GEMMs write Gate and Up to memory, then this reads them).
+ *  1 G, 2 U, 3 Y   M x N contiguous, dtype SG_BF16 or SG_F16 (all three);
+ *  4 M, 5 N >= 0; 6 dtype; 7 stream.
+ * Invalid: NULL pointer (-1/-2/-3), negative size (-4/-5), unsupported dtype (-6).
+ */
+int sg_silu_mul(const void* G, const void* U, void* Y, int64_t M, int64_t N,
+                int dtype, void* stream);
+
+/* Text for a status code returned by any sg_* call (static storage). */
+const char* sg_status_string(int status);
+
+/*
+ * Describes the kernel configuration chosen by the most recent successful
+ * sg_gemm / sg_swiglu_gemm call on the calling thread (tile, split count) as a
+ * NUL-terminated string copied into buf (at most len bytes).  Returns the full
+ * length of the description.
+ */
+int sg_last_config(char* buf, int len);
+
+/* Frees the library-owned split-K workspace on every device.  Must not be called
+ * while enqueued work that uses it is still running. */
+void sg_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_GEMM_H */

@@ -1,0 +1,475 @@
+// api.hip -- the C ABI of libswiglu_gemm.so: argument validation, kernel choice,
+// split-K workspace and launches on the caller's stream.  Declarations and the
+// contract of every entry point are in include/swiglu_gemm.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "aux_kernels.hpp"
+#include "gemm16.hpp"
+#include "swiglu_gemm.h"
+
+using namespace sg;
+
+namespace {
+
+constexpr int kNumCU = 256;               // MI355X: 256 compute units in 8 XCDs
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+thread_local char g_last_cfg[160] = "none";
+
+bool trans_ok(char t) { return t == 'N' || t == 'n' || t == 'T' || t == 't'; }
+bool is_t(char t) { return t == 'T' || t == 't'; }
+bool aligned(const void* p, int bytes) { return ((uintptr_t)p % bytes) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
+
+// ---------------------------------------------------------------- workspace
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+Workspace g_ws[64];
+
+hipError_t workspace(size_t bytes, float** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace& w = g_ws[dev];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return e;
+            e = hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+            if (e != hipSuccess) return e;
+        }
+        size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
+        e = hipMalloc(&w.ptr, want);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return e;
+        }
+        w.bytes = want;
+    }
+    *out = reinterpret_cast<float*>(w.ptr);
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------- configs
+struct Cfg16 {
+    int BM, BN, WM, WN;
+    const char* name;
+};
+// Index = config id (SG_FORCE_CONFIG=<id>[,<splits>] overrides the choice).
+const Cfg16 kCfg16[] = {
+    {256, 256, 2, 2, "256x256x64 4w(128x128)"},
+    {256, 256, 2, 4, "256x256x64 8w(128x64)"},
+    {128, 128, 2, 2, "128x128x64 4w(64x64)"},
+    {128, 256, 1, 4, "128x256x64 4w(128x64)"},
+};
+constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
+
+bool forced_config(int* cfg, int* splits) {
+    const char* s = std::getenv("SG_FORCE_CONFIG");
+    if (!s || !*s) return false;
+    int c = -1, k = 0;
+    if (std::sscanf(s, "%d,%d", &c, &k) < 1) return false;
+    *cfg = c;
+    *splits = k;
+    return true;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Choose a tile config and split count for an M x N x K 16-bit problem.
+void choose16(int64_t M, int64_t N, int64_t K, bool swiglu, int* cfg, int* splits) {
+    int fc = -1, fs = 0;
+    if (forced_config(&fc, &fs) && fc >= 0 && fc < kNumCfg16) {
+        *cfg = fc;
+        *splits = fs > 0 ? fs : 1;
+        return;
+    }
+    (void)swiglu;
+    const int64_t big = cdiv(M, 256) * cdiv(N, 256);
+    int c = big >= kNumCU / 2 ? 0 : 2;
+    const int64_t tiles = cdiv(M, kCfg16[c].BM) * cdiv(N, kCfg16[c].BN);
+    int s = 1;
+    if (tiles < kNumCU && K >= 1024) {
+        s = (int)cdiv(kNumCU, tiles);
+        const int64_t max_s = K / 512;
+        if (s > max_s) s = (int)max_s;
+        if (s < 1) s = 1;
+    }
+    *cfg = c;
+    *splits = s;
+}
+
+template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int WM, int WN>
+hipError_t launch16_cfg(const Gemm16Params& p, int splits, hipStream_t st) {
+    dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)splits);
+    hipLaunchKernelGGL((gemm16_kernel<DT, TA, TB, EPI, BM, BN, WM, WN>), grid, dim3(64 * WM * WN),
+                       0, st, p);
+    return hipGetLastError();
+}
+
+template <int DT, bool TA, bool TB, int EPI>
+hipError_t launch16(int cfg, Gemm16Params p, int splits, hipStream_t st) {
+    const Cfg16& c = kCfg16[cfg];
+    p.tiles_m = (int)cdiv(p.M, c.BM);
+    p.tiles_n = (int)cdiv(p.N, c.BN);
+    p.group_m = 8;
+    switch (cfg) {
+        case 0: return launch16_cfg<DT, TA, TB, EPI, 256, 256, 2, 2>(p, splits, st);
+        case 1: return launch16_cfg<DT, TA, TB, EPI, 256, 256, 2, 4>(p, splits, st);
+        case 2: return launch16_cfg<DT, TA, TB, EPI, 128, 128, 2, 2>(p, splits, st);
+        case 3: return launch16_cfg<DT, TA, TB, EPI, 128, 256, 1, 4>(p, splits, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT, int EPI>
+hipError_t launch16_trans(bool ta, bool tb, int cfg, const Gemm16Params& p, int splits,
+                          hipStream_t st) {
+    if (!ta && !tb) return launch16<DT, false, false, EPI>(cfg, p, splits, st);
+    if (!ta && tb) return launch16<DT, false, true, EPI>(cfg, p, splits, st);
+    if (ta && !tb) return launch16<DT, true, false, EPI>(cfg, p, splits, st);
+    return launch16<DT, true, true, EPI>(cfg, p, splits, st);
+}
+
+unsigned grid_1d(int64_t total) {
+    int64_t b = cdiv(total, 256);
+    if (b > 8 * kNumCU * 4) b = 8 * kNumCU * 4;
+    if (b < 1) b = 1;
+    return (unsigned)b;
+}
+
+void set_last(const char* what, int cfg, int splits) {
+    std::snprintf(g_last_cfg, sizeof(g_last_cfg), "%s cfg=%d %s splits=%d", what, cfg,
+                  cfg >= 0 && cfg < kNumCfg16 ? kCfg16[cfg].name : "-", splits);
+}
+
+template <int DT>
+hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
+                  const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                  int64_t ldc, hipStream_t st) {
+    int cfg = 0, splits = 1;
+    choose16(M, N, K, false, &cfg, &splits);
+    Gemm16Params p{};
+    p.A = reinterpret_cast<const uint16_t*>(A);
+    p.B = reinterpret_cast<const uint16_t*>(B);
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.vec_a = aligned(A, 16) && (lda % 8 == 0);
+    p.vec_b = aligned(B, 16) && (ldb % 8 == 0);
+    if (splits > 1) {
+        p.k_per_split = (int)(cdiv(cdiv(K, splits), BK16) * BK16);
+        splits = (int)cdiv(K, p.k_per_split);
+    }
+    if (splits <= 1) {
+        p.C = C;
+        p.vec_c = aligned(C, 8) && (ldc % 4 == 0);
+        p.k_per_split = (int)(cdiv(K, BK16) * BK16);
+        set_last("gemm16", cfg, 1);
+        return launch16_trans<DT, EPI_GEMM>(ta, tb, cfg, p, 1, st);
+    }
+    float* ws = nullptr;
+    hipError_t e = workspace((size_t)splits * M * N * sizeof(float), &ws);
+    if (e != hipSuccess) return e;
+    p.C = ws;
+    p.vec_c = 1;
+    set_last("gemm16", cfg, splits);
+    e = launch16_trans<DT, EPI_PARTIAL>(ta, tb, cfg, p, splits, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_gemm_kernel<DT>, dim3(grid_1d(M * N)), dim3(256), 0, st, ws, splits,
+                       (int)M, (int)N, C, ldc, alpha, beta);
+    return hipGetLastError();
+}
+
+template <bool TA, bool TB>
+hipError_t launch_f32(const GemmF32Params& p, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                       dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
+                    const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                    int64_t ldc, hipStream_t st) {
+    GemmF32Params p{};
+    p.A = reinterpret_cast<const float*>(A);
+    p.B = reinterpret_cast<const float*>(B);
+    p.C = reinterpret_cast<float*>(C);
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.tiles_m = (int)cdiv(M, 64);
+    p.tiles_n = (int)cdiv(N, 64);
+    std::snprintf(g_last_cfg, sizeof(g_last_cfg), "gemm_f32 64x64x16 mfma32x32x2 splits=1");
+    if (!ta && !tb) return launch_f32<false, false>(p, st);
+    if (!ta && tb) return launch_f32<false, true>(p, st);
+    if (ta && !tb) return launch_f32<true, false>(p, st);
+    return launch_f32<true, true>(p, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
+            const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+            int64_t ldc, int dtype, void* stream) {
+    if (!trans_ok(transA)) return -1;
+    if (!trans_ok(transB)) return -2;
+    if (M < 0 || M > kMaxDim) return -3;
+    if (N < 0 || N > kMaxDim) return -4;
+    if (K < 0 || K > kMaxDim) return -5;
+    const bool ta = is_t(transA), tb = is_t(transB);
+    const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
+    if (reads_ab && !A) return -7;
+    {
+        const int64_t need = ta ? M : K;
+        if (lda < (need > 1 ? need : 1)) return -8;
+    }
+    if (reads_ab && !B) return -9;
+    {
+        const int64_t need = tb ? K : N;
+        if (ldb < (need > 1 ? need : 1)) return -10;
+    }
+    if (M > 0 && N > 0 && !C) return -12;
+    if (ldc < (N > 1 ? N : 1)) return -13;
+    if (dtype < SG_F32 || dtype > SG_F8E4M3) return -14;
+    if ((int64_t)M * N > ((int64_t)1 << 40)) return -3;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (M == 0 || N == 0) return 0;
+
+    if (!reads_ab) {
+        std::snprintf(g_last_cfg, sizeof(g_last_cfg), "scale_only");
+        const unsigned g = grid_1d(M * N);
+        switch (dtype) {
+            case SG_F32:
+                hipLaunchKernelGGL(scale_kernel<DT_F32>, dim3(g), dim3(256), 0, st, C, ldc,
+                                   (int)M, (int)N, beta);
+                break;
+            case SG_F16:
+                hipLaunchKernelGGL(scale_kernel<DT_F16>, dim3(g), dim3(256), 0, st, C, ldc,
+                                   (int)M, (int)N, beta);
+                break;
+            default:  // bf16 output (SG_BF16 and SG_F8E4M3)
+                hipLaunchKernelGGL(scale_kernel<DT_BF16>, dim3(g), dim3(256), 0, st, C, ldc,
+                                   (int)M, (int)N, beta);
+                break;
+        }
+        return status_of(hipGetLastError());
+    }
+
+    hipError_t e;
+    switch (dtype) {
+        case SG_F32:
+            e = gemm_f32(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
+            break;
+        case SG_F16:
+            e = gemm16<DT_F16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
+            break;
+        case SG_BF16:
+            e = gemm16<DT_BF16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
+            break;
+        default:
+            return -14;  // e4m3 GEMM: not built yet
+    }
+    return status_of(e);
+}
+
+int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_t N, int64_t K,
+                   int dtype, float scale_a, float scale_w, void* stream) {
+    if (!A) return -1;
+    if (!Wfused) return -2;
+    if (!Y) return -3;
+    if (M < 0 || M > kMaxDim) return -4;
+    if (N < 0 || N > kMaxDim / 2) return -5;
+    if (K < 0 || K > kMaxDim) return -6;
+    if (dtype != SG_BF16 && dtype != SG_F16 && dtype != SG_F8E4M3) return -7;
+    if (!std::isfinite(scale_a) || !(scale_a > 0.0f)) return -8;
+    if (!std::isfinite(scale_w) || !(scale_w > 0.0f)) return -9;
+    if (dtype != SG_F8E4M3 && scale_a != 1.0f) return -8;
+    if (dtype != SG_F8E4M3 && scale_w != 1.0f) return -9;
+    if (dtype == SG_F8E4M3) return -7;  // not built yet
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (M == 0 || N == 0) return 0;
+    const int out_dt = dtype == SG_F16 ? SG_F16 : SG_BF16;
+    if (K == 0) {
+        std::snprintf(g_last_cfg, sizeof(g_last_cfg), "swiglu K=0 zero fill");
+        const unsigned g = grid_1d(M * N);
+        if (out_dt == SG_F16)
+            hipLaunchKernelGGL(scale_kernel<DT_F16>, dim3(g), dim3(256), 0, st, Y, N, (int)M,
+                               (int)N, 0.0f);
+        else
+            hipLaunchKernelGGL(scale_kernel<DT_BF16>, dim3(g), dim3(256), 0, st, Y, N, (int)M,
+                               (int)N, 0.0f);
+        return status_of(hipGetLastError());
+    }
+    const int64_t N2 = 2 * N;
+    int cfg = 0, splits = 1;
+    choose16(M, N2, K, true, &cfg, &splits);
+    Gemm16Params p{};
+    p.A = reinterpret_cast<const uint16_t*>(A);
+    p.B = reinterpret_cast<const uint16_t*>(Wfused);
+    p.lda = K;
+    p.ldb = N2;
+    p.ldc = N;
+    p.M = (int)M;
+    p.N = (int)N2;
+    p.K = (int)K;
+    p.alpha = scale_a * scale_w;
+    p.beta = 0.0f;
+    p.vec_a = aligned(A, 16) && (K % 8 == 0);
+    p.vec_b = aligned(Wfused, 16) && (N2 % 8 == 0);
+    if (splits > 1) {
+        p.k_per_split = (int)(cdiv(cdiv(K, splits), BK16) * BK16);
+        splits = (int)cdiv(K, p.k_per_split);
+    }
+    hipError_t e;
+    if (splits <= 1) {
+        p.C = Y;
+        p.vec_c = aligned(Y, 8) && (N % 4 == 0);
+        p.k_per_split = (int)(cdiv(K, BK16) * BK16);
+        set_last("swiglu16", cfg, 1);
+        if (out_dt == SG_F16)
+            e = launch16<DT_F16, false, false, EPI_SWIGLU>(cfg, p, 1, st);
+        else
+            e = launch16<DT_BF16, false, false, EPI_SWIGLU>(cfg, p, 1, st);
+        return status_of(e);
+    }
+    float* ws = nullptr;
+    e = workspace((size_t)splits * M * N2 * sizeof(float), &ws);
+    if (e != hipSuccess) return status_of(e);
+    p.C = ws;
+    p.vec_c = 1;
+    set_last("swiglu16", cfg, splits);
+    if (out_dt == SG_F16)
+        e = launch16<DT_F16, false, false, EPI_PARTIAL>(cfg, p, splits, st);
+    else
+        e = launch16<DT_BF16, false, false, EPI_PARTIAL>(cfg, p, splits, st);
+    if (e != hipSuccess) return status_of(e);
+    const unsigned g = grid_1d(M * N);
+    if (out_dt == SG_F16)
+        hipLaunchKernelGGL(reduce_swiglu_kernel<DT_F16>, dim3(g), dim3(256), 0, st, ws, splits,
+                           (int)M, (int)N, reinterpret_cast<uint16_t*>(Y), p.alpha);
+    else
+        hipLaunchKernelGGL(reduce_swiglu_kernel<DT_BF16>, dim3(g), dim3(256), 0, st, ws, splits,
+                           (int)M, (int)N, reinterpret_cast<uint16_t*>(Y), p.alpha);
+    return status_of(hipGetLastError());
+}
+
+int sg_interleave_gate_up(const void* W1, const void* W2, void* Wfused, int64_t K, int64_t N,
+                          int dtype, void* stream) {
+    if (!W1) return -1;
+    if (!W2) return -2;
+    if (!Wfused) return -3;
+    if (K < 0) return -4;
+    if (N < 0) return -5;
+    if (dtype < SG_F32 || dtype > SG_F8E4M3) return -6;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int64_t total = K * N;
+    if (total == 0) return 0;
+    const unsigned g = grid_1d(total);
+    switch (dtype) {
+        case SG_F32:
+            hipLaunchKernelGGL(interleave_kernel<uint32_t>, dim3(g), dim3(256), 0, st,
+                               (const uint32_t*)W1, (const uint32_t*)W2, (uint32_t*)Wfused, total);
+            break;
+        case SG_F8E4M3:
+            hipLaunchKernelGGL(interleave_kernel<uint8_t>, dim3(g), dim3(256), 0, st,
+                               (const uint8_t*)W1, (const uint8_t*)W2, (uint8_t*)Wfused, total);
+            break;
+        default:
+            hipLaunchKernelGGL(interleave_kernel<uint16_t>, dim3(g), dim3(256), 0, st,
+                               (const uint16_t*)W1, (const uint16_t*)W2, (uint16_t*)Wfused, total);
+            break;
+    }
+    return status_of(hipGetLastError());
+}
+
+int sg_silu_mul(const void* G, const void* U, void* Y, int64_t M, int64_t N, int dtype,
+                void* stream) {
+    if (!G) return -1;
+    if (!U) return -2;
+    if (!Y) return -3;
+    if (M < 0) return -4;
+    if (N < 0) return -5;
+    if (dtype != SG_BF16 && dtype != SG_F16) return -6;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int64_t total = M * N;
+    if (total == 0) return 0;
+    const int vec = aligned(G, 16) && aligned(U, 16) && aligned(Y, 16);
+    const unsigned g = grid_1d(vec ? cdiv(total, 8) : total);
+    if (dtype == SG_F16)
+        hipLaunchKernelGGL(silu_mul_kernel<DT_F16>, dim3(g), dim3(256), 0, st, (const uint16_t*)G,
+                           (const uint16_t*)U, (uint16_t*)Y, total, vec);
+    else
+        hipLaunchKernelGGL(silu_mul_kernel<DT_BF16>, dim3(g), dim3(256), 0, st,
+                           (const uint16_t*)G, (const uint16_t*)U, (uint16_t*)Y, total, vec);
+    return status_of(hipGetLastError());
+}
+
+const char* sg_status_string(int status) {
+    static const char* const kArg[] = {
+        "success",         "invalid argument 1", "invalid argument 2",  "invalid argument 3",
+        "invalid argument 4", "invalid argument 5", "invalid argument 6", "invalid argument 7",
+        "invalid argument 8", "invalid argument 9", "invalid argument 10",
+        "invalid argument 11", "invalid argument 12", "invalid argument 13",
+        "invalid argument 14", "invalid argument 15"};
+    if (status <= 0 && status >= -15) return kArg[-status];
+    if (status < 0) return "invalid argument";
+    return hipGetErrorString(static_cast<hipError_t>(status));
+}
+
+int sg_last_config(char* buf, int len) {
+    const int n = (int)std::strlen(g_last_cfg);
+    if (buf && len > 0) {
+        std::strncpy(buf, g_last_cfg, (size_t)len - 1);
+        buf[len - 1] = '\0';
+    }
+    return n;
+}
+
+void sg_release(void) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+    for (int d = 0; d < 64; ++d) {
+        if (g_ws[d].ptr) {
+            if (hipSetDevice(d) == hipSuccess) {
+                (void)hipDeviceSynchronize();
+                (void)hipFree(g_ws[d].ptr);
+            }
+            g_ws[d].ptr = nullptr;
+            g_ws[d].bytes = 0;
+        }
+    }
+    if (cur >= 0) (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

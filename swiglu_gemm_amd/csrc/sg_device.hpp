@@ -1,0 +1,70 @@
+// sg_device.hpp -- device-side types and helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3 };
+enum : int { EPI_GEMM = 0, EPI_SWIGLU = 1, EPI_PARTIAL = 2 };
+
+// ---------------------------------------------------------------------------
+// 16-bit storage <-> fp32
+// ---------------------------------------------------------------------------
+template <int DT> __device__ __forceinline__ float to_f32(uint16_t b);
+template <> __device__ __forceinline__ float to_f32<DT_F16>(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+template <> __device__ __forceinline__ float to_f32<DT_BF16>(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+// round-to-nearest-even conversions (v_cvt_f16_f32 / v_cvt_pk_bf16_f32)
+template <int DT> __device__ __forceinline__ uint16_t from_f32(float x);
+template <> __device__ __forceinline__ uint16_t from_f32<DT_F16>(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <> __device__ __forceinline__ uint16_t from_f32<DT_BF16>(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// SiLU(x) = x / (1 + e^-x); e^-x -> +inf for very negative x gives -0, never NaN.
+__device__ __forceinline__ float silu(float x) {
+    return x / (1.0f + __expf(-x));
+}
+
+// ---------------------------------------------------------------------------
+// XCD-aware block order.  Work-groups are handed to the 8 XCDs round-robin
+// (block b runs on XCD b % 8); remap so that consecutive logical tiles share an
+// XCD (and so its L2).  Bijective for any count.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    constexpr int NXCD = 8;
+    if (nblocks < NXCD) return bid;
+    const int per = nblocks / NXCD, rem = nblocks % NXCD;
+    const int xcd = bid % NXCD, idx = bid / NXCD;
+    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+// Grouped ("super-tile") order: walk GROUP_M tile-rows at a time so the tiles in
+// flight share A rows and B columns.
+__device__ __forceinline__ void tile_coords(int lid, int tiles_m, int tiles_n, int group_m,
+                                            int& tm, int& tn) {
+    const int per_group = group_m * tiles_n;
+    const int g = lid / per_group;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int r = lid - g * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+}  // namespace sg

@@ -1,0 +1,109 @@
+"""Host-only checks of the C ABI: the library loads, exports every function that
+include/swiglu_gemm.h declares, and rejects invalid arguments with the documented
+negative status before making any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+
+import pytest
+
+import swiglu_gemm_amd as sg
+from swiglu_gemm_amd import build as sgbuild
+
+
+@pytest.fixture(scope="module")
+def L():
+    if sgbuild.is_stale():
+        sgbuild.build()
+    return sg.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = sg.declared_symbols()
+    assert set(names) >= {"sg_gemm", "sg_swiglu_gemm", "sg_interleave_gate_up", "sg_silu_mul",
+                          "sg_status_string", "sg_last_config", "sg_release"}
+    for n in names:
+        assert hasattr(L, n), "libswiglu_gemm.so does not export %s" % n
+
+
+def test_no_torch_types_in_header():
+    text = open(sg.HEADER).read()
+    assert "torch" not in text.lower().replace("torch tensors", "")
+    assert 'extern "C"' in text
+
+
+P = ctypes.c_void_p(0x1000)     # never dereferenced: every call below fails validation
+NUL = ctypes.c_void_p(0)
+
+
+def gemm(L, ta=b"N", tb=b"N", M=2, N=2, K=2, alpha=1.0, A=P, lda=2, B=P, ldb=2, beta=0.0, C=P,
+         ldc=2, dtype=0):
+    return L.sg_gemm(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, NUL)
+
+
+def test_gemm_argument_validation(L):
+    assert gemm(L, ta=b"X") == -1
+    assert gemm(L, tb=b"C") == -2
+    assert gemm(L, M=-1) == -3
+    assert gemm(L, N=-1) == -4
+    assert gemm(L, K=-1) == -5
+    assert gemm(L, A=NUL) == -7
+    assert gemm(L, lda=1) == -8                       # 'N': lda >= K
+    assert gemm(L, ta=b"T", M=3, lda=2) == -8         # 'T': lda >= M
+    assert gemm(L, B=NUL) == -9
+    assert gemm(L, ldb=1) == -10                      # 'N': ldb >= N
+    assert gemm(L, tb=b"t", K=3, lda=3, ldb=2) == -10  # 'T': ldb >= K
+    assert gemm(L, C=NUL) == -12
+    assert gemm(L, ldc=1) == -13
+    assert gemm(L, dtype=7) == -14
+    # quick returns never touch the device
+    assert gemm(L, M=0, A=NUL, B=NUL, C=NUL) == 0
+    assert gemm(L, N=0, A=NUL, B=NUL, C=NUL, ldb=1, ldc=1) == 0
+
+
+def test_swiglu_argument_validation(L):
+    def sw(A=P, W=P, Y=P, M=2, N=2, K=2, dt=2, sa=1.0, sw_=1.0):
+        return L.sg_swiglu_gemm(A, W, Y, M, N, K, dt, sa, sw_, NUL)
+    assert sw(A=NUL) == -1
+    assert sw(W=NUL) == -2
+    assert sw(Y=NUL) == -3
+    assert sw(M=-1) == -4
+    assert sw(N=-1) == -5
+    assert sw(K=-1) == -6
+    assert sw(dt=0) == -7
+    assert sw(dt=3, sa=0.0) == -8
+    assert sw(dt=3, sa=float("inf")) == -8
+    assert sw(dt=3, sw_=float("nan")) == -9
+    assert sw(dt=2, sa=2.0) == -8                    # scales must be 1 for bf16
+    assert sw(M=0) == 0
+
+
+def test_other_entry_points_validation(L):
+    assert L.sg_interleave_gate_up(NUL, P, P, 1, 1, 2, NUL) == -1
+    assert L.sg_interleave_gate_up(P, P, P, -1, 1, 2, NUL) == -4
+    assert L.sg_interleave_gate_up(P, P, P, 1, 1, 9, NUL) == -6
+    assert L.sg_interleave_gate_up(P, P, P, 0, 5, 2, NUL) == 0
+    assert L.sg_silu_mul(P, P, NUL, 1, 1, 2, NUL) == -3
+    assert L.sg_silu_mul(P, P, P, 1, 1, 0, NUL) == -6
+
+
+def test_status_strings(L):
+    assert sg.status_string(0) == "success"
+    assert sg.status_string(-8) == "invalid argument 8"
+    assert isinstance(sg.last_config(), str)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(sg, "_lib", None)
+    monkeypatch.setattr(sg, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(sg.SwigluGemmError):
+        sg.lib()
+
+
+def test_product_path_does_not_import_oracle():
+    here = os.path.dirname(sg.__file__)
+    for root, _, files in os.walk(here):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(root, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "oracle." not in text.replace(
+                    "the oracle", ""), f
