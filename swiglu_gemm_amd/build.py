@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libswiglu_gemm.so")
-SOURCES = ["api.hip"]
+SOURCES = ["api.hip", "inst_f16.hip", "inst_bf16.hip"]
 ARCH = "gfx950"
 
 
@@ -24,23 +24,38 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def compile_cmd(out: str, extra=()) -> list:
-    return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-shared", "-fPIC",
+def _flags() -> list:
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             # packed-fp32 VALU ops are kept out of the generated code on purpose
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-I", CSRC, "-o", out] + list(extra) + \
-        [os.path.join(CSRC, s) for s in SOURCES]
+            "-I", INCLUDE, "-I", CSRC]
 
 
 def build(verbose: bool = False) -> str:
+    """Compile each translation unit in parallel, then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed on %s" % src)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = compile_cmd(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libswiglu_gemm.so")
+        raise RuntimeError("hipcc failed linking libswiglu_gemm.so")
     os.replace(tmp, LIB)
     return LIB
 

@@ -13,10 +13,22 @@
 #include <string>
 
 #include "aux_kernels.hpp"
-#include "gemm16.hpp"
+#include "configs16.hpp"
+#include "sg_device.hpp"
 #include "swiglu_gemm.h"
 
 using namespace sg;
+
+namespace sg {
+// defined in inst_f16.hip / inst_bf16.hip
+template <int DT>
+hipError_t launch16_dt(bool ta, bool tb, int epi, int cfg, const Gemm16Params& p, int splits,
+                       hipStream_t st);
+extern template hipError_t launch16_dt<DT_F16>(bool, bool, int, int, const Gemm16Params&, int,
+                                               hipStream_t);
+extern template hipError_t launch16_dt<DT_BF16>(bool, bool, int, int, const Gemm16Params&, int,
+                                                hipStream_t);
+}  // namespace sg
 
 namespace {
 
@@ -68,19 +80,6 @@ hipError_t workspace(size_t bytes, float** out) {
 }
 
 // ---------------------------------------------------------------- configs
-struct Cfg16 {
-    int BM, BN, WM, WN;
-    const char* name;
-};
-// Index = config id (SG_FORCE_CONFIG=<id>[,<splits>] overrides the choice).
-const Cfg16 kCfg16[] = {
-    {256, 256, 2, 2, "256x256x64 4w(128x128)"},
-    {256, 256, 2, 4, "256x256x64 8w(128x64)"},
-    {128, 128, 2, 2, "128x128x64 4w(64x64)"},
-    {128, 256, 1, 4, "128x256x64 4w(128x64)"},
-};
-constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
-
 bool forced_config(int* cfg, int* splits) {
     const char* s = std::getenv("SG_FORCE_CONFIG");
     if (!s || !*s) return false;
@@ -93,59 +92,48 @@ bool forced_config(int* cfg, int* splits) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Choose a tile config and split count for an M x N x K 16-bit problem.
-void choose16(int64_t M, int64_t N, int64_t K, bool swiglu, int* cfg, int* splits) {
-    int fc = -1, fs = 0;
-    if (forced_config(&fc, &fs) && fc >= 0 && fc < kNumCfg16) {
-        *cfg = fc;
-        *splits = fs > 0 ? fs : 1;
-        return;
-    }
-    (void)swiglu;
-    const int64_t big = cdiv(M, 256) * cdiv(N, 256);
-    int c = big >= kNumCU / 2 ? 0 : 2;
-    const int64_t tiles = cdiv(M, kCfg16[c].BM) * cdiv(N, kCfg16[c].BN);
+struct Problem16 {
+    int64_t M, N, K;      // N: fused width for SwiGLU
+    bool vec_a, vec_b;    // 16-byte aligned base and ld % 8 == 0
+};
+
+// The DMA kernels need whole tiles and 16-byte aligned rows.
+bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
+    return c.dma && q.vec_a && q.vec_b && q.M % c.BM == 0 && q.N % c.BN == 0 &&
+           q.K % c.BK == 0 && kps % c.BK == 0;
+}
+
+int64_t split_len(int64_t K, int splits) { return cdiv(cdiv(K, splits), 64) * 64; }
+
+int pick_splits(const Cfg16& c, const Problem16& q) {
+    const int64_t tiles = cdiv(q.M, c.BM) * cdiv(q.N, c.BN);
     int s = 1;
-    if (tiles < kNumCU && K >= 1024) {
+    if (tiles < kNumCU && q.K >= 1024) {
         s = (int)cdiv(kNumCU, tiles);
-        const int64_t max_s = K / 512;
+        const int64_t max_s = q.K / 512;
         if (s > max_s) s = (int)max_s;
         if (s < 1) s = 1;
     }
-    *cfg = c;
-    *splits = s;
+    return s;
 }
 
-template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int WM, int WN>
-hipError_t launch16_cfg(const Gemm16Params& p, int splits, hipStream_t st) {
-    dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)splits);
-    hipLaunchKernelGGL((gemm16_kernel<DT, TA, TB, EPI, BM, BN, WM, WN>), grid, dim3(64 * WM * WN),
-                       0, st, p);
-    return hipGetLastError();
-}
-
-template <int DT, bool TA, bool TB, int EPI>
-hipError_t launch16(int cfg, Gemm16Params p, int splits, hipStream_t st) {
-    const Cfg16& c = kCfg16[cfg];
-    p.tiles_m = (int)cdiv(p.M, c.BM);
-    p.tiles_n = (int)cdiv(p.N, c.BN);
-    p.group_m = 8;
-    switch (cfg) {
-        case 0: return launch16_cfg<DT, TA, TB, EPI, 256, 256, 2, 2>(p, splits, st);
-        case 1: return launch16_cfg<DT, TA, TB, EPI, 256, 256, 2, 4>(p, splits, st);
-        case 2: return launch16_cfg<DT, TA, TB, EPI, 128, 128, 2, 2>(p, splits, st);
-        case 3: return launch16_cfg<DT, TA, TB, EPI, 128, 256, 1, 4>(p, splits, st);
-        default: return hipErrorInvalidValue;
+// Choose a configuration and split count; falls back to a register-staged
+// configuration whenever a DMA configuration does not fit the problem.
+void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
+    int cfg = -1, splits = 0;
+    const bool forced = forced_config(&cfg, &splits) && cfg >= 0 && cfg < kNumCfg16;
+    if (!forced) {
+        const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
+        cfg = big >= kNumCU / 2 ? 3 : 6;
+        splits = 0;
     }
-}
-
-template <int DT, int EPI>
-hipError_t launch16_trans(bool ta, bool tb, int cfg, const Gemm16Params& p, int splits,
-                          hipStream_t st) {
-    if (!ta && !tb) return launch16<DT, false, false, EPI>(cfg, p, splits, st);
-    if (!ta && tb) return launch16<DT, false, true, EPI>(cfg, p, splits, st);
-    if (ta && !tb) return launch16<DT, true, false, EPI>(cfg, p, splits, st);
-    return launch16<DT, true, true, EPI>(cfg, p, splits, st);
+    if (splits <= 0) splits = pick_splits(kCfg16[cfg], q);
+    if (kCfg16[cfg].dma && !dma_ok(kCfg16[cfg], q, split_len(q.K, splits))) {
+        cfg = kCfg16[cfg].BM >= 256 ? 1 : 2;
+        if (!forced) splits = pick_splits(kCfg16[cfg], q);
+    }
+    *cfg_out = cfg;
+    *splits_out = splits;
 }
 
 unsigned grid_1d(int64_t total) {
@@ -160,12 +148,42 @@ void set_last(const char* what, int cfg, int splits) {
                   cfg >= 0 && cfg < kNumCfg16 ? kCfg16[cfg].name : "-", splits);
 }
 
+constexpr int BK16 = 64;   // split lengths are multiples of this
+
+template <int DT>
+hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* out,
+                 bool out_vec, const char* what, hipStream_t st, int* splits_used) {
+    int cfg = 0, splits = 1;
+    choose16(q, &cfg, &splits);
+    const Cfg16& c = kCfg16[cfg];
+    p.tiles_m = (int)cdiv(q.M, c.BM);
+    p.tiles_n = (int)cdiv(q.N, c.BN);
+    p.group_m = 8;
+    if (splits > 1) {
+        p.k_per_split = (int)split_len(q.K, splits);
+        splits = (int)cdiv(q.K, p.k_per_split);
+    }
+    *splits_used = splits;
+    if (splits <= 1) {
+        p.C = out;
+        p.vec_c = out_vec;
+        p.k_per_split = (int)(cdiv(q.K, BK16) * BK16);
+        set_last(what, cfg, 1);
+        return launch16_dt<DT>(ta, tb, epi, cfg, p, 1, st);
+    }
+    float* ws = nullptr;
+    hipError_t e = workspace((size_t)splits * q.M * q.N * sizeof(float), &ws);
+    if (e != hipSuccess) return e;
+    p.C = ws;
+    p.vec_c = 1;
+    set_last(what, cfg, splits);
+    return launch16_dt<DT>(ta, tb, EPI_PARTIAL, cfg, p, splits, st);
+}
+
 template <int DT>
 hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
                   const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
                   int64_t ldc, hipStream_t st) {
-    int cfg = 0, splits = 1;
-    choose16(M, N, K, false, &cfg, &splits);
     Gemm16Params p{};
     p.A = reinterpret_cast<const uint16_t*>(A);
     p.B = reinterpret_cast<const uint16_t*>(B);
@@ -179,24 +197,13 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
     p.beta = beta;
     p.vec_a = aligned(A, 16) && (lda % 8 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 8 == 0);
-    if (splits > 1) {
-        p.k_per_split = (int)(cdiv(cdiv(K, splits), BK16) * BK16);
-        splits = (int)cdiv(K, p.k_per_split);
-    }
-    if (splits <= 1) {
-        p.C = C;
-        p.vec_c = aligned(C, 8) && (ldc % 4 == 0);
-        p.k_per_split = (int)(cdiv(K, BK16) * BK16);
-        set_last("gemm16", cfg, 1);
-        return launch16_trans<DT, EPI_GEMM>(ta, tb, cfg, p, 1, st);
-    }
+    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b};
+    int splits = 1;
+    hipError_t e = run16<DT>(ta, tb, EPI_GEMM, q, p, C, aligned(C, 8) && (ldc % 4 == 0), "gemm16",
+                             st, &splits);
+    if (e != hipSuccess || splits <= 1) return e;
     float* ws = nullptr;
-    hipError_t e = workspace((size_t)splits * M * N * sizeof(float), &ws);
-    if (e != hipSuccess) return e;
-    p.C = ws;
-    p.vec_c = 1;
-    set_last("gemm16", cfg, splits);
-    e = launch16_trans<DT, EPI_PARTIAL>(ta, tb, cfg, p, splits, st);
+    e = workspace((size_t)splits * M * N * sizeof(float), &ws);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_gemm_kernel<DT>, dim3(grid_1d(M * N)), dim3(256), 0, st, ws, splits,
                        (int)M, (int)N, C, ldc, alpha, beta);
@@ -331,8 +338,6 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
         return status_of(hipGetLastError());
     }
     const int64_t N2 = 2 * N;
-    int cfg = 0, splits = 1;
-    choose16(M, N2, K, true, &cfg, &splits);
     Gemm16Params p{};
     p.A = reinterpret_cast<const uint16_t*>(A);
     p.B = reinterpret_cast<const uint16_t*>(Wfused);
@@ -346,32 +351,16 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
     p.beta = 0.0f;
     p.vec_a = aligned(A, 16) && (K % 8 == 0);
     p.vec_b = aligned(Wfused, 16) && (N2 % 8 == 0);
-    if (splits > 1) {
-        p.k_per_split = (int)(cdiv(cdiv(K, splits), BK16) * BK16);
-        splits = (int)cdiv(K, p.k_per_split);
-    }
-    hipError_t e;
-    if (splits <= 1) {
-        p.C = Y;
-        p.vec_c = aligned(Y, 8) && (N % 4 == 0);
-        p.k_per_split = (int)(cdiv(K, BK16) * BK16);
-        set_last("swiglu16", cfg, 1);
-        if (out_dt == SG_F16)
-            e = launch16<DT_F16, false, false, EPI_SWIGLU>(cfg, p, 1, st);
-        else
-            e = launch16<DT_BF16, false, false, EPI_SWIGLU>(cfg, p, 1, st);
-        return status_of(e);
-    }
+    Problem16 q{M, N2, K, (bool)p.vec_a, (bool)p.vec_b};
+    // Y stores are 4 or 8 bytes wide depending on the kernel: require the stricter
+    const bool yvec = aligned(Y, 8) && (N % 4 == 0);
+    int splits = 1;
+    hipError_t e = out_dt == SG_F16
+        ? run16<DT_F16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits)
+        : run16<DT_BF16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits);
+    if (e != hipSuccess || splits <= 1) return status_of(e);
     float* ws = nullptr;
     e = workspace((size_t)splits * M * N2 * sizeof(float), &ws);
-    if (e != hipSuccess) return status_of(e);
-    p.C = ws;
-    p.vec_c = 1;
-    set_last("swiglu16", cfg, splits);
-    if (out_dt == SG_F16)
-        e = launch16<DT_F16, false, false, EPI_PARTIAL>(cfg, p, splits, st);
-    else
-        e = launch16<DT_BF16, false, false, EPI_PARTIAL>(cfg, p, splits, st);
     if (e != hipSuccess) return status_of(e);
     const unsigned g = grid_1d(M * N);
     if (out_dt == SG_F16)

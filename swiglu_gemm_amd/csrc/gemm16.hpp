@@ -38,21 +38,11 @@
 
 #include <type_traits>
 
+#include "epilogue16.hpp"
 #include "sg_device.hpp"
 
 namespace sg {
 
-struct Gemm16Params {
-    const uint16_t* A;
-    const uint16_t* B;
-    void* C;            // EPI_GEMM: C (dtype); EPI_SWIGLU: Y; EPI_PARTIAL: fp32 workspace
-    int64_t lda, ldb, ldc;
-    int M, N, K;        // N is the fused width 2*N_out for SwiGLU / its partials
-    float alpha, beta;  // SwiGLU: alpha = scale_a * scale_w
-    int vec_a, vec_b, vec_c;
-    int tiles_m, tiles_n, group_m;
-    int k_per_split;    // a multiple of 64; gridDim.y splits
-};
 
 constexpr int BK16 = 64;
 
@@ -82,6 +72,7 @@ template <int R, int NT>
 struct LoadDirect {
     static constexpr int CH = R * 8 / NT;
     static_assert((R * 8) % NT == 0, "tile rows must split evenly over the threads");
+    static constexpr int NLOAD = CH, NSTORE = CH;   // global loads / LDS stores per thread
     u32x4 v[CH];
 
     __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int r0, int rows,
@@ -114,6 +105,7 @@ template <int R, int NT, bool DEINTERLEAVE>
 struct LoadTrans {
     static constexpr int NB = R;                  // (BK/8) * (R/8) blocks
     static constexpr int BPT = (NB + NT - 1) / NT;
+    static constexpr int NLOAD = BPT * 8, NSTORE = BPT * 8;
     u32x4 v[BPT][8];
 
     __device__ __forceinline__ void load(const uint16_t* base, int64_t ld, int r0, int rows,
@@ -168,16 +160,6 @@ struct LoadTrans {
     }
 };
 
-template <int DT>
-__device__ __forceinline__ f32x16 mfma16(const u32x4& a, const u32x4& b, const f32x16& c) {
-    if constexpr (DT == DT_F16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_kernel(const Gemm16Params p) {
     constexpr int NT = 64 * WM * WN;
@@ -217,167 +199,98 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_kernel(const Gemm16Par
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // Software pipeline over K tiles (two LDS stages, fragments double-buffered
+    // in registers).  Per tile: k-steps 0..2 each read the fragments of the next
+    // k-step while their own MFMAs run; the next tile's global loads are issued
+    // with k-step 0 and written to the other LDS stage with k-step 2; after the
+    // barrier, the MFMAs of k-step 3 overlap the reads of the next tile's first
+    // fragments, so the MFMA pipe stays busy across the barrier.
     if (nkt > 0) {
-        {
-            const bool fast = full_mn && (kbeg + BK16 <= kend);
-            la.load(p.A, p.lda, m0, p.M, kbeg, kend, fast, vec_a);
-            lb.load(p.B, p.ldb, n0, p.N, kbeg, kend, fast, vec_b);
-            la.store(smem);
-            lb.store(smem + A_BYTES);
-        }
-        __syncthreads();
+        const char* const stage0 = smem;
+        const int kfull = full_mn ? (kend - kbeg) / BK16 : 0;   // tiles loadable unguarded
 
-        for (int kt = 0; kt < nkt; ++kt) {
-            const int cur = kt & 1;
-            const bool more = kt + 1 < nkt;
-            if (more) {
-                const int k0 = kbeg + (kt + 1) * BK16;
-                const bool fast = full_mn && (k0 + BK16 <= kend);
-                la.load(p.A, p.lda, m0, p.M, k0, kend, fast, vec_a);
-                lb.load(p.B, p.ldb, n0, p.N, k0, kend, fast, vec_b);
+        u32x4 fa[2][FM], fb[2][FN];
+        auto read_frags = [&](const char* st, int s, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+            const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+            for (int tm = 0; tm < FM; ++tm) {
+                const int row = wm * TM + tm * 32 + (lane & 31);
+                af[tm] = *reinterpret_cast<const u32x4*>(st + lds_off(row, chunk));
             }
-            const char* As = smem + cur * STAGE;
-            const char* Bs = As + A_BYTES;
 #pragma unroll
-            for (int s = 0; s < BK16 / 16; ++s) {
-                const int chunk = 2 * s + (lane >> 5);
-                u32x4 af[FM], bf[FN];
-#pragma unroll
-                for (int tm = 0; tm < FM; ++tm) {
-                    const int row = wm * TM + tm * 32 + (lane & 31);
-                    af[tm] = *reinterpret_cast<const u32x4*>(As + lds_off(row, chunk));
-                }
-#pragma unroll
-                for (int tn = 0; tn < FN; ++tn) {
-                    const int row = wn * TN + tn * 32 + (lane & 31);
-                    bf[tn] = *reinterpret_cast<const u32x4*>(Bs + lds_off(row, chunk));
-                }
-#pragma unroll
-                for (int tn = 0; tn < FN; ++tn)
-#pragma unroll
-                    for (int tm = 0; tm < FM; ++tm)
-                        acc[tn][tm] = mfma16<DT>(bf[tn], af[tm], acc[tn][tm]);
+            for (int tn = 0; tn < FN; ++tn) {
+                const int row = wn * TN + tn * 32 + (lane & 31);
+                bf[tn] = *reinterpret_cast<const u32x4*>(st + A_BYTES + lds_off(row, chunk));
             }
+        };
+        auto mfma_step = [&](const u32x4 (&af)[FM], const u32x4 (&bf)[FN]) {
+#pragma unroll
+            for (int tn = 0; tn < FN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < FM; ++tm)
+                    acc[tn][tm] = mfma16<DT>(bf[tn], af[tm], acc[tn][tm]);
+        };
+        auto load_tile = [&](int t, bool fast) {
+            const int k0 = kbeg + t * BK16;
+            la.load(p.A, p.lda, m0, p.M, k0, kend, fast, vec_a);
+            lb.load(p.B, p.ldb, n0, p.N, k0, kend, fast, vec_b);
+        };
+
+        load_tile(0, kfull > 0);
+        la.store(smem);
+        lb.store(smem + A_BYTES);
+        __syncthreads();
+        read_frags(stage0, 0, fa[0], fb[0]);
+
+        // FAST: the next tile is loaded without guards (branch-free body)
+        constexpr int NMF = FM * FN;           // MFMAs per k-step
+        constexpr int NFR = FM + FN;           // fragment reads per k-step
+        constexpr int NGL = LA::NLOAD + LB::NLOAD;
+        constexpr int NST = LA::NSTORE + LB::NSTORE;
+        auto body = [&](int kt, auto fast_tag) {
+            constexpr bool FAST = decltype(fast_tag)::value;
+            const char* cur = smem + (kt & 1) * STAGE;
+            char* nxt = smem + ((kt & 1) ^ 1) * STAGE;
+            const bool more = FAST || (kt + 1 < nkt);
+            // k-step 0 (+ next tile's global loads)
+            if (FAST) load_tile(kt + 1, true);
+            else if (more) load_tile(kt + 1, false);
+            read_frags(cur, 1, fa[1], fb[1]);
+            mfma_step(fa[0], fb[0]);
+            if (FAST) sched_interleave<NMF, NFR, NGL, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            // k-step 1
+            read_frags(cur, 2, fa[0], fb[0]);
+            mfma_step(fa[1], fb[1]);
+            sched_interleave<NMF, NFR, 0, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+            // k-step 2 (+ the next tile to the other stage)
+            read_frags(cur, 3, fa[1], fb[1]);
+            mfma_step(fa[0], fb[0]);
             if (more) {
-                char* nxt = smem + (cur ^ 1) * STAGE;
                 la.store(nxt);
                 lb.store(nxt + A_BYTES);
             }
+            // LDS reads (this stage) first, then the writes (other stage): the
+            // compiler cannot prove the two stages disjoint, so keep program order
+            if (FAST) {
+                sched_interleave<NMF / 2, NFR, 0, 0>();
+                sched_interleave<NMF - NMF / 2, 0, 0, NST>();
+            }
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
-        }
+            // k-step 3 overlapping the next tile's first fragments
+            if (more) read_frags(nxt, 0, fa[0], fb[0]);
+            mfma_step(fa[1], fb[1]);
+            if (FAST) sched_interleave<NMF, NFR, 0, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int kt = 0;
+        for (; kt + 1 < kfull; ++kt) body(kt, std::true_type{});
+        for (; kt < nkt; ++kt) body(kt, std::false_type{});
     }
 
-    // ---------------------------------------------------------------- epilogue
-    // accumulator acc[tn][tm], lane l, register r holds output
-    //   m = mb + tm*32 + (l & 31),  n = nb + tn*32 + 8*(r/4) + 4*(l/32) + (r%4)
-    const int mb = m0 + wm * TM;
-    const int nb = n0 + wn * TN;
-    const int lm = lane & 31, lq = (lane >> 5) * 4;
-
-    if constexpr (EPI == EPI_GEMM) {
-        uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
-        const bool full_c = (m0 + BM <= p.M) && (n0 + BN <= p.N) && p.vec_c;
-        const float alpha = p.alpha, beta = p.beta;
-#pragma unroll
-        for (int tm = 0; tm < FM; ++tm) {
-            const int m = mb + tm * 32 + lm;
-            if (!full_c && m >= p.M) continue;
-#pragma unroll
-            for (int tn = 0; tn < FN; ++tn) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = nb + tn * 32 + 8 * g + lq;
-                    uint16_t* c = C + (int64_t)m * p.ldc + n;
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = alpha * acc[tn][tm][4 * g + e];
-                    if (full_c) {
-                        if (beta != 0.0f) {
-                            const u32x2 old = *reinterpret_cast<const u32x2*>(c);
-                            v[0] += beta * to_f32<DT>((uint16_t)(old.x & 0xffff));
-                            v[1] += beta * to_f32<DT>((uint16_t)(old.x >> 16));
-                            v[2] += beta * to_f32<DT>((uint16_t)(old.y & 0xffff));
-                            v[3] += beta * to_f32<DT>((uint16_t)(old.y >> 16));
-                        }
-                        u32x2 o;
-                        o.x = (uint32_t)from_f32<DT>(v[0]) | ((uint32_t)from_f32<DT>(v[1]) << 16);
-                        o.y = (uint32_t)from_f32<DT>(v[2]) | ((uint32_t)from_f32<DT>(v[3]) << 16);
-                        *reinterpret_cast<u32x2*>(c) = o;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (n + e < p.N) {
-                                float x = v[e];
-                                if (beta != 0.0f) x += beta * to_f32<DT>(c[e]);
-                                c[e] = from_f32<DT>(x);
-                            }
-                        }
-                    }
-                }
-            }
-        }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-        uint16_t* Y = reinterpret_cast<uint16_t*>(p.C);
-        const int nout = p.N >> 1;                 // p.N is the fused width
-        const bool full_c = (m0 + BM <= p.M) && (n0 + BN <= p.N) && p.vec_c;
-        const float s = p.alpha;
-        const int ob = nb >> 1;                    // first output column of this wave
-#pragma unroll
-        for (int tm = 0; tm < FM; ++tm) {
-            const int m = mb + tm * 32 + lm;
-            if (!full_c && m >= p.M) continue;
-#pragma unroll
-            for (int q = 0; q < FN / 2; ++q) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = ob + q * 32 + 8 * g + lq;
-                    uint16_t* y = Y + (int64_t)m * nout + n;
-                    float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float gate = s * acc[2 * q][tm][4 * g + e];
-                        const float up = s * acc[2 * q + 1][tm][4 * g + e];
-                        v[e] = silu(gate) * up;
-                    }
-                    if (full_c) {
-                        u32x2 o;
-                        o.x = (uint32_t)from_f32<DT>(v[0]) | ((uint32_t)from_f32<DT>(v[1]) << 16);
-                        o.y = (uint32_t)from_f32<DT>(v[2]) | ((uint32_t)from_f32<DT>(v[3]) << 16);
-                        *reinterpret_cast<u32x2*>(y) = o;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < nout) y[e] = from_f32<DT>(v[e]);
-                    }
-                }
-            }
-        }
-    } else {  // EPI_PARTIAL: raw fp32 sums of this split, [split][M][N] with ld N
-        float* W = reinterpret_cast<float*>(p.C) + (int64_t)blockIdx.y * p.M * p.N;
-        const bool full_c = (m0 + BM <= p.M) && (n0 + BN <= p.N) && ((p.N & 3) == 0);
-#pragma unroll
-        for (int tm = 0; tm < FM; ++tm) {
-            const int m = mb + tm * 32 + lm;
-            if (!full_c && m >= p.M) continue;
-#pragma unroll
-            for (int tn = 0; tn < FN; ++tn) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = nb + tn * 32 + 8 * g + lq;
-                    float* w = W + (int64_t)m * p.N + n;
-                    if (full_c) {
-                        f32x4 o = {acc[tn][tm][4 * g], acc[tn][tm][4 * g + 1],
-                                   acc[tn][tm][4 * g + 2], acc[tn][tm][4 * g + 3]};
-                        *reinterpret_cast<f32x4*>(w) = o;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < p.N) w[e] = acc[tn][tm][4 * g + e];
-                    }
-                }
-            }
-        }
-    }
+    epilogue16<DT, EPI, false, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN, lane);
 }
 
 }  // namespace sg

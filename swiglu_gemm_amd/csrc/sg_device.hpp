@@ -41,6 +41,19 @@ __device__ __forceinline__ float silu(float x) {
     return x / (1.0f + __expf(-x));
 }
 
+// Arguments of the 16-bit / 8-bit MFMA GEMM kernels.
+struct Gemm16Params {
+    const uint16_t* A;   // storage of A (16-bit elements; e4m3 kernels reinterpret)
+    const uint16_t* B;
+    void* C;            // EPI_GEMM: C (dtype); EPI_SWIGLU: Y; EPI_PARTIAL: fp32 workspace
+    int64_t lda, ldb, ldc;
+    int M, N, K;        // N is the fused width 2*N_out for SwiGLU / its partials
+    float alpha, beta;  // SwiGLU: alpha = scale_a * scale_w
+    int vec_a, vec_b, vec_c;
+    int tiles_m, tiles_n, group_m;
+    int k_per_split;    // a multiple of 64; gridDim.y splits
+};
+
 // ---------------------------------------------------------------------------
 // XCD-aware block order.  Work-groups are handed to the 8 XCDs round-robin
 // (block b runs on XCD b % 8); remap so that consecutive logical tiles share an
@@ -65,6 +78,33 @@ __device__ __forceinline__ void tile_coords(int lid, int tiles_m, int tiles_n, i
     const int r = lid - g * per_group;
     tm = first_m + r % gm;
     tn = r / gm;
+}
+
+// ---------------------------------------------------------------------------
+// Scheduling hint: spread NR LDS reads, NV global loads and NW LDS writes evenly
+// between NM MFMAs of one scheduling region (hint only; never changes results).
+template <int NM, int NR, int NV, int NW, int I = 0>
+__device__ __forceinline__ void sched_interleave() {
+    if constexpr (I < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+        constexpr int r = (I + 1) * NR / NM - I * NR / NM;
+        constexpr int v = (I + 1) * NV / NM - I * NV / NM;
+        constexpr int w = (I + 1) * NW / NM - I * NW / NM;
+        if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);   // DS read
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);   // VMEM read
+        if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);   // DS write
+        sched_interleave<NM, NR, NV, NW, I + 1>();
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma16(const u32x4& a, const u32x4& b, const f32x16& c) {
+    if constexpr (DT == DT_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 }  // namespace sg

@@ -1,0 +1,107 @@
+"""Every kernel configuration (register-staged and DMA ring), every transpose pair,
+each epilogue (alpha/beta, SwiGLU pair, split-K partials + reduction), forced
+through SG_FORCE_CONFIG and checked against the fp64 oracle.  Shapes are
+multiples of every tile so the DMA configurations are eligible."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from swiglu_gemm_amd import inputs
+from helpers import assert_close, bits_equal, from_dev, split_count, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+NCFG = 8
+TRANS = ["NN", "NT", "TN", "TT"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import swiglu_gemm_amd as sg
+    sg.lib()
+    yield
+    os.environ.pop("SG_FORCE_CONFIG", None)
+
+
+def forced(cfg, splits=0):
+    os.environ["SG_FORCE_CONFIG"] = "%d,%d" % (cfg, splits)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("tr", TRANS)
+@pytest.mark.parametrize("cfg", range(NCFG))
+def test_gemm_every_config(cfg, tr, splits):
+    import swiglu_gemm_amd as sg
+    M, N, K = 512, 256, 768
+    ta, tb = tr
+    dtype = "bf16" if cfg % 2 else "f16"
+    p = inputs.gemm_problem(60 + cfg, ta, tb, M, N, K, dtype, "normal", ld_mode="tight")
+    A, B, C = to_dev(p["A"], dtype), to_dev(p["B"], dtype), to_dev(p["C"], dtype)
+    forced(cfg, splits)
+    print("cfg %d %s splits %d" % (cfg, tr, splits), flush=True)
+    try:
+        sg.gemm(A, B, C, alpha=0.7, beta=0.3, transA=ta, transB=tb, M=M, N=N, K=K,
+                lda=p["lda"], ldb=p["ldb"], ldc=p["ldc"], dtype={"f16": 1, "bf16": 2}[dtype])
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    assert split_count(desc) == splits, desc
+    ref = oracle.gemm(ta, tb, M, N, K, 0.7, p["A"], p["lda"], p["B"], p["ldb"], 0.3, p["C"],
+                      p["ldc"], dtype)
+    assert_close(oracle.decode(from_dev(C), dtype), ref, dtype, K, desc)
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+@pytest.mark.parametrize("cfg", range(NCFG))
+def test_swiglu_every_config(cfg, splits):
+    import swiglu_gemm_amd as sg
+    M, N, K = 256, 512, 512          # W_fused is 512 x 1024
+    pb = inputs.swiglu_problem(70 + cfg, M, N, K, "bf16", w_std=0.05)
+    Wf = oracle.interleave(pb["W1"], pb["W2"])
+    A, W = to_dev(pb["A"], "bf16"), to_dev(Wf, "bf16")
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    forced(cfg, splits)
+    print("swiglu cfg %d splits %d" % (cfg, splits), flush=True)
+    try:
+        sg.swiglu_gemm(A, W, Y)
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+        y1 = from_dev(Y)
+        sg.swiglu_gemm(A, W, Y)
+        torch.cuda.synchronize()
+        y2 = from_dev(Y)
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    assert split_count(desc) == splits, desc
+    assert bits_equal(y1, y2), "not run-to-run identical"
+    ref = oracle.swiglu(M, N, K, pb["A"], Wf, "bf16")
+    assert_close(oracle.decode(y1, "bf16"), ref, "bf16", K, desc)
+
+
+@pytest.mark.parametrize("cfg", range(NCFG))
+def test_identity_bit_exact_every_config(cfg):
+    """A @ I == A bit-exactly through every configuration (layout check)."""
+    import swiglu_gemm_amd as sg
+    M, K = 256, 256
+    gen = np.random.default_rng(cfg)
+    Ab = inputs.to_storage(gen.standard_normal((M, K)), "bf16")
+    Ib = inputs.to_storage(np.eye(K), "bf16")
+    A, I = to_dev(Ab, "bf16"), to_dev(Ib, "bf16")
+    C = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
+    forced(cfg, 1)
+    try:
+        sg.gemm(A, I, C)
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    assert bits_equal(from_dev(C), Ab), desc
