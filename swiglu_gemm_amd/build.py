@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libswiglu_gemm.so")
-SOURCES = ["api.hip", "inst_f16.hip", "inst_bf16.hip"]
+SOURCES = ["api.hip"] + ["inst_%s_%s.hip" % (d, t) for d in ("f16", "bf16", "e4m3")
+                        for t in ("nn", "nt", "tn", "tt")]
 ARCH = "gfx950"
 
 

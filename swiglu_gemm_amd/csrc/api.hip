@@ -20,14 +20,18 @@
 using namespace sg;
 
 namespace sg {
-// defined in inst_f16.hip / inst_bf16.hip
+// defined in inst_<dtype>_<transposes>.hip
+template <int DT, bool TA, bool TB>
+hipError_t launch16_tr(int epi, int cfg, const Gemm16Params& p, int splits, hipStream_t st);
+
 template <int DT>
 hipError_t launch16_dt(bool ta, bool tb, int epi, int cfg, const Gemm16Params& p, int splits,
-                       hipStream_t st);
-extern template hipError_t launch16_dt<DT_F16>(bool, bool, int, int, const Gemm16Params&, int,
-                                               hipStream_t);
-extern template hipError_t launch16_dt<DT_BF16>(bool, bool, int, int, const Gemm16Params&, int,
-                                                hipStream_t);
+                       hipStream_t st) {
+    if (!ta && !tb) return launch16_tr<DT, false, false>(epi, cfg, p, splits, st);
+    if (!ta && tb) return launch16_tr<DT, false, true>(epi, cfg, p, splits, st);
+    if (ta && !tb) return launch16_tr<DT, true, false>(epi, cfg, p, splits, st);
+    return launch16_tr<DT, true, true>(epi, cfg, p, splits, st);
+}
 }  // namespace sg
 
 namespace {
@@ -92,18 +96,36 @@ bool forced_config(int* cfg, int* splits) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-struct Problem16 {
-    int64_t M, N, K;      // N: fused width for SwiGLU
-    bool vec_a, vec_b;    // 16-byte aligned base and ld % 8 == 0
-};
-
-// The DMA kernels need whole tiles and 16-byte aligned rows.
-bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
-    return c.dma && q.vec_a && q.vec_b && q.M % c.BM == 0 && q.N % c.BN == 0 &&
-           q.K % c.BK == 0 && kps % c.BK == 0;
+// Tile-rows walked together by the grouped tile order (SG_GROUP_M overrides).
+int group_m() {
+    const char* s = std::getenv("SG_GROUP_M");
+    const int g = s ? std::atoi(s) : 0;
+    return g > 0 ? g : 4;
 }
 
-int64_t split_len(int64_t K, int splits) { return cdiv(cdiv(K, splits), 64) * 64; }
+struct Problem16 {
+    int64_t M, N, K;      // N: fused width for SwiGLU
+    bool vec_a, vec_b;    // 16-byte aligned base and ld*size % 16 == 0
+    bool ta, tb;          // transposes
+    int esz;              // operand element size (2: fp16/bf16, 1: e4m3)
+};
+
+// Whether a direct-to-LDS configuration can run the problem: no K tail, aligned
+// operands, DMA-compatible tiles, and a row-contiguous operand whose row length
+// is a whole number of 16-byte chunks (edge rows / chunks are clamped in-kernel).
+bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
+    if (!c.dma || c.e4m3 != (q.esz == 1)) return false;
+    if (!q.vec_a || !q.vec_b || q.K % c.BK != 0 || kps % c.BK != 0) return false;
+    const int nw = c.WM * c.WN;
+    if (!dma_tile_ok(!q.ta, c.BM, c.BK, q.esz, nw) || !dma_tile_ok(q.tb, c.BN, c.BK, q.esz, nw))
+        return false;
+    if (q.ta && (q.M * q.esz) % 16 != 0) return false;   // A rows hold M elements
+    if (!q.tb && (q.N * q.esz) % 16 != 0) return false;  // B rows hold N elements
+    return true;
+}
+
+// split lengths are multiples of 128 (a whole number of K tiles for every config)
+int64_t split_len(int64_t K, int splits) { return cdiv(cdiv(K, splits), 128) * 128; }
 
 int pick_splits(const Cfg16& c, const Problem16& q) {
     const int64_t tiles = cdiv(q.M, c.BM) * cdiv(q.N, c.BN);
@@ -117,20 +139,33 @@ int pick_splits(const Cfg16& c, const Problem16& q) {
     return s;
 }
 
-// Choose a configuration and split count; falls back to a register-staged
-// configuration whenever a DMA configuration does not fit the problem.
+// Choose a configuration and split count.  16-bit problems fall back to a
+// register-staged configuration when a DMA configuration does not fit; e4m3
+// problems report -1 (the caller then runs the generic kernel).
 void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
     int cfg = -1, splits = 0;
-    const bool forced = forced_config(&cfg, &splits) && cfg >= 0 && cfg < kNumCfg16;
+    const bool e4m3 = q.esz == 1;
+    const bool forced = forced_config(&cfg, &splits) && cfg >= 0 && cfg < kNumCfg16 &&
+                        (kCfg16[cfg].e4m3 != 0) == e4m3;
     if (!forced) {
+        // measured on MI355X: 256x256 tiles once there are >= 2 full waves of
+        // them, else 128x128 tiles (8 waves when M allows two 128-row tiles);
+        // e4m3 with few rows uses 32-row tiles
         const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
-        cfg = big >= kNumCU / 2 ? 3 : 6;
+        if (!e4m3)
+            cfg = big >= 2 * kNumCU ? 10 : (q.M >= 256 ? 13 : 6);
+        else
+            cfg = big >= 2 * kNumCU ? 14 : (q.M >= 256 ? 15 : (cdiv(q.N, 256) >= 128 ? 16 : 17));
         splits = 0;
     }
     if (splits <= 0) splits = pick_splits(kCfg16[cfg], q);
-    if (kCfg16[cfg].dma && !dma_ok(kCfg16[cfg], q, split_len(q.K, splits))) {
-        cfg = kCfg16[cfg].BM >= 256 ? 1 : 2;
-        if (!forced) splits = pick_splits(kCfg16[cfg], q);
+    if (!dma_ok(kCfg16[cfg], q, split_len(q.K, splits))) {
+        if (kCfg16[cfg].dma && !e4m3 && !kCfg16[cfg].e4m3) {
+            cfg = kCfg16[cfg].BM >= 256 ? 0 : 2;
+            if (!forced) splits = pick_splits(kCfg16[cfg], q);
+        } else if (kCfg16[cfg].dma) {
+            cfg = -1;
+        }
     }
     *cfg_out = cfg;
     *splits_out = splits;
@@ -148,17 +183,16 @@ void set_last(const char* what, int cfg, int splits) {
                   cfg >= 0 && cfg < kNumCfg16 ? kCfg16[cfg].name : "-", splits);
 }
 
-constexpr int BK16 = 64;   // split lengths are multiples of this
-
 template <int DT>
 hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* out,
                  bool out_vec, const char* what, hipStream_t st, int* splits_used) {
     int cfg = 0, splits = 1;
     choose16(q, &cfg, &splits);
+    if (cfg < 0) return hipErrorNotSupported;   // caller takes its generic path
     const Cfg16& c = kCfg16[cfg];
     p.tiles_m = (int)cdiv(q.M, c.BM);
     p.tiles_n = (int)cdiv(q.N, c.BN);
-    p.group_m = 8;
+    p.group_m = group_m();
     if (splits > 1) {
         p.k_per_split = (int)split_len(q.K, splits);
         splits = (int)cdiv(q.K, p.k_per_split);
@@ -167,7 +201,7 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
     if (splits <= 1) {
         p.C = out;
         p.vec_c = out_vec;
-        p.k_per_split = (int)(cdiv(q.K, BK16) * BK16);
+        p.k_per_split = (int)split_len(q.K, 1);
         set_last(what, cfg, 1);
         return launch16_dt<DT>(ta, tb, epi, cfg, p, 1, st);
     }
@@ -197,7 +231,7 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
     p.beta = beta;
     p.vec_a = aligned(A, 16) && (lda % 8 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 8 == 0);
-    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b};
+    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 2};
     int splits = 1;
     hipError_t e = run16<DT>(ta, tb, EPI_GEMM, q, p, C, aligned(C, 8) && (ldc % 4 == 0), "gemm16",
                              st, &splits);
@@ -207,6 +241,43 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_gemm_kernel<DT>, dim3(grid_1d(M * N)), dim3(256), 0, st, ws, splits,
                        (int)M, (int)N, C, ldc, alpha, beta);
+    return hipGetLastError();
+}
+
+// e4m3 GEMM: A, B e4m3 codes, C bf16 (alpha carries the per-tensor scales).
+hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                 int64_t lda, const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+                 hipStream_t st) {
+    Gemm16Params p{};
+    p.A = reinterpret_cast<const uint16_t*>(A);
+    p.B = reinterpret_cast<const uint16_t*>(B);
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.vec_a = aligned(A, 16) && (lda % 16 == 0);
+    p.vec_b = aligned(B, 16) && (ldb % 16 == 0);
+    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1};
+    int splits = 1;
+    hipError_t e = run16<DT_E4M3>(ta, tb, EPI_GEMM, q, p, C, aligned(C, 8) && (ldc % 4 == 0),
+                                  "gemm8", st, &splits);
+    if (e == hipErrorNotSupported) {
+        std::snprintf(g_last_cfg, sizeof(g_last_cfg), "gemm8 generic splits=1");
+        hipLaunchKernelGGL(gemm_e4m3_generic, dim3(grid_1d(M * N)), dim3(256), 0, st,
+                           (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, lda, ldb, ldc,
+                           (int)M, (int)N, (int)K, (int)ta, (int)tb, alpha, beta);
+        return hipGetLastError();
+    }
+    if (e != hipSuccess || splits <= 1) return e;
+    float* ws = nullptr;
+    e = workspace((size_t)splits * M * N * sizeof(float), &ws);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_gemm_kernel<DT_BF16>, dim3(grid_1d(M * N)), dim3(256), 0, st, ws,
+                       splits, (int)M, (int)N, C, ldc, alpha, beta);
     return hipGetLastError();
 }
 
@@ -304,7 +375,8 @@ int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alp
             e = gemm16<DT_BF16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
             break;
         default:
-            return -14;  // e4m3 GEMM: not built yet
+            e = gemm8(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
+            break;
     }
     return status_of(e);
 }
@@ -322,7 +394,6 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
     if (!std::isfinite(scale_w) || !(scale_w > 0.0f)) return -9;
     if (dtype != SG_F8E4M3 && scale_a != 1.0f) return -8;
     if (dtype != SG_F8E4M3 && scale_w != 1.0f) return -9;
-    if (dtype == SG_F8E4M3) return -7;  // not built yet
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (M == 0 || N == 0) return 0;
     const int out_dt = dtype == SG_F16 ? SG_F16 : SG_BF16;
@@ -349,15 +420,28 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
     p.K = (int)K;
     p.alpha = scale_a * scale_w;
     p.beta = 0.0f;
-    p.vec_a = aligned(A, 16) && (K % 8 == 0);
-    p.vec_b = aligned(Wfused, 16) && (N2 % 8 == 0);
-    Problem16 q{M, N2, K, (bool)p.vec_a, (bool)p.vec_b};
+    const int esz = dtype == SG_F8E4M3 ? 1 : 2;
+    p.vec_a = aligned(A, 16) && ((K * esz) % 16 == 0);
+    p.vec_b = aligned(Wfused, 16) && ((N2 * esz) % 16 == 0);
+    Problem16 q{M, N2, K, (bool)p.vec_a, (bool)p.vec_b, false, false, esz};
     // Y stores are 4 or 8 bytes wide depending on the kernel: require the stricter
     const bool yvec = aligned(Y, 8) && (N % 4 == 0);
     int splits = 1;
-    hipError_t e = out_dt == SG_F16
-        ? run16<DT_F16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits)
-        : run16<DT_BF16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits);
+    hipError_t e;
+    if (dtype == SG_F8E4M3) {
+        e = run16<DT_E4M3>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu8", st, &splits);
+        if (e == hipErrorNotSupported) {
+            std::snprintf(g_last_cfg, sizeof(g_last_cfg), "swiglu8 generic splits=1");
+            hipLaunchKernelGGL(swiglu_e4m3_generic, dim3(grid_1d(M * N)), dim3(256), 0, st,
+                               (const uint8_t*)A, (const uint8_t*)Wfused, (uint16_t*)Y, (int)M,
+                               (int)N, (int)K, p.alpha);
+            return status_of(hipGetLastError());
+        }
+    } else if (out_dt == SG_F16) {
+        e = run16<DT_F16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits);
+    } else {
+        e = run16<DT_BF16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits);
+    }
     if (e != hipSuccess || splits <= 1) return status_of(e);
     float* ws = nullptr;
     e = workspace((size_t)splits * M * N2 * sizeof(float), &ws);

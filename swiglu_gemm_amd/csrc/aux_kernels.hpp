@@ -196,3 +196,59 @@ __global__ void __launch_bounds__(256) silu_mul_kernel(const uint16_t* G, const 
 }
 
 }  // namespace sg
+
+namespace sg {
+
+// ---------------------------------------------------------------------------
+// Generic e4m3 kernels for shapes the direct-to-LDS kernel does not take (a K
+// tail, odd sizes or alignment): one thread per output, exact e4m3 -> fp32
+// decode, fp32 accumulation in k order, bf16 output.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_to_f32(uint8_t q) {
+    const int e = (q >> 3) & 15, f = q & 7;
+    float v;
+    if (e == 15 && f == 7) v = __builtin_nanf("");
+    else if (e == 0) v = ldexpf((float)f, -9);
+    else v = ldexpf((float)(8 + f), e - 10);
+    return (q & 0x80) ? -v : v;
+}
+
+__global__ void __launch_bounds__(256) gemm_e4m3_generic(const uint8_t* A, const uint8_t* B,
+                                                         uint16_t* C, int64_t lda, int64_t ldb,
+                                                         int64_t ldc, int M, int N, int K, int ta,
+                                                         int tb, float alpha, float beta) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+        float s = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const uint8_t a = ta ? A[(int64_t)k * lda + m] : A[(int64_t)m * lda + k];
+            const uint8_t b = tb ? B[(int64_t)n * ldb + k] : B[(int64_t)k * ldb + n];
+            s += e4m3_to_f32(a) * e4m3_to_f32(b);
+        }
+        uint16_t* c = C + (int64_t)m * ldc + n;
+        float v = alpha * s;
+        if (beta != 0.0f) v += beta * to_f32<DT_BF16>(*c);
+        *c = from_f32<DT_BF16>(v);
+    }
+}
+
+__global__ void __launch_bounds__(256) swiglu_e4m3_generic(const uint8_t* A, const uint8_t* Wf,
+                                                           uint16_t* Y, int M, int N, int K,
+                                                           float s) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+        float g = 0.0f, u = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const float a = e4m3_to_f32(A[(int64_t)m * K + k]);
+            g += a * e4m3_to_f32(Wf[(int64_t)k * 2 * N + 2 * n]);
+            u += a * e4m3_to_f32(Wf[(int64_t)k * 2 * N + 2 * n + 1]);
+        }
+        Y[i] = from_f32<DT_BF16>(silu(s * g) * (s * u));
+    }
+}
+
+}  // namespace sg

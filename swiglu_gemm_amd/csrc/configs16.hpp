@@ -4,6 +4,7 @@
 namespace sg {
 
 struct Cfg16 {
+    int e4m3;           // 1: e4m3 operands (BK in bytes), 0: fp16 / bf16 operands
     int dma;            // 1: direct global->LDS ring (gemm16_dma.hpp), 0: register-staged
     int BM, BN, BK, S;  // tile and LDS stages
     int WM, WN;         // waves along M and N
@@ -11,16 +12,63 @@ struct Cfg16 {
 };
 
 // Index = configuration id (SG_FORCE_CONFIG=<id>[,<splits>] overrides the choice).
+// Every row must also appear in the SG_CONFIGS list below, with the same values.
 constexpr Cfg16 kCfg16[] = {
-    {0, 256, 256, 64, 2, 2, 2, "reg 256x256x64 s2 4w"},
-    {0, 256, 256, 64, 2, 2, 4, "reg 256x256x64 s2 8w"},
-    {0, 128, 128, 64, 2, 2, 2, "reg 128x128x64 s2 4w"},
-    {1, 256, 256, 32, 4, 2, 2, "dma 256x256x32 s4 4w"},
-    {1, 256, 256, 32, 4, 2, 4, "dma 256x256x32 s4 8w"},
-    {1, 256, 256, 64, 2, 2, 2, "dma 256x256x64 s2 4w"},
-    {1, 128, 128, 32, 4, 2, 2, "dma 128x128x32 s4 4w"},
-    {1, 128, 128, 64, 3, 2, 2, "dma 128x128x64 s3 4w"},
+    {0, 0, 256, 256, 64, 2, 2, 2, "reg 256x256x64 s2 2x2w"},
+    {0, 0, 256, 256, 64, 2, 2, 4, "reg 256x256x64 s2 2x4w"},
+    {0, 0, 128, 128, 64, 2, 2, 2, "reg 128x128x64 s2 2x2w"},
+    {0, 1, 256, 256, 32, 4, 2, 2, "dma 256x256x32 s4 2x2w"},
+    {0, 1, 256, 256, 32, 4, 2, 4, "dma 256x256x32 s4 2x4w"},
+    {0, 1, 256, 256, 64, 2, 2, 2, "dma 256x256x64 s2 2x2w"},
+    {0, 1, 128, 128, 32, 4, 2, 2, "dma 128x128x32 s4 2x2w"},
+    {0, 1, 128, 128, 64, 3, 2, 2, "dma 128x128x64 s3 2x2w"},
+    {0, 1, 256, 256, 64, 2, 2, 4, "dma 256x256x64 s2 2x4w"},
+    {0, 1, 256, 256, 32, 4, 4, 2, "dma 256x256x32 s4 4x2w"},
+    {0, 1, 256, 256, 64, 2, 4, 2, "dma 256x256x64 s2 4x2w"},
+    {0, 1, 128, 256, 64, 2, 2, 2, "dma 128x256x64 s2 2x2w"},
+    {0, 1, 256, 128, 64, 2, 2, 2, "dma 256x128x64 s2 2x2w"},
+    {0, 1, 128, 128, 64, 2, 2, 4, "dma 128x128x64 s2 2x4w"},
+    {1, 1, 256, 256, 128, 2, 4, 2, "e4m3 dma 256x256x128 s2 4x2w"},
+    {1, 1, 128, 128, 128, 2, 2, 4, "e4m3 dma 128x128x128 s2 2x4w"},
+    {1, 1, 32, 256, 128, 4, 1, 4, "e4m3 dma 32x256x128 s4 1x4w"},
+    {1, 1, 32, 128, 128, 4, 1, 4, "e4m3 dma 32x128x128 s4 1x4w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
+
+constexpr int kFirstCfgE4M3 = 14;
+
+// Whether the direct-to-LDS kernel supports an operand tile: KC (k-contiguous)
+// rows of 64 or 128 bytes, row-contiguous rows of 128..1024 bytes, a whole number
+// of 1 KiB DMA blocks per wave.
+constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
+    const int row_bytes = kc ? bk * esz : rows * esz;
+    const int bytes = rows * bk * esz;
+    return (kc ? (row_bytes == 64 || row_bytes == 128) : (row_bytes >= 128 && row_bytes <= 1024)) &&
+           bytes % 1024 == 0 && (bytes / 1024) % nwaves == 0;
+}
+
+// X(id, dma, BM, BN, BK, S, WM, WN) for every 16-bit row of kCfg16
+#define SG_CONFIGS(X)                  \
+    X(0, 0, 256, 256, 64, 2, 2, 2)     \
+    X(1, 0, 256, 256, 64, 2, 2, 4)     \
+    X(2, 0, 128, 128, 64, 2, 2, 2)     \
+    X(3, 1, 256, 256, 32, 4, 2, 2)     \
+    X(4, 1, 256, 256, 32, 4, 2, 4)     \
+    X(5, 1, 256, 256, 64, 2, 2, 2)     \
+    X(6, 1, 128, 128, 32, 4, 2, 2)     \
+    X(7, 1, 128, 128, 64, 3, 2, 2)     \
+    X(8, 1, 256, 256, 64, 2, 2, 4)     \
+    X(9, 1, 256, 256, 32, 4, 4, 2)     \
+    X(10, 1, 256, 256, 64, 2, 4, 2)    \
+    X(11, 1, 128, 256, 64, 2, 2, 2)    \
+    X(12, 1, 256, 128, 64, 2, 2, 2)    \
+    X(13, 1, 128, 128, 64, 2, 2, 4)
+
+// the same for every e4m3 row (all direct-to-LDS)
+#define SG_CONFIGS_E4M3(X)             \
+    X(14, 1, 256, 256, 128, 2, 4, 2)   \
+    X(15, 1, 128, 128, 128, 2, 2, 4)   \
+    X(16, 1, 32, 256, 128, 4, 1, 4)    \
+    X(17, 1, 32, 128, 128, 4, 1, 4)
 
 }  // namespace sg

@@ -1,28 +1,36 @@
-// gemm16_dma.hpp -- fp16 / bf16 MFMA GEMM with direct global->LDS loads (gfx950).
+// gemm16_dma.hpp -- MFMA GEMM with direct global->LDS loads (gfx950), for 16-bit
+// (fp16 / bf16, v_mfma_f32_32x32x16) and 8-bit (OCP e4m3, v_mfma_scale_f32_
+// 32x32x64_f8f6f4 with unit block scales) operands; fp32 accumulation; the
+// transposed accumulator D^T and the epilogues of epilogue16.hpp.
 //
-// Same arithmetic and epilogues as gemm16.hpp (acc = op(A)_tile * op(B)_tile in
-// fp32 with v_mfma_f32_32x32x16_{f16,bf16}, transposed accumulator D^T), but the
-// tiles travel from global memory straight into LDS with global_load_lds_dwordx4
-// (16 bytes per lane, no VGPR staging), through a ring of S LDS stages, so loads
+// Tiles travel from global memory straight into LDS with global_load_lds_dwordx4
+// (16 bytes per lane, no VGPR staging) through a ring of S LDS stages, so loads
 // run S-1 tiles ahead of the MFMAs.
 //
 // LDS layouts, chosen so both operand orientations feed the MFMA directly:
 // * k-contiguous operand (A 'N', B 'T'): [R][BK] with 16-byte chunks XOR-swizzled
-//   by row; an MFMA fragment (32 rows x 8 k per lane) is one ds_read_b128.
+//   by row; a fragment (32 rows x one k-step per lane) is one (16-bit) or two
+//   (8-bit) ds_read_b128.
 // * row-contiguous operand (A 'T', B 'N', W_fused): [BK][R] as stored in memory,
-//   32-byte units XOR-swizzled by k; the fragment is two ds_read_b64_tr_b16
-//   (each 16-lane group turns four 32-byte row pieces into 4 k-values per lane).
-// The DMA writes 1 KiB per wave instruction in lane order; the swizzle is applied
-// by choosing which global 16-byte chunk each lane fetches.
+//   32-byte units XOR-swizzled by k; the fragment comes from ds_read_b64_tr_b16
+//   (x2) or ds_read_b64_tr_b8 (x4): each 16-lane group turns 4 (8) row pieces into
+//   4 (8) k-values per lane.
+// The swizzles keep every 16-lane / 32-lane LDS phase on distinct banks.  The DMA
+// writes 1 KiB per wave instruction in lane order; the swizzle is applied by
+// choosing which global 16-byte chunk each lane fetches.
 //
-// W_fused keeps its interleaved column order here: in the D^T accumulator layout
-// fused columns (2n, 2n+1) land in registers (r, r+1) of one lane, so the SwiGLU
+// W_fused keeps its interleaved column order: in the D^T accumulator layout fused
+// columns (2n, 2n+1) land in registers (r, r+1) of one lane, so the SwiGLU
 // epilogue pairs them in place ("Resumo Técnico: Sobreposição de Ativação em Nível
 // de Tile ...", Metodologia / Kernel-2).
 //
-// Used only when every tile is full (M % BM == N % BN == 0, K-split lengths a
-// multiple of BK) and operands are 16-byte aligned with ld % 8 == 0; other
-// problems take the register-staged kernel of gemm16.hpp.
+// Edge tiles: a k-contiguous operand's rows past M (N) are clamped to the last
+// valid row, and a row-contiguous operand's 16-byte chunks past N (M) to the
+// last valid chunk, so every load stays inside the operand; the outputs those
+// rows/columns feed are never stored.  K must be a multiple of BK (no K tail),
+// operands 16-byte aligned with ld*size % 16 == 0, and for a row-contiguous
+// operand its row length*size % 16 == 0; other problems take gemm16.hpp or the
+// generic e4m3 kernel.
 #pragma once
 
 #include "epilogue16.hpp"
@@ -31,25 +39,33 @@
 namespace sg {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
-template <bool KC, int R, int BK>
+template <bool KC, int R, int BK, int ESZ>
 struct DmaTile {
-    static constexpr int ROW_BYTES = KC ? BK * 2 : R * 2;
-    static constexpr int BYTES = R * BK * 2;
+    static constexpr int ROW_BYTES = KC ? BK * ESZ : R * ESZ;
+    static constexpr int BYTES = R * BK * ESZ;
     static constexpr int SLOTS = ROW_BYTES / 16;         // 16-byte slots per row
     static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;  // rows per 1 KiB DMA block
     static constexpr int BLOCKS = BYTES / 1024;
     static_assert(ROW_BYTES <= 1024 && 1024 % ROW_BYTES == 0, "row must divide 1 KiB");
-    static_assert(KC ? (BK == 32 || BK == 64) : (R >= 128), "unsupported tile");
+    static_assert(KC ? (ROW_BYTES == 64 || ROW_BYTES == 128) : (ROW_BYTES >= 128),
+                  "unsupported tile");
 
     // physical 16-byte chunk (KC) or 32-byte unit (row-contiguous) for a row
     static __device__ __forceinline__ int swz(int row) {
         if constexpr (KC) {
-            if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
+            if constexpr (ROW_BYTES == 128) return (row & 7) ^ ((row >> 3) & 1);
             else return (row >> 2) & 3;
+        } else if constexpr (ESZ == 2) {
+            return (row & 3) << 1;                    // 4 rows x 2 units per phase
+        } else if constexpr (ROW_BYTES >= 256) {
+            return row & 7;                           // 8 rows x 1 unit per phase
         } else {
-            return (row & 3) << 1;
+            return (row >> 1) & 3;                    // 128-byte rows: 2 rows per bank row
         }
     }
 };
@@ -61,16 +77,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One operand's DMA stream: NI instructions per thread per K tile.
-template <bool KC, int R, int BK, int NWAVES>
+template <bool KC, int R, int BK, int ESZ, int NWAVES>
 struct DmaStream {
-    using T = DmaTile<KC, R, BK>;
+    using T = DmaTile<KC, R, BK, ESZ>;
     static_assert(T::BLOCKS % NWAVES == 0, "DMA blocks must split evenly over the waves");
     static constexpr int NI = T::BLOCKS / NWAVES;
-    const uint16_t* gp[NI];
-    int64_t step;   // elements to advance per K tile
+    const char* gp[NI];
+    int64_t step;   // bytes to advance per K tile
 
-    __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int r0, int k0,
+    // rows: valid extent of the tile-row dimension (M or N) for edge clamping
+    __device__ __forceinline__ void init(const void* base_, int64_t ld, int r0, int rows, int k0,
                                          int wave, int lane) {
+        const char* base = reinterpret_cast<const char*>(base_);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int b = wave + i * NWAVES;
@@ -78,13 +96,15 @@ struct DmaStream {
             const int slot = lane % T::SLOTS;
             if constexpr (KC) {
                 const int c = slot ^ T::swz(row);
-                gp[i] = base + (int64_t)(r0 + row) * ld + (k0 + c * 8);
+                const int r = min(r0 + row, rows - 1);
+                gp[i] = base + ((int64_t)r * ld + k0) * ESZ + c * 16;
             } else {
                 const int u = (slot >> 1) ^ T::swz(row);
-                gp[i] = base + (int64_t)(k0 + row) * ld + (r0 + u * 16 + (slot & 1) * 8);
+                const int cb = min(r0 * ESZ + u * 32 + (slot & 1) * 16, rows * ESZ - 16);
+                gp[i] = base + (int64_t)(k0 + row) * ld * ESZ + cb;
             }
         }
-        step = KC ? (int64_t)BK : (int64_t)BK * ld;
+        step = KC ? (int64_t)BK * ESZ : (int64_t)BK * ld * ESZ;
     }
     // Issue the DMA of K tile `t` (relative to the split start) into stage memory.
     // Written as inline asm so the compiler does not model the asynchronous LDS
@@ -96,25 +116,39 @@ struct DmaStream {
             const int b = wave + i * NWAVES;
             const uint32_t lds = (uint32_t)(uintptr_t)(
                 (__attribute__((address_space(3))) char*)(stage + b * 1024));
-            const uint16_t* g = gp[i] + t * step;
+            const char* g = gp[i] + t * step;
             asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                          :: "s"(lds), "v"(g) : "memory", "m0");
         }
     }
 };
 
-// MFMA fragment: 32 rows (rbase + lane%32) x 8 k (16*s + 8*(lane/32) + 0..7).
-template <bool KC, int R, int BK>
-__device__ __forceinline__ u32x4 read_frag(const char* tile, int rbase, int s, int lane) {
-    using T = DmaTile<KC, R, BK>;
+// Per-lane MFMA operand: 16-bit: 8 k-values (u32x4); 8-bit: 32 k-values (u32x8).
+template <int ESZ> struct FragT;
+template <> struct FragT<2> { typedef u32x4 type; };
+template <> struct FragT<1> { typedef u32x8 type; };
+
+// Fragment for k-step s: rows rbase + lane%32; k = KSTEP*s + (KSTEP/2)*(lane/32) +
+// 0..KSTEP/2-1, with KSTEP = 16 (16-bit) or 64 (8-bit) elements.
+template <bool KC, int R, int BK, int ESZ>
+__device__ __forceinline__ typename FragT<ESZ>::type read_frag(const char* tile, int rbase, int s,
+                                                               int lane) {
+    using T = DmaTile<KC, R, BK, ESZ>;
     if constexpr (KC) {
         const int row = rbase + (lane & 31);
-        const int chunk = 2 * s + (lane >> 5);
-        return *reinterpret_cast<const u32x4*>(tile + row * T::ROW_BYTES +
-                                               ((chunk ^ T::swz(row)) << 4));
-    } else {
+        const char* rp = tile + row * T::ROW_BYTES;
+        if constexpr (ESZ == 2) {
+            const int chunk = 2 * s + (lane >> 5);
+            return *reinterpret_cast<const u32x4*>(rp + ((chunk ^ T::swz(row)) << 4));
+        } else {
+            const int chunk = 4 * s + 2 * (lane >> 5);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(rp + ((chunk ^ T::swz(row)) << 4));
+            const u32x4 b = *reinterpret_cast<const u32x4*>(rp + (((chunk + 1) ^ T::swz(row)) << 4));
+            return u32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        }
+    } else if constexpr (ESZ == 2) {
         const int g = lane >> 4, L = lane & 15, j = L >> 2, q = L & 3;
-        const int r = rbase + 16 * (g & 1) + 4 * q;
+        const int r = rbase + 16 * (g & 1) + 4 * q;          // element column of this piece
         const int k0 = 16 * s + 8 * (g >> 1) + j;
         const int k1 = k0 + 4;
         const char* p0 = tile + k0 * T::ROW_BYTES + (((r >> 4) ^ T::swz(k0)) << 5) + ((r & 15) << 1);
@@ -123,19 +157,54 @@ __device__ __forceinline__ u32x4 read_frag(const char* tile, int rbase, int s, i
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
         const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
         return u32x4{a.x, a.y, b.x, b.y};
+    } else {
+        // 16 lanes read an 8 x 16-byte block (lanes 2j, 2j+1 give row j) and lane i
+        // receives byte i of each row: 8 consecutive k for column rbase + lane%32
+        const int g = lane >> 4, i = lane & 15, j = i >> 1, h = i & 1;
+        const int c = rbase + 16 * (g & 1) + 8 * h;          // byte column of this piece
+        const int kb = 64 * s + 32 * (g >> 1) + j;
+        u32x8 out;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int k = kb + 8 * rr;
+            const char* pp = tile + k * T::ROW_BYTES + (((c >> 5) ^ T::swz(k)) << 5) + (c & 31);
+            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(pp));
+            out[2 * rr] = (uint32_t)v.x;
+            out[2 * rr + 1] = (uint32_t)v.y;
+        }
+        return out;
     }
 }
 
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_op(const typename FragT<DT == DT_E4M3 ? 1 : 2>::type& a,
+                                          const typename FragT<DT == DT_E4M3 ? 1 : 2>::type& b,
+                                          const f32x16& c) {
+    if constexpr (DT == DT_E4M3) {
+        // format 0 = e4m3 for both operands; E8M0 block scale 0x7F = 2^0
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c, 0, 0, 0, 0x7F7F7F7F, 0,
+            0x7F7F7F7F);
+    } else {
+        return mfma16<DT>(a, b, c);
+    }
+}
+
+// BK is in elements.  Output type: DT for 16-bit operands, bf16 for e4m3.
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_dma_kernel(const Gemm16Params p) {
+__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16Params p) {
+    constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
+    constexpr int DT_OUT = DT == DT_E4M3 ? DT_BF16 : DT;
+    constexpr int KSTEP = ESZ == 2 ? 16 : 64;
+    using Frag = typename FragT<ESZ>::type;
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int KS = BK / 16;
-    static_assert(KS % 2 == 0, "k-steps per tile must be even (fragment double buffer)");
+    constexpr int KS = BK / KSTEP;
+    static_assert(BK % KSTEP == 0 && KS % 2 == 0, "k-steps per tile must be even");
     constexpr bool KCA = !TA, KCB = TB;          // k-contiguous operands
-    using TA_ = DmaTile<KCA, BM, BK>;
-    using TB_ = DmaTile<KCB, BN, BK>;
+    using TA_ = DmaTile<KCA, BM, BK, ESZ>;
+    using TB_ = DmaTile<KCB, BN, BK, ESZ>;
     constexpr int STAGE = TA_::BYTES + TB_::BYTES;
     static_assert(S * STAGE <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
@@ -152,11 +221,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_dma_kernel(const Gemm1
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wm = wave % WM, wn = wave / WM;
 
-    DmaStream<KCA, BM, BK, NW> da;
-    DmaStream<KCB, BN, BK, NW> db;
-    da.init(p.A, p.lda, m0, kbeg, wave, lane);
-    db.init(p.B, p.ldb, n0, kbeg, wave, lane);
-    constexpr int NL = DmaStream<KCA, BM, BK, NW>::NI + DmaStream<KCB, BN, BK, NW>::NI;
+    DmaStream<KCA, BM, BK, ESZ, NW> da;
+    DmaStream<KCB, BN, BK, ESZ, NW> db;
+    da.init(p.A, p.lda, m0, p.M, kbeg, wave, lane);
+    db.init(p.B, p.ldb, n0, p.N, kbeg, wave, lane);
+    constexpr int NL = DmaStream<KCA, BM, BK, ESZ, NW>::NI + DmaStream<KCB, BN, BK, ESZ, NW>::NI;
 
     f32x16 acc[FN][FM];
 #pragma unroll
@@ -166,19 +235,20 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_dma_kernel(const Gemm1
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    u32x4 fa[2][FM], fb[2][FN];
-    auto read_all = [&](const char* st, int s, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+    Frag fa[2][FM], fb[2][FN];
+    auto read_all = [&](const char* st, int s, Frag (&af)[FM], Frag (&bf)[FN]) {
 #pragma unroll
-        for (int tm = 0; tm < FM; ++tm) af[tm] = read_frag<KCA, BM, BK>(st, wm * TM + tm * 32, s, lane);
+        for (int tm = 0; tm < FM; ++tm)
+            af[tm] = read_frag<KCA, BM, BK, ESZ>(st, wm * TM + tm * 32, s, lane);
 #pragma unroll
         for (int tn = 0; tn < FN; ++tn)
-            bf[tn] = read_frag<KCB, BN, BK>(st + TA_::BYTES, wn * TN + tn * 32, s, lane);
+            bf[tn] = read_frag<KCB, BN, BK, ESZ>(st + TA_::BYTES, wn * TN + tn * 32, s, lane);
     };
-    auto mfma_all = [&](const u32x4 (&af)[FM], const u32x4 (&bf)[FN]) {
+    auto mfma_all = [&](const Frag (&af)[FM], const Frag (&bf)[FN]) {
 #pragma unroll
         for (int tn = 0; tn < FN; ++tn)
 #pragma unroll
-            for (int tm = 0; tm < FM; ++tm) acc[tn][tm] = mfma16<DT>(bf[tn], af[tm], acc[tn][tm]);
+            for (int tm = 0; tm < FM; ++tm) acc[tn][tm] = mfma_op<DT>(bf[tn], af[tm], acc[tn][tm]);
     };
     auto issue = [&](int t) {
         char* st = smem + (t % S) * STAGE;
@@ -197,7 +267,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_dma_kernel(const Gemm1
         read_all(smem, 0, fa[0], fb[0]);
 
         constexpr int NMF = FM * FN;
-        constexpr int NRD = (KCA ? FM : 2 * FM) + (KCB ? FN : 2 * FN);
+        constexpr int RD_KC = ESZ == 2 ? 1 : 2, RD_RC = ESZ == 2 ? 2 : 4;
+        constexpr int NRD = (KCA ? RD_KC : RD_RC) * FM + (KCB ? RD_KC : RD_RC) * FN;
         for (int t = 0; t < nkt; ++t) {
             const char* cur = smem + (t % S) * STAGE;
             const bool ahead = t + S - 1 < nkt;
@@ -223,7 +294,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_dma_kernel(const Gemm1
         }
     }
 
-    epilogue16<DT, EPI, true, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN, lane);
+    epilogue16<DT_OUT, EPI, true, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
+                                         lane);
 }
 
 }  // namespace sg

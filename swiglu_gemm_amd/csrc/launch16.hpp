@@ -1,6 +1,6 @@
-// launch16.hpp -- launchers for every (configuration, transpose, epilogue) of the
-// 16-bit MFMA GEMM kernels.  Instantiated once per dtype (inst_f16.hip,
-// inst_bf16.hip) so the two compile in parallel.
+// launch16.hpp -- launchers for every (configuration, epilogue) of the MFMA GEMM
+// kernels (16-bit and e4m3 operands) for one (dtype, transpose pair).  Each pair is instantiated in its
+// own translation unit (inst_*.hip) so they compile in parallel.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,42 +19,46 @@ inline hipError_t launch_grid(Kern k, const Gemm16Params& p, int splits, int thr
     return hipGetLastError();
 }
 
+template <int DT, bool TA, bool TB, int EPI, int DMA, int BM, int BN, int BK, int S, int WM, int WN>
+inline hipError_t launch_one(const Gemm16Params& p, int splits, hipStream_t st) {
+    constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
+    if constexpr (DMA || DT == DT_E4M3) {
+        if constexpr (dma_tile_ok(!TA, BM, BK, ESZ, WM * WN) && dma_tile_ok(TB, BN, BK, ESZ, WM * WN))
+            return launch_grid(gemm_dma_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
+                               64 * WM * WN, st);
+        else
+            return hipErrorInvalidValue;
+    } else
+        return launch_grid(gemm16_kernel<DT, TA, TB, EPI, BM, BN, WM, WN>, p, splits,
+                           64 * WM * WN, st);
+}
+
 template <int DT, bool TA, bool TB, int EPI>
 hipError_t launch16_cfg(int cfg, const Gemm16Params& p, int splits, hipStream_t st) {
-    switch (cfg) {
-#define SG_REG(ID, BM, BN, WM, WN) \
-    case ID: return launch_grid(gemm16_kernel<DT, TA, TB, EPI, BM, BN, WM, WN>, p, splits, 64 * WM * WN, st);
-#define SG_DMA(ID, BM, BN, BK, S, WM, WN) \
-    case ID: return launch_grid(gemm16_dma_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits, 64 * WM * WN, st);
-        SG_REG(0, 256, 256, 2, 2)
-        SG_REG(1, 256, 256, 2, 4)
-        SG_REG(2, 128, 128, 2, 2)
-        SG_DMA(3, 256, 256, 32, 4, 2, 2)
-        SG_DMA(4, 256, 256, 32, 4, 2, 4)
-        SG_DMA(5, 256, 256, 64, 2, 2, 2)
-        SG_DMA(6, 128, 128, 32, 4, 2, 2)
-        SG_DMA(7, 128, 128, 64, 3, 2, 2)
-#undef SG_REG
-#undef SG_DMA
-        default: return hipErrorInvalidValue;
+#define SG_CASE(ID, DMA, BM, BN, BK, S, WM, WN) \
+    case ID: return launch_one<DT, TA, TB, EPI, DMA, BM, BN, BK, S, WM, WN>(p, splits, st);
+    if constexpr (DT == DT_E4M3) {
+        switch (cfg) {
+            SG_CONFIGS_E4M3(SG_CASE)
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (cfg) {
+            SG_CONFIGS(SG_CASE)
+            default: return hipErrorInvalidValue;
+        }
     }
+#undef SG_CASE
 }
 
 // epi: EPI_GEMM / EPI_PARTIAL for any transpose pair; EPI_SWIGLU for NN only.
-template <int DT>
-hipError_t launch16_dt(bool ta, bool tb, int epi, int cfg, const Gemm16Params& p, int splits,
-                       hipStream_t st) {
-    if (epi == EPI_SWIGLU) return launch16_cfg<DT, false, false, EPI_SWIGLU>(cfg, p, splits, st);
-    if (epi == EPI_GEMM) {
-        if (!ta && !tb) return launch16_cfg<DT, false, false, EPI_GEMM>(cfg, p, splits, st);
-        if (!ta && tb) return launch16_cfg<DT, false, true, EPI_GEMM>(cfg, p, splits, st);
-        if (ta && !tb) return launch16_cfg<DT, true, false, EPI_GEMM>(cfg, p, splits, st);
-        return launch16_cfg<DT, true, true, EPI_GEMM>(cfg, p, splits, st);
-    }
-    if (!ta && !tb) return launch16_cfg<DT, false, false, EPI_PARTIAL>(cfg, p, splits, st);
-    if (!ta && tb) return launch16_cfg<DT, false, true, EPI_PARTIAL>(cfg, p, splits, st);
-    if (ta && !tb) return launch16_cfg<DT, true, false, EPI_PARTIAL>(cfg, p, splits, st);
-    return launch16_cfg<DT, true, true, EPI_PARTIAL>(cfg, p, splits, st);
+template <int DT, bool TA, bool TB>
+hipError_t launch16_tr(int epi, int cfg, const Gemm16Params& p, int splits, hipStream_t st) {
+    if constexpr (!TA && !TB)
+        if (epi == EPI_SWIGLU) return launch16_cfg<DT, TA, TB, EPI_SWIGLU>(cfg, p, splits, st);
+    if (epi == EPI_GEMM) return launch16_cfg<DT, TA, TB, EPI_GEMM>(cfg, p, splits, st);
+    if (epi == EPI_PARTIAL) return launch16_cfg<DT, TA, TB, EPI_PARTIAL>(cfg, p, splits, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace sg

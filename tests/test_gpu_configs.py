@@ -14,7 +14,7 @@ from helpers import assert_close, bits_equal, from_dev, split_count, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-NCFG = 8
+NCFG = 14
 TRANS = ["NN", "NT", "TN", "TT"]
 
 

@@ -1,0 +1,164 @@
+"""GPU parity of the OCP e4m3 path (fused SwiGLU-GEMM and GEMM) against the fp64
+oracle, through the C ABI.
+
+Workload: A[M x 4096] ~ N(0,1), W1, W2 [4096 x 11008] ~ N(0, 0.02^2), each tensor
+quantised per tensor (s = amax/448, W1 and W2 share one scale as they form one
+W_fused), W_fused [4096 x 22016], Y bf16, M in {1, 16, 256, 4096}.  The oracle
+reads the same codes and scales ("GEMM o Coração Matemático" §12.4: value =
+s * code)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from swiglu_gemm_amd import inputs
+from helpers import assert_close, bits_equal, from_dev, split_count, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+E4M3_CFGS = [14, 15, 16, 17]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import swiglu_gemm_amd as sg
+    sg.lib()
+    yield
+    os.environ.pop("SG_FORCE_CONFIG", None)
+
+
+def run_swiglu8(pb, Wf, M, N, K):
+    import swiglu_gemm_amd as sg
+    A = to_dev(pb["A"], "e4m3")
+    W = to_dev(Wf, "e4m3")
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    print("swiglu e4m3 M=%d N=%d K=%d" % (M, N, K), flush=True)
+    sg.swiglu_gemm(A, W, Y, pb["scale_a"], pb["scale_w"])
+    torch.cuda.synchronize()
+    return from_dev(Y), sg.last_config()
+
+
+@pytest.fixture(scope="module")
+def weights():
+    N, K = 11008, 4096
+    pb = inputs.swiglu_problem(5, 1, N, K, "e4m3")
+    return pb, oracle.interleave(pb["W1"], pb["W2"])
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_swiglu_e4m3_skinny_full(M, weights):
+    N, K = 11008, 4096
+    wb, Wf = weights
+    pb = inputs.swiglu_problem(5, M, N, K, "e4m3")
+    assert pb["scale_w"] == wb["scale_w"]
+    y, cfg = run_swiglu8(pb, Wf, M, N, K)
+    ref = oracle.swiglu(M, N, K, pb["A"], Wf, "e4m3", pb["scale_a"], pb["scale_w"])
+    assert_close(oracle.decode(y, "bf16"), ref, "e4m3", K, "swiglu e4m3 M=%d %s" % (M, cfg))
+
+
+@pytest.mark.parametrize("M", [256, 4096])
+def test_swiglu_e4m3_sampled_rows(M, weights):
+    N, K = 11008, 4096
+    _, Wf = weights
+    pb = inputs.swiglu_problem(5, M, N, K, "e4m3")
+    y, cfg = run_swiglu8(pb, Wf, M, N, K)
+    got = oracle.decode(y, "bf16")
+    assert np.all(np.isfinite(got))
+    gen = np.random.default_rng(M)
+    rows = sorted(set([0, 1, 31, 32, 127, 128, M // 2, M - 1] + list(gen.integers(0, M, size=8))))
+    ref = oracle.swiglu(len(rows), N, K, pb["A"][rows, :], Wf, "e4m3", pb["scale_a"], pb["scale_w"])
+    assert_close(got[rows, :], ref, "e4m3", K, "swiglu e4m3 M=%d %s" % (M, cfg))
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+@pytest.mark.parametrize("cfg", E4M3_CFGS)
+def test_swiglu_e4m3_every_config(cfg, splits):
+    import swiglu_gemm_amd as sg
+    M, N, K = 96, 640, 1024            # ragged M for every tile height
+    pb = inputs.swiglu_problem(80 + cfg, M, N, K, "e4m3")
+    Wf = oracle.interleave(pb["W1"], pb["W2"])
+    os.environ["SG_FORCE_CONFIG"] = "%d,%d" % (cfg, splits)
+    try:
+        y1, desc = run_swiglu8(pb, Wf, M, N, K)
+        y2, _ = run_swiglu8(pb, Wf, M, N, K)
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    assert split_count(desc) == splits, desc
+    assert bits_equal(y1, y2)
+    ref = oracle.swiglu(M, N, K, pb["A"], Wf, "e4m3", pb["scale_a"], pb["scale_w"])
+    assert_close(oracle.decode(y1, "bf16"), ref, "e4m3", K, desc)
+
+
+@pytest.mark.parametrize("tr", ["NN", "NT", "TN", "TT"])
+@pytest.mark.parametrize("cfg", E4M3_CFGS + [None])
+def test_gemm_e4m3_configs_and_transposes(cfg, tr):
+    import swiglu_gemm_amd as sg
+    M, N, K = 160, 384, 1024
+    ta, tb = tr
+    p = inputs.gemm_problem(90, ta, tb, M, N, K, "e4m3", "normal", ld_mode="tight",
+                            c_dtype="bf16")
+    alpha = p["scale_a"] * p["scale_b"] * 0.5
+    A, B, C = to_dev(p["A"], "e4m3"), to_dev(p["B"], "e4m3"), to_dev(p["C"], "bf16")
+    if cfg is not None:
+        os.environ["SG_FORCE_CONFIG"] = "%d,0" % cfg
+    try:
+        sg.gemm(A, B, C, alpha=alpha, beta=0.25, transA=ta, transB=tb, M=M, N=N, K=K,
+                lda=p["lda"], ldb=p["ldb"], ldc=p["ldc"], dtype=3)
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    if cfg is not None and not (ta == "T" and cfg in (16, 17)):
+        assert "cfg=%d " % cfg in desc, desc
+    ref = oracle.gemm(ta, tb, M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], 0.25, p["C"],
+                      p["ldc"], "e4m3", c_dtype="bf16")
+    assert_close(oracle.decode(from_dev(C), "bf16"), ref, "e4m3", K, desc)
+
+
+@pytest.mark.parametrize("shape", [(37, 50, 70), (1, 1, 1), (5, 300, 130)])
+def test_generic_e4m3_odd_shapes(shape):
+    """K tails and odd sizes take the generic e4m3 kernels."""
+    import swiglu_gemm_amd as sg
+    M, N, K = shape
+    p = inputs.gemm_problem(91, "N", "N", M, N, K, "e4m3", "normal", c_dtype="bf16")
+    A, B, C = to_dev(p["A"], "e4m3"), to_dev(p["B"], "e4m3"), to_dev(p["C"], "bf16")
+    sg.gemm(A, B, C, alpha=1.0, beta=0.0, M=M, N=N, K=K, lda=p["lda"], ldb=p["ldb"],
+            ldc=p["ldc"], dtype=3)
+    torch.cuda.synchronize()
+    desc = sg.last_config()
+    ref = oracle.gemm("N", "N", M, N, K, 1.0, p["A"], p["lda"], p["B"], p["ldb"], 0.0, p["C"],
+                      p["ldc"], "e4m3", c_dtype="bf16")
+    assert_close(oracle.decode(from_dev(C), "bf16"), ref, "e4m3", K, desc)
+    pb = inputs.swiglu_problem(92, M, N, K, "e4m3")
+    Wf = oracle.interleave(pb["W1"], pb["W2"])
+    y, desc = run_swiglu8(pb, Wf, M, N, K)
+    ref = oracle.swiglu(M, N, K, pb["A"], Wf, "e4m3", pb["scale_a"], pb["scale_w"])
+    assert_close(oracle.decode(y, "bf16"), ref, "e4m3", K, desc)
+
+
+@pytest.mark.parametrize("M", [1, 16, 256])
+def test_swiglu_e4m3_one_hot_bit_exact(M):
+    """Unit scales; W1, W2 select columns of A.  Gate sources are powers of two
+    in [32, 256] (exact in e4m3; SiLU(g) rounds to g in fp32), up sources are
+    integers in [-3, 3]: Y = g*u exactly in bf16."""
+    N, K = 512, 1024
+    gen = np.random.default_rng(M + 7)
+    half = K // 2
+    A = np.zeros((M, K))
+    A[:, :half] = 2.0 ** gen.integers(5, 9, size=(M, half))
+    A[:, half:] = gen.integers(-3, 4, size=(M, K - half))
+    pi1 = gen.integers(0, half, size=N)
+    pi2 = half + gen.integers(0, K - half, size=N)
+    W1 = np.zeros((K, N))
+    W2 = np.zeros((K, N))
+    W1[pi1, np.arange(N)] = 1.0
+    W2[pi2, np.arange(N)] = 1.0
+    pb = dict(A=inputs.to_storage(A, "e4m3"), scale_a=1.0, scale_w=1.0)
+    Wf = oracle.interleave(inputs.to_storage(W1, "e4m3"), inputs.to_storage(W2, "e4m3"))
+    y, cfg = run_swiglu8(pb, Wf, M, N, K)
+    assert np.array_equal(oracle.decode(y, "bf16"), A[:, pi1] * A[:, pi2]), cfg
