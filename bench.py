@@ -1,25 +1,32 @@
-"""Benchmark: fp16 8192^3 GEMM (headline) and the fused SwiGLU-GEMM at M = 2048.
+"""Benchmark: fp16 8192^3 GEMM (headline) and the fused SwiGLU-GEMM (M = 2048 and
+the other workload sizes), on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
 
 A step is one sg_gemm call C = alpha*A@B + beta*C (NN, fp16 in, fp32 accumulate,
 fp16 out, M = N = K = 8192, alpha = 1, beta = 0) on inputs already resident in
-HBM: host validation, tile loads, MFMA main loop and epilogue.  Timing uses HIP
-events recorded on the stream the library launches on (torch's current stream),
-W untimed warm-up steps, then exactly K timed steps between two synchronisations.
-Three input sets are rotated so the 256 MB last-level cache cannot keep one set
-resident across steps.
+HBM: host validation, tile loads, MFMA main loop and epilogue (one kernel
+launch).  Timing uses HIP events recorded on the stream the library launches on
+(torch's current stream): W untimed warm-up steps, then exactly K timed steps
+between two synchronisations.  Three input sets are rotated so the 256 MB
+last-level cache cannot keep one set resident across steps.
 
-Also reported (same run): the fused SwiGLU-GEMM, bf16, A[2048 x 896] x
-W_fused[896 x 9728] -> Y[2048 x 4864], against this library's unfused path
-(two sg_gemm calls writing Gate and Up, then sg_silu_mul) and torch eager as
+Also reported, same run: the fused SwiGLU-GEMM (bf16: A[M x 896], W_fused[896 x
+9728], M in {128, 512, 2048, 8192}; e4m3 with per-tensor scales: A[M x 4096],
+W_fused[4096 x 22016], M in {1, 16, 256, 4096}) against this library's unfused
+path (two sg_gemm calls writing Gate and Up, then sg_silu_mul) and torch eager as
 context; and the fp64 CPU oracle timed on a bounded sample of the GEMM rows.
 
 Prints ONE JSON line.
+
+Counter helpers (used to produce the committed HBM-traffic figure):
+    python bench.py --pmc-probe            # copy of a known size, then 3 GEMM launches
+    python bench.py --pmc-summarize FETCH.csv WRITE.csv   # -> profiles/traffic_*.json
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -33,9 +40,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "TFLOPS & % of MFMA peak: fp16 8192³ GEMM; fused SwiGLU-GEMM at M=2048"
-PEAK_F16_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA peak
+PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0}   # MI355X dense MFMA TFLOP/s
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm16_f16_nn_8192.json")
+COPY_BYTES = 512 * 1024 * 1024          # calibration copy: reads and writes this many bytes
 
 
 def kernel_source_hash() -> str:
@@ -76,6 +84,8 @@ def time_steps(fn, steps, warmup, torch):
 
 def to_dev(bits, dtype, torch):
     t = torch.from_numpy(np.ascontiguousarray(bits))
+    if dtype == "e4m3":
+        return t.view(torch.float8_e4m3fn).to("cuda:0")
     t = t.view(torch.int16).view(torch.float16 if dtype == "f16" else torch.bfloat16)
     return t.to("cuda:0")
 
@@ -102,46 +112,127 @@ def cpu_baseline(p, M, N, K, budget_s=12.0):
                       "oracle incl. decode, %.1f s" % (done, M, M, N, K, t_total)}
 
 
-def bench_swiglu(torch, sg, inputs, steps, warmup):
-    M, N, K = 2048, 4864, 896
+def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True):
+    """Fused vs this library's unfused path (vs torch eager) for one SwiGLU size."""
+    workload = 4 if dtype == "bf16" else 5
+    nsets = 2
     sets = []
-    for r in range(4):
-        pb = inputs.swiglu_problem(4, M + r, N, K, "bf16")      # distinct seeds per set
-        A = to_dev(pb["A"][:M], "bf16", torch)
-        W1 = to_dev(pb["W1"], "bf16", torch)
-        W2 = to_dev(pb["W2"], "bf16", torch)
+    for r in range(nsets):
+        pb = inputs.swiglu_problem(workload, M, N, K, dtype) if r == 0 else \
+            inputs.swiglu_problem(100 + workload, M, N, K, dtype)
+        A = to_dev(pb["A"], dtype, torch)
+        W1 = to_dev(pb["W1"], dtype, torch)
+        W2 = to_dev(pb["W2"], dtype, torch)
         Wf = sg.interleave_gate_up(W1, W2)
-        sets.append((A, W1, W2, Wf))
+        sets.append((A, W1, W2, Wf, pb["scale_a"], pb["scale_w"]))
     Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     G = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     U = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
 
     def fused(i):
-        A, _, _, Wf = sets[i % 4]
-        sg.swiglu_gemm(A, Wf, Y)
+        A, _, _, Wf, sa, sw = sets[i % nsets]
+        sg.swiglu_gemm(A, Wf, Y, sa, sw)
 
     def unfused(i):
-        A, W1, W2, _ = sets[i % 4]
-        sg.gemm(A, W1, G)
-        sg.gemm(A, W2, U)
+        A, W1, W2, _, sa, sw = sets[i % nsets]
+        sg.gemm(A, W1, G, alpha=sa * sw)
+        sg.gemm(A, W2, U, alpha=sa * sw)
         sg.silu_mul(G, U, Y)
-
-    def eager(i):
-        A, W1, W2, _ = sets[i % 4]
-        torch.nn.functional.silu(A @ W1) * (A @ W2)
 
     t_fused = time_steps(fused, steps, warmup, torch)
     cfg = sg.last_config()
     t_unfused = time_steps(unfused, steps, warmup, torch)
-    t_eager = time_steps(eager, steps, warmup, torch)
+    esz = 1 if dtype == "e4m3" else 2
     flops = 4.0 * M * N * K
+    nbytes = M * K * esz + K * 2 * N * esz + M * N * 2
     tf = flops / (t_fused * 1e-3) / 1e12
-    return {"workload": "fused SwiGLU-GEMM bf16 A[2048x896] W_fused[896x9728] -> Y[2048x4864]",
-            "ms": round(t_fused, 5), "tflops": round(tf, 2),
-            "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4),
-            "unfused_ms": round(t_unfused, 5), "speedup_vs_unfused": round(t_unfused / t_fused, 3),
-            "torch_eager_ms": round(t_eager, 5),
-            "speedup_vs_torch_eager": round(t_eager / t_fused, 3), "kernel_config": cfg}
+    gbs = nbytes / (t_fused * 1e-3) / 1e9
+    out = {"dtype": dtype, "M": M, "N": N, "K": K, "ms": round(t_fused, 5),
+           "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK[dtype], 4),
+           "hbm_gbs_algorithmic": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "unfused_ms": round(t_unfused, 5), "speedup_vs_unfused": round(t_unfused / t_fused, 3),
+           "kernel_config": cfg}
+    if eager and dtype == "bf16":
+        def eager_fn(i):
+            A, W1, W2, _, _, _ = sets[i % nsets]
+            torch.nn.functional.silu(A @ W1) * (A @ W2)
+        t_eager = time_steps(eager_fn, steps, warmup, torch)
+        out["torch_eager_ms"] = round(t_eager, 5)
+        out["speedup_vs_torch_eager"] = round(t_eager / t_fused, 3)
+    return out
+
+
+def gemm_inputs(inputs, torch, M, N, K, nsets):
+    host = inputs.gemm_problem(2, "N", "N", M, N, K, "f16", "normal", scale=1.0 / np.sqrt(K),
+                               beta_zero=True)
+    sets = []
+    for r in range(nsets):
+        if r == 0:
+            A, B = to_dev(host["A"], "f16", torch), to_dev(host["B"], "f16", torch)
+        else:   # further sets: same distribution, other seeds
+            p2 = inputs.gemm_problem(200 + r, "N", "N", M, N, K, "f16", "normal",
+                                     scale=1.0 / np.sqrt(K), beta_zero=True)
+            A, B = to_dev(p2["A"], "f16", torch), to_dev(p2["B"], "f16", torch)
+        C = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+        sets.append((A, B, C))
+    return host, sets
+
+
+def pmc_probe():
+    """Run under rocprofv3 --pmc: one device copy of COPY_BYTES (the calibration
+    kernel), then three launches of the headline GEMM."""
+    import torch
+    import swiglu_gemm_amd as sg
+    from swiglu_gemm_amd import inputs
+    sg.lib()
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    _, sets = gemm_inputs(inputs, torch, 8192, 8192, 8192, 1)
+    A, B, C = sets[0]
+    for _ in range(3):
+        sg.gemm(A, B, C)
+    torch.cuda.synchronize()
+    print("pmc probe done: %s" % sg.last_config(), flush=True)
+
+
+def pmc_summarize(fetch_csv, write_csv):
+    """Turn the two counter runs into HBM bytes per GEMM launch (calibrated by the
+    copy kernel) and write TRAFFIC_FILE."""
+    def per_dispatch(path, counter):
+        rows = list(csv.DictReader(open(path)))
+        agg = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            name = r["Kernel_Name"]
+            agg.setdefault(key, [name, 0.0])
+            agg[key][1] += float(r["Counter_Value"])
+        return [agg[k] for k in sorted(agg)]
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        d = per_dispatch(path, counter)
+        copy = [v for n, v in d if "copy" in n.lower() or "elementwise" in n.lower()]
+        gemm = [v for n, v in d if "gemm" in n and "dma" in n]
+        if not copy or not gemm:
+            raise SystemExit("counter file %s lacks the copy or GEMM dispatches" % path)
+        copy_kib = max(copy)                     # the 512 MiB copy dominates
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        out[counter] = {"gemm_kib_per_launch": sum(gemm) / len(gemm),
+                        "copy_kib": copy_kib, "scale_factor": factor,
+                        "gemm_bytes_per_launch": sum(gemm) / len(gemm) * 1024.0 * factor}
+    total = out["FETCH_SIZE"]["gemm_bytes_per_launch"] + out["WRITE_SIZE"]["gemm_bytes_per_launch"]
+    res = {"kernel_src_sha": kernel_source_hash(), "workload": "fp16 GEMM NN 8192^3",
+           "algorithmic_bytes_per_launch": 3 * 8192 * 8192 * 2,
+           "hbm_bytes_per_launch": total, "counters": out}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
 
 
 def main():
@@ -150,13 +241,21 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-swiglu", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline GEMM and SwiGLU M=2048 only")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--pmc-probe", action="store_true")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only (the library is single-GPU); --gpus %d is not "
               "supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
+    if args.pmc_probe:
+        pmc_probe()
+        return
 
     import torch
     import swiglu_gemm_amd as sg
@@ -166,18 +265,7 @@ def main():
 
     M = N = K = 8192
     print("bench: generating inputs", file=sys.stderr, flush=True)
-    host = inputs.gemm_problem(2, "N", "N", M, N, K, "f16", "normal", scale=1.0 / np.sqrt(K),
-                               beta_zero=True)
-    sets = []
-    for r in range(3):
-        if r == 0:
-            A, B = to_dev(host["A"], "f16", torch), to_dev(host["B"], "f16", torch)
-        else:   # further sets: same distribution, other seeds
-            p2 = inputs.gemm_problem(200 + r, "N", "N", M, N, K, "f16", "normal",
-                                     scale=1.0 / np.sqrt(K), beta_zero=True)
-            A, B = to_dev(p2["A"], "f16", torch), to_dev(p2["B"], "f16", torch)
-        C = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
-        sets.append((A, B, C))
+    host, sets = gemm_inputs(inputs, torch, M, N, K, 3)
 
     def step(i):
         A, B, C = sets[i % 3]
@@ -189,6 +277,8 @@ def main():
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic()
+    del sets
+    torch.cuda.empty_cache()
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -197,14 +287,24 @@ def main():
         "config": {"workload": "fp16 GEMM NN M=N=K=8192 alpha=1 beta=0, fp32 accumulate, fp16 out; "
                                "A,B ~ N(0,1)/sqrt(K)", "M": M, "N": N, "K": K,
                    "kernel_config": cfg, "input_sets_rotated": 3},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_F16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "gemm16_kernel (one launch per step)",
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK["f16"],
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK["f16"], 4),
+                     "traffic": traffic, "kernel": "gemm_dma_kernel (one launch per step)",
                      "algorithmic_flops_per_launch": flops},
     }
-    if not args.no_swiglu:
-        print("bench: timing SwiGLU M=2048", file=sys.stderr, flush=True)
-        out["swiglu_m2048"] = bench_swiglu(torch, sg, inputs, args.steps, args.warmup)
+    sizes = [("bf16", 2048, 4864, 896)]
+    if not args.quick:
+        sizes = [("bf16", m, 4864, 896) for m in (128, 512, 2048, 8192)] + \
+                [("e4m3", m, 11008, 4096) for m in (1, 16, 256, 4096)]
+    sw = []
+    for dt, m, n, k in sizes:
+        print("bench: SwiGLU %s M=%d" % (dt, m), file=sys.stderr, flush=True)
+        sw.append(bench_swiglu(torch, sg, inputs, dt, m, n, k, max(10, args.steps // 2),
+                               args.warmup))
+        torch.cuda.empty_cache()
+    out["swiglu_m2048"] = [s for s in sw if s["dtype"] == "bf16" and s["M"] == 2048][0]
+    if len(sw) > 1:
+        out["swiglu_all"] = sw
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(host, M, N, K, args.cpu_budget)
