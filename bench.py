@@ -7,8 +7,9 @@ A step is one sg_gemm call C = alpha*A@B + beta*C (NN, fp16 in, fp32 accumulate,
 fp16 out, M = N = K = 8192, alpha = 1, beta = 0) on inputs already resident in
 HBM: host validation, tile loads, MFMA main loop and epilogue (one kernel
 launch).  Timing uses HIP events recorded on the stream the library launches on
-(torch's current stream): W untimed warm-up steps, then exactly K timed steps
-between two synchronisations.  Three input sets are rotated so the 256 MB
+(torch's current stream): ~0.4 s of untimed spin-up work so the clocks have
+ramped, W untimed warm-up steps, then exactly K timed steps between two
+synchronisations.  Three input sets are rotated so the 256 MB
 last-level cache cannot keep one set resident across steps.
 
 Also reported, same run: the fused SwiGLU-GEMM (bf16: A[M x 896], W_fused[896 x
@@ -68,7 +69,19 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def spin_up(fn, torch, seconds=0.4):
+    """Untimed work before the warm-up steps so the GPU clocks have ramped up."""
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_steps(fn, steps, warmup, torch):
+    spin_up(fn, torch)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()

@@ -116,7 +116,7 @@ struct Problem16 {
 bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
     if (!c.dma || c.e4m3 != (q.esz == 1)) return false;
     if (!q.vec_a || !q.vec_b || q.K % c.BK != 0 || kps % c.BK != 0) return false;
-    const int nw = c.WM * c.WN;
+    const int nw = c.dma == 2 ? 4 : c.WM * c.WN;     // ping-pong: group 0 issues the DMA
     if (!dma_tile_ok(!q.ta, c.BM, c.BK, q.esz, nw) || !dma_tile_ok(q.tb, c.BN, c.BK, q.esz, nw))
         return false;
     if (q.ta && (q.M * q.esz) % 16 != 0) return false;   // A rows hold M elements

@@ -5,7 +5,9 @@ namespace sg {
 
 struct Cfg16 {
     int e4m3;           // 1: e4m3 operands (BK in bytes), 0: fp16 / bf16 operands
-    int dma;            // 1: direct global->LDS ring (gemm16_dma.hpp), 0: register-staged
+    int dma;            // 0: register-staged (gemm16.hpp), 1: direct global->LDS ring
+                        // (gemm16_dma.hpp), 2: the same ring with the 8-wave ping-pong
+                        // schedule (gemm_pingpong.hpp)
     int BM, BN, BK, S;  // tile and LDS stages
     int WM, WN;         // waves along M and N
     const char* name;
@@ -32,6 +34,12 @@ constexpr Cfg16 kCfg16[] = {
     {1, 1, 128, 128, 128, 2, 2, 4, "e4m3 dma 128x128x128 s2 2x4w"},
     {1, 1, 32, 256, 128, 4, 1, 4, "e4m3 dma 32x256x128 s4 1x4w"},
     {1, 1, 32, 128, 128, 4, 1, 4, "e4m3 dma 32x128x128 s4 1x4w"},
+    {0, 2, 256, 256, 64, 2, 4, 2, "pp 256x256x64 s2 4x2w"},
+    {0, 2, 256, 256, 32, 4, 4, 2, "pp 256x256x32 s4 4x2w"},
+    {0, 2, 256, 256, 64, 2, 2, 4, "pp 256x256x64 s2 2x4w"},
+    {1, 2, 256, 256, 128, 2, 4, 2, "e4m3 pp 256x256x128 s2 4x2w"},
+    {0, 2, 128, 256, 64, 2, 2, 4, "pp 128x256x64 s2 2x4w"},
+    {1, 2, 128, 256, 128, 2, 2, 4, "e4m3 pp 128x256x128 s2 2x4w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
@@ -62,13 +70,19 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(10, 1, 256, 256, 64, 2, 4, 2)    \
     X(11, 1, 128, 256, 64, 2, 2, 2)    \
     X(12, 1, 256, 128, 64, 2, 2, 2)    \
-    X(13, 1, 128, 128, 64, 2, 2, 4)
+    X(13, 1, 128, 128, 64, 2, 2, 4)     \
+    X(18, 2, 256, 256, 64, 2, 4, 2)    \
+    X(19, 2, 256, 256, 32, 4, 4, 2)    \
+    X(20, 2, 256, 256, 64, 2, 2, 4)    \
+    X(22, 2, 128, 256, 64, 2, 2, 4)
 
 // the same for every e4m3 row (all direct-to-LDS)
 #define SG_CONFIGS_E4M3(X)             \
     X(14, 1, 256, 256, 128, 2, 4, 2)   \
     X(15, 1, 128, 128, 128, 2, 2, 4)   \
     X(16, 1, 32, 256, 128, 4, 1, 4)    \
-    X(17, 1, 32, 128, 128, 4, 1, 4)
+    X(17, 1, 32, 128, 128, 4, 1, 4)    \
+    X(21, 2, 256, 256, 128, 2, 4, 2)   \
+    X(23, 2, 128, 256, 128, 2, 2, 4)
 
 }  // namespace sg

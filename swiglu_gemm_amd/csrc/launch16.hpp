@@ -8,6 +8,7 @@
 #include "configs16.hpp"
 #include "gemm16.hpp"
 #include "gemm16_dma.hpp"
+#include "gemm_pingpong.hpp"
 
 namespace sg {
 
@@ -22,7 +23,13 @@ inline hipError_t launch_grid(Kern k, const Gemm16Params& p, int splits, int thr
 template <int DT, bool TA, bool TB, int EPI, int DMA, int BM, int BN, int BK, int S, int WM, int WN>
 inline hipError_t launch_one(const Gemm16Params& p, int splits, hipStream_t st) {
     constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
-    if constexpr (DMA || DT == DT_E4M3) {
+    if constexpr (DMA == 2) {
+        if constexpr (dma_tile_ok(!TA, BM, BK, ESZ, 4) && dma_tile_ok(TB, BN, BK, ESZ, 4))
+            return launch_grid(gemm_pp_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
+                               64 * WM * WN, st);
+        else
+            return hipErrorInvalidValue;
+    } else if constexpr (DMA || DT == DT_E4M3) {
         if constexpr (dma_tile_ok(!TA, BM, BK, ESZ, WM * WN) && dma_tile_ok(TB, BN, BK, ESZ, WM * WN))
             return launch_grid(gemm_dma_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
                                64 * WM * WN, st);
