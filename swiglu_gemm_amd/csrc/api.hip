@@ -124,14 +124,17 @@ bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
     return true;
 }
 
-// split lengths are multiples of 128 (a whole number of K tiles for every config)
-int64_t split_len(int64_t K, int splits) { return cdiv(cdiv(K, splits), 128) * 128; }
+// K per split: the K tiles of depth bk dealt out as evenly as whole tiles allow
+int64_t split_len(int64_t K, int splits, int bk) { return cdiv(cdiv(K, bk), splits) * bk; }
 
+// Split K only when the tiles would leave most of the GPU idle: the fp32 partial
+// round trip through memory costs more than it saves otherwise (measured on
+// MI355X for the 128..512-row SwiGLU and 1..16-row e4m3 shapes).
 int pick_splits(const Cfg16& c, const Problem16& q) {
     const int64_t tiles = cdiv(q.M, c.BM) * cdiv(q.N, c.BN);
     int s = 1;
-    if (tiles < kNumCU && q.K >= 1024) {
-        s = (int)cdiv(kNumCU, tiles);
+    if (tiles * 4 <= kNumCU && q.K >= 1024) {
+        s = (int)cdiv(kNumCU / 2, tiles);
         const int64_t max_s = q.K / 512;
         if (s > max_s) s = (int)max_s;
         if (s < 1) s = 1;
@@ -139,27 +142,59 @@ int pick_splits(const Cfg16& c, const Problem16& q) {
     return s;
 }
 
+// 16-bit direct-to-LDS candidates with their measured full-tile rate (TFLOP/s per
+// CU on MI355X, random fp16/bf16 data).  A problem takes the eligible candidate
+// with the least  waves * (tile flops / rate + kTileOverheadUs), waves = the
+// number of rounds of one work-group per CU, which weighs tile size (operand
+// re-reads, MFMA efficiency) against the idle CUs of the last round.
+struct Cand16 {
+    int id;
+    double tf_per_cu;
+};
+constexpr Cand16 kCand16[] = {{10, 4.7}, {24, 5.0}, {13, 3.6}, {6, 3.4}};
+constexpr double kTileOverheadUs = 3.0;   // pipeline fill + epilogue per tile
+
+double est_us(const Cfg16& c, const Problem16& q, int splits, double tf_per_cu) {
+    const int64_t items = cdiv(q.M, c.BM) * cdiv(q.N, c.BN) * splits;
+    const double waves = (double)cdiv(items, kNumCU);
+    const double item_flops = 2.0 * c.BM * c.BN * (double)split_len(q.K, splits, c.BK);
+    return waves * (item_flops / (tf_per_cu * 1e6) + kTileOverheadUs);
+}
+
 // Choose a configuration and split count.  16-bit problems fall back to a
-// register-staged configuration when a DMA configuration does not fit; e4m3
-// problems report -1 (the caller then runs the generic kernel).
+// register-staged configuration when no DMA configuration fits; e4m3 problems
+// report -1 (the caller then runs the generic kernel).
 void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
     int cfg = -1, splits = 0;
     const bool e4m3 = q.esz == 1;
     const bool forced = forced_config(&cfg, &splits) && cfg >= 0 && cfg < kNumCfg16 &&
                         (kCfg16[cfg].e4m3 != 0) == e4m3;
     if (!forced) {
-        // measured on MI355X: 256x256 tiles once there are >= 2 full waves of
-        // them, else 128x128 tiles (8 waves when M allows two 128-row tiles);
-        // e4m3 with few rows uses 32-row tiles
-        const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
-        if (!e4m3)
-            cfg = big >= 2 * kNumCU ? 10 : (q.M >= 256 ? 13 : 6);
-        else
-            cfg = big >= 2 * kNumCU ? 14 : (q.M >= 256 ? 15 : (cdiv(q.N, 256) >= 128 ? 16 : 17));
         splits = 0;
+        if (e4m3) {
+            // measured on MI355X: 256x256 tiles once there are >= 2 full rounds of
+            // them, else 128x128 tiles while M allows two 128-row tiles, else
+            // 32-row tiles (256 wide when that still gives half a round)
+            const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
+            cfg = big >= 2 * kNumCU ? 14
+                                    : (q.M >= 256 ? 15 : (cdiv(q.N, 256) >= 128 ? 16 : 17));
+        } else {
+            double best = 0.0;
+            for (const Cand16& cand : kCand16) {
+                const Cfg16& c = kCfg16[cand.id];
+                const int sp = pick_splits(c, q);
+                if (!dma_ok(c, q, split_len(q.K, sp, c.BK))) continue;
+                const double t = est_us(c, q, sp, cand.tf_per_cu);
+                if (cfg < 0 || t < best) {
+                    cfg = cand.id;
+                    best = t;
+                }
+            }
+            if (cfg < 0) cfg = cdiv(q.M, 256) * cdiv(q.N, 256) >= kNumCU ? 0 : 2;
+        }
     }
     if (splits <= 0) splits = pick_splits(kCfg16[cfg], q);
-    if (!dma_ok(kCfg16[cfg], q, split_len(q.K, splits))) {
+    if (!dma_ok(kCfg16[cfg], q, split_len(q.K, splits, kCfg16[cfg].BK))) {
         if (kCfg16[cfg].dma && !e4m3 && !kCfg16[cfg].e4m3) {
             cfg = kCfg16[cfg].BM >= 256 ? 0 : 2;
             if (!forced) splits = pick_splits(kCfg16[cfg], q);
@@ -194,14 +229,14 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
     p.tiles_n = (int)cdiv(q.N, c.BN);
     p.group_m = group_m();
     if (splits > 1) {
-        p.k_per_split = (int)split_len(q.K, splits);
+        p.k_per_split = (int)split_len(q.K, splits, c.BK);
         splits = (int)cdiv(q.K, p.k_per_split);
     }
     *splits_used = splits;
     if (splits <= 1) {
         p.C = out;
         p.vec_c = out_vec;
-        p.k_per_split = (int)split_len(q.K, 1);
+        p.k_per_split = (int)split_len(q.K, 1, c.BK);
         set_last(what, cfg, 1);
         return launch16_dt<DT>(ta, tb, epi, cfg, p, 1, st);
     }
@@ -426,6 +461,7 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
     Problem16 q{M, N2, K, (bool)p.vec_a, (bool)p.vec_b, false, false, esz};
     // Y stores are 4 or 8 bytes wide depending on the kernel: require the stricter
     const bool yvec = aligned(Y, 8) && (N % 4 == 0);
+    p.epi_flags = aligned(Y, 16) && N % 8 == 0 ? EPI_Y16 : 0;
     int splits = 1;
     hipError_t e;
     if (dtype == SG_F8E4M3) {

@@ -40,19 +40,30 @@ constexpr Cfg16 kCfg16[] = {
     {1, 2, 256, 256, 128, 2, 4, 2, "e4m3 pp 256x256x128 s2 4x2w"},
     {0, 2, 128, 256, 64, 2, 2, 4, "pp 128x256x64 s2 2x4w"},
     {1, 2, 128, 256, 128, 2, 2, 4, "e4m3 pp 128x256x128 s2 2x4w"},
+    {0, 1, 256, 320, 64, 2, 4, 2, "dma 256x320x64 s2 4x2w"},
+    {0, 2, 256, 320, 64, 2, 4, 2, "pp 256x320x64 s2 4x2w"},
+    {0, 2, 256, 320, 32, 4, 4, 2, "pp 256x320x32 s4 4x2w"},
+    {0, 1, 256, 256, 32, 5, 4, 2, "dma 256x256x32 s5 4x2w"},
+    {0, 1, 256, 256, 32, 5, 2, 4, "dma 256x256x32 s5 2x4w"},
+    {0, 2, 256, 256, 32, 5, 4, 2, "pp 256x256x32 s5 4x2w"},
+    {0, 1, 128, 128, 64, 5, 2, 4, "dma 128x128x64 s5 2x4w"},
+    {0, 1, 128, 128, 32, 8, 2, 2, "dma 128x128x32 s8 2x2w"},
+    {0, 1, 128, 256, 64, 3, 2, 4, "dma 128x256x64 s3 2x4w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
 constexpr int kFirstCfgE4M3 = 14;
 
-// Whether the direct-to-LDS kernel supports an operand tile: KC (k-contiguous)
-// rows of 64 or 128 bytes, row-contiguous rows of 128..1024 bytes, a whole number
-// of 1 KiB DMA blocks per wave.
+// Whether the direct-to-LDS kernel supports an operand tile: k-contiguous rows of
+// 64 or 128 bytes; row-contiguous rows of 128..1024 bytes made of an even number
+// of 32-byte units (what the bank swizzles cover); a whole number of 1 KiB DMA
+// blocks per issuing wave.
 constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     const int row_bytes = kc ? bk * esz : rows * esz;
     const int bytes = rows * bk * esz;
-    return (kc ? (row_bytes == 64 || row_bytes == 128) : (row_bytes >= 128 && row_bytes <= 1024)) &&
-           bytes % 1024 == 0 && (bytes / 1024) % nwaves == 0;
+    const bool rc_ok = row_bytes >= 128 && row_bytes <= 1024 && row_bytes % 64 == 0;
+    return (kc ? (row_bytes == 64 || row_bytes == 128) : rc_ok) && bytes % 1024 == 0 &&
+           (bytes / 1024) % nwaves == 0;
 }
 
 // X(id, dma, BM, BN, BK, S, WM, WN) for every 16-bit row of kCfg16
@@ -74,7 +85,16 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(18, 2, 256, 256, 64, 2, 4, 2)    \
     X(19, 2, 256, 256, 32, 4, 4, 2)    \
     X(20, 2, 256, 256, 64, 2, 2, 4)    \
-    X(22, 2, 128, 256, 64, 2, 2, 4)
+    X(22, 2, 128, 256, 64, 2, 2, 4)    \
+    X(24, 1, 256, 320, 64, 2, 4, 2)    \
+    X(25, 2, 256, 320, 64, 2, 4, 2)    \
+    X(26, 2, 256, 320, 32, 4, 4, 2)    \
+    X(27, 1, 256, 256, 32, 5, 4, 2)    \
+    X(28, 1, 256, 256, 32, 5, 2, 4)    \
+    X(29, 2, 256, 256, 32, 5, 4, 2)    \
+    X(30, 1, 128, 128, 64, 5, 2, 4)    \
+    X(31, 1, 128, 128, 32, 8, 2, 2)    \
+    X(32, 1, 128, 256, 64, 3, 2, 4)
 
 // the same for every e4m3 row (all direct-to-LDS)
 #define SG_CONFIGS_E4M3(X)             \

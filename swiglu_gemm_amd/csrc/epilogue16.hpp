@@ -9,10 +9,11 @@
 //                round-to-nearest-even conversion ("GEMM o Coração Matemático" §1).
 //   EPI_SWIGLU   y = SiLU(s*gate) * (s*up) for each fused column pair (2n, 2n+1)
 //                ("Resumo Técnico: Sobreposição de Ativação em Nível de Tile ...",
-//                Metodologia / Kernel-2).  PAIR_ADJ: the B tile kept W_fused's
-//                interleaved column order, so a pair sits in registers (r, r+1) of
-//                one lane.  Otherwise the B tile was de-interleaved per 64 fused
-//                columns and a pair sits at the same register of tiles 2q, 2q+1.
+//                Metodologia / Kernel-2).  epilogue16 serves the register-staged
+//                kernel, whose B tile was de-interleaved per 64 fused columns so a
+//                pair sits at the same register of tiles 2q, 2q+1.  The direct-to-
+//                LDS kernels keep W_fused's interleaved order (a pair sits in
+//                registers (r, r+1) of one lane) and use epilogue_swiglu_lds.
 //   EPI_PARTIAL  raw fp32 sums of one K split into workspace [split][M][N].
 #pragma once
 
@@ -25,7 +26,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return (uint32_t)from_f32<DT>(a) | ((uint32_t)from_f32<DT>(b) << 16);
 }
 
-template <int DT, int EPI, bool PAIR_ADJ, int FM, int FN>
+template <int DT, int EPI, int FM, int FN>
 __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[FN][FM], int m0,
                                            int n0, int BM, int BN, int mb, int nb, int lane) {
     const int lm = lane & 31, lq = (lane >> 5) * 4;
@@ -78,31 +79,7 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
         const int nout = p.N >> 1;                 // p.N is the fused width
         const bool full_c = inside && p.vec_c;
         const float s = p.alpha;
-        if constexpr (PAIR_ADJ) {
-            // fused columns nf..nf+3 in registers 4g..4g+3: pairs (0,1), (2,3)
-#pragma unroll
-            for (int tm = 0; tm < FM; ++tm) {
-                const int m = mb + tm * 32 + lm;
-                if (!full_c && m >= p.M) continue;
-#pragma unroll
-                for (int tn = 0; tn < FN; ++tn) {
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int no = (nb + tn * 32 + 8 * g + lq) >> 1;
-                        uint16_t* y = Y + (int64_t)m * nout + no;
-                        const float y0 = silu(s * acc[tn][tm][4 * g]) * (s * acc[tn][tm][4 * g + 1]);
-                        const float y1 =
-                            silu(s * acc[tn][tm][4 * g + 2]) * (s * acc[tn][tm][4 * g + 3]);
-                        if (full_c) {
-                            *reinterpret_cast<uint32_t*>(y) = pack2<DT>(y0, y1);
-                        } else {
-                            if (no < nout) y[0] = from_f32<DT>(y0);
-                            if (no + 1 < nout) y[1] = from_f32<DT>(y1);
-                        }
-                    }
-                }
-            }
-        } else {
+        {
             const int ob = nb >> 1;                // first output column of this wave
 #pragma unroll
             for (int tm = 0; tm < FM; ++tm) {
@@ -159,6 +136,63 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
                     }
                 }
             }
+        }
+    }
+}
+
+// SwiGLU epilogue of the direct-to-LDS kernels, staged through LDS so that the
+// global stores run along rows.  In the MFMA accumulator layout a wave holds 32
+// rows x a few columns, so storing from registers touches 32 rows (cache lines)
+// per instruction; here each wave first writes its packed output pairs into a
+// row-major [BM][BN/2] tile in LDS (rows padded by 8 bytes: 32 rows at one column
+// fall on distinct banks), then all threads copy whole 16-byte row pieces out.
+// Called by every thread of the work-group after the main loop (LDS is free once
+// every wave passed the barrier at the top).
+template <int DT, int FM, int FN, int BM, int BN, int NT>
+__device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
+                                                    f32x16 (&acc)[FN][FM], char* smem, int m0,
+                                                    int n0, int rb, int cb, int lane) {
+    constexpr int ROW = BN + 8;        // bytes per staged row: BN/2 outputs of 2 bytes + pad
+    constexpr int CPR = BN / 16;       // 16-byte pieces (8 outputs) per row
+    static_assert(BN % 16 == 0, "whole 16-byte row pieces");
+    __syncthreads();
+    const int lm = lane & 31, lq = (lane >> 5) * 4;
+    const float s = p.alpha;
+#pragma unroll
+    for (int tm = 0; tm < FM; ++tm) {
+        char* row = smem + (rb + tm * 32 + lm) * ROW;
+#pragma unroll
+        for (int tn = 0; tn < FN; ++tn) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // fused columns c..c+3 hold two (gate, up) pairs -> outputs c/2, c/2+1,
+                // at byte offset c of the staged row
+                const int c = cb + tn * 32 + 8 * g + lq;
+                const float y0 = silu(s * acc[tn][tm][4 * g]) * (s * acc[tn][tm][4 * g + 1]);
+                const float y1 = silu(s * acc[tn][tm][4 * g + 2]) * (s * acc[tn][tm][4 * g + 3]);
+                *reinterpret_cast<uint32_t*>(row + c) = pack2<DT>(y0, y1);
+            }
+        }
+    }
+    __syncthreads();
+    uint16_t* Y = reinterpret_cast<uint16_t*>(p.C);
+    const int nout = p.N >> 1, o0 = n0 >> 1;
+    const bool v16 = (p.epi_flags & EPI_Y16) != 0;
+    for (int idx = threadIdx.x; idx < BM * CPR; idx += NT) {
+        const int r = idx / CPR, c = idx - r * CPR;
+        const int m = m0 + r, o = o0 + c * 8;
+        if (m >= p.M || o >= nout) continue;
+        const char* src = smem + r * ROW + c * 16;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
+        uint16_t* y = Y + (int64_t)m * nout + o;
+        if (v16 && o + 8 <= nout) {
+            *reinterpret_cast<u32x4*>(y) = u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+            const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (o + e < nout) y[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
     }
 }

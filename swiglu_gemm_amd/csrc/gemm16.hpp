@@ -290,7 +290,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_kernel(const Gemm16Par
         for (; kt < nkt; ++kt) body(kt, std::false_type{});
     }
 
-    epilogue16<DT, EPI, false, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN, lane);
+    epilogue16<DT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN, lane);
 }
 
 }  // namespace sg

@@ -21,8 +21,9 @@
 //
 // W_fused keeps its interleaved column order: in the D^T accumulator layout fused
 // columns (2n, 2n+1) land in registers (r, r+1) of one lane, so the SwiGLU
-// epilogue pairs them in place ("Resumo Técnico: Sobreposição de Ativação em Nível
-// de Tile ...", Metodologia / Kernel-2).
+// epilogue pairs them in registers ("Resumo Técnico: Sobreposição de Ativação em
+// Nível de Tile ...", Metodologia / Kernel-2) and stages the bf16/fp16 outputs
+// through the then idle LDS ring for row-contiguous stores.
 //
 // Edge tiles: a k-contiguous operand's rows past M (N) are clamped to the last
 // valid row, and a row-contiguous operand's 16-byte chunks past N (M) to the
@@ -49,23 +50,31 @@ struct DmaTile {
     static constexpr int ROW_BYTES = KC ? BK * ESZ : R * ESZ;
     static constexpr int BYTES = R * BK * ESZ;
     static constexpr int SLOTS = ROW_BYTES / 16;         // 16-byte slots per row
-    static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;  // rows per 1 KiB DMA block
-    static constexpr int BLOCKS = BYTES / 1024;
-    static_assert(ROW_BYTES <= 1024 && 1024 % ROW_BYTES == 0, "row must divide 1 KiB");
-    static_assert(KC ? (ROW_BYTES == 64 || ROW_BYTES == 128) : (ROW_BYTES >= 128),
+    static constexpr int BLOCKS = BYTES / 1024;          // 1 KiB DMA blocks
+    static constexpr int UNITS = ROW_BYTES / 32;         // row-contiguous: 32-byte units
+    static_assert(BYTES % 1024 == 0, "whole 1 KiB DMA blocks");
+    static_assert(KC ? (ROW_BYTES == 64 || ROW_BYTES == 128)
+                     : (ROW_BYTES >= 128 && ROW_BYTES <= 1024 && ROW_BYTES % 64 == 0),
                   "unsupported tile");
 
-    // physical 16-byte chunk (KC) or 32-byte unit (row-contiguous) for a row
+    // Physical 16-byte chunk (KC) or 32-byte unit (row-contiguous) XOR mask for a
+    // row.  A row-contiguous fragment read touches one or two units of 4 (16-bit)
+    // or 8 (8-bit) consecutive k rows in one LDS phase; unit u of row k sits at
+    // 32-byte bank slot (UNITS*k + (u ^ swz(k))) mod 8, and the masks below make
+    // those slots distinct for every even UNITS (XOR stays inside the row: UNITS
+    // is a multiple of the largest mask + 1 in each case).
     static __device__ __forceinline__ int swz(int row) {
         if constexpr (KC) {
             if constexpr (ROW_BYTES == 128) return (row & 7) ^ ((row >> 3) & 1);
             else return (row >> 2) & 3;
         } else if constexpr (ESZ == 2) {
-            return (row & 3) << 1;                    // 4 rows x 2 units per phase
-        } else if constexpr (ROW_BYTES >= 256) {
-            return row & 7;                           // 8 rows x 1 unit per phase
+            if constexpr (UNITS % 8 == 0) return (row & 3) << 1;   // 4 rows x 2 units
+            else if constexpr (UNITS % 8 == 4) return row & 2;     // rows alternate halves
+            else return 0;                                         // UNITS = 2 mod 4
         } else {
-            return (row >> 1) & 3;                    // 128-byte rows: 2 rows per bank row
+            if constexpr (UNITS % 8 == 0) return row & 7;          // 8 rows x 1 unit
+            else if constexpr (UNITS % 8 == 4) return (row >> 1) & 3;
+            else return (row >> 2) & 1;                            // UNITS = 2 mod 4
         }
     }
 };
@@ -92,8 +101,9 @@ struct DmaStream {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int b = wave + i * NWAVES;
-            const int row = b * T::ROWS_PER_KB + lane / T::SLOTS;
-            const int slot = lane % T::SLOTS;
+            const int chunk = b * 64 + lane;                 // 16-byte chunk of the tile
+            const int row = chunk / T::SLOTS;
+            const int slot = chunk % T::SLOTS;
             if constexpr (KC) {
                 const int c = slot ^ T::swz(row);
                 const int r = min(r0 + row, rows - 1);
@@ -294,8 +304,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
         }
     }
 
-    epilogue16<DT_OUT, EPI, true, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
-                                         lane);
+    if constexpr (EPI == EPI_SWIGLU) {
+        static_assert(BM * (BN + 8) <= S * STAGE, "staged SwiGLU tile fits the LDS ring");
+        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN>(p, acc, smem, m0, n0, wm * TM,
+                                                                       wn * TN, lane);
+    } else {
+        epilogue16<DT_OUT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
+                                        lane);
+    }
 }
 
 }  // namespace sg

@@ -38,8 +38,9 @@ struct DmaStreamS {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int b = widx + i * NWD;
-            const int row = b * T::ROWS_PER_KB + lane / T::SLOTS;
-            const int slot = lane % T::SLOTS;
+            const int chunk = b * 64 + lane;
+            const int row = chunk / T::SLOTS;
+            const int slot = chunk % T::SLOTS;
             if constexpr (KC) {
                 const int c = slot ^ T::swz(row);
                 const int r = min(r0 + row, rows - 1) - r0;            // >= 0
@@ -181,8 +182,14 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const Gemm16Params p) {
         if (group == 0) barrier();
     }
 
-    epilogue16<DT_OUT, EPI, true, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
-                                         lane);
+    if constexpr (EPI == EPI_SWIGLU) {
+        static_assert(BM * (BN + 8) <= S * STAGE, "staged SwiGLU tile fits the LDS ring");
+        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 512>(p, acc, smem, m0, n0, wm * TM,
+                                                              wn * TN, lane);
+    } else {
+        epilogue16<DT_OUT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
+                                        lane);
+    }
 }
 
 }  // namespace sg

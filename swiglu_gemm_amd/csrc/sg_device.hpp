@@ -36,9 +36,13 @@ template <> __device__ __forceinline__ uint16_t from_f32<DT_BF16>(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// SiLU(x) = x / (1 + e^-x); e^-x -> +inf for very negative x gives -0, never NaN.
+// SiLU(x) = x / (1 + e^-x), evaluated as x * rcp(1 + 2^(-x*log2 e)) with the
+// hardware exp2 and reciprocal (about 1 ulp each in fp32, far below the bf16 /
+// fp16 output rounding).  e^-x -> +inf for very negative x gives rcp = 0 and
+// -0, never NaN; for x >= ~17, 1 + e^-x rounds to 1 and SiLU(x) = x exactly.
 __device__ __forceinline__ float silu(float x) {
-    return x / (1.0f + __expf(-x));
+    const float e = __builtin_amdgcn_exp2f(x * -1.44269504088896341f);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Arguments of the 16-bit / 8-bit MFMA GEMM kernels.
@@ -52,7 +56,10 @@ struct Gemm16Params {
     int vec_a, vec_b, vec_c;
     int tiles_m, tiles_n, group_m;
     int k_per_split;    // a multiple of 64; gridDim.y splits
+    int epi_flags;      // EPI_SWIGLU: EPI_Y16 (Y rows allow 16-byte stores)
 };
+
+enum { EPI_Y16 = 1 };
 
 // ---------------------------------------------------------------------------
 // XCD-aware block order.  Work-groups are handed to the 8 XCDs round-robin

@@ -14,7 +14,8 @@ from helpers import assert_close, bits_equal, from_dev, split_count, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-CFGS16 = list(range(14)) + [18, 19, 20, 22]   # every 16-bit configuration id
+CFGS16 = list(range(14)) + [18, 19, 20, 22] + list(range(24, 33))   # every 16-bit configuration id
+WIDE = [24, 25, 26]                # 320-column tiles (640-byte LDS rows)
 TRANS = ["NN", "NT", "TN", "TT"]
 
 
@@ -99,6 +100,71 @@ def test_identity_bit_exact_every_config(cfg):
     forced(cfg, 1)
     try:
         sg.gemm(A, I, C)
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    assert bits_equal(from_dev(C), Ab), desc
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+@pytest.mark.parametrize("tr", TRANS)
+@pytest.mark.parametrize("cfg", WIDE)
+def test_wide_tiles_ragged(cfg, tr, splits):
+    """320-column tiles on a shape with two full tiles and a ragged third in N,
+    a ragged M tile, and an odd number of 64-deep K tiles per split."""
+    import swiglu_gemm_amd as sg
+    M, N, K = 520, 1000, 640
+    ta, tb = tr
+    p = inputs.gemm_problem(110 + cfg, ta, tb, M, N, K, "bf16", "normal", ld_mode="padded")
+    A, B, C = to_dev(p["A"], "bf16"), to_dev(p["B"], "bf16"), to_dev(p["C"], "bf16")
+    forced(cfg, splits)
+    print("wide cfg %d %s splits %d" % (cfg, tr, splits), flush=True)
+    try:
+        sg.gemm(A, B, C, alpha=0.7, beta=0.3, transA=ta, transB=tb, M=M, N=N, K=K,
+                lda=p["lda"], ldb=p["ldb"], ldc=p["ldc"], dtype=2)
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    ref = oracle.gemm(ta, tb, M, N, K, 0.7, p["A"], p["lda"], p["B"], p["ldb"], 0.3, p["C"],
+                      p["ldc"], "bf16")
+    cbits = from_dev(C)
+    assert bits_equal(cbits[:, N:], p["C"][:, N:]), "ld padding of C was written"
+    assert_close(oracle.decode(cbits, "bf16")[:, :N], ref[:, :N], "bf16", K, desc)
+
+
+@pytest.mark.parametrize("cfg", WIDE)
+def test_wide_tiles_swiglu_and_identity(cfg):
+    """SwiGLU pairing across 320-column tiles (fused N = 9728 / 320 is not whole)
+    and A @ I bit-exact with a ragged last column tile."""
+    import swiglu_gemm_amd as sg
+    M, N, K = 256, 4864, 128
+    pb = inputs.swiglu_problem(120 + cfg, M, N, K, "bf16")
+    Wf = oracle.interleave(pb["W1"], pb["W2"])
+    A, W = to_dev(pb["A"], "bf16"), to_dev(Wf, "bf16")
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    forced(cfg, 1)
+    try:
+        sg.swiglu_gemm(A, W, Y)
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    ref = oracle.swiglu(M, N, K, pb["A"], Wf, "bf16")
+    assert_close(oracle.decode(from_dev(Y), "bf16"), ref, "bf16", K, desc)
+
+    Mi, Ki = 256, 704
+    gen = np.random.default_rng(cfg)
+    Ab = inputs.to_storage(gen.standard_normal((Mi, Ki)), "bf16")
+    Ib = inputs.to_storage(np.eye(Ki), "bf16")
+    C = torch.empty((Mi, Ki), dtype=torch.bfloat16, device="cuda:0")
+    forced(cfg, 1)
+    try:
+        sg.gemm(to_dev(Ab, "bf16"), to_dev(Ib, "bf16"), C)
         torch.cuda.synchronize()
         desc = sg.last_config()
     finally:
