@@ -23,6 +23,9 @@ Prints ONE JSON line.
 Counter helpers (used to produce the committed HBM-traffic figure):
     python bench.py --pmc-probe            # copy of a known size, then 3 GEMM launches
     python bench.py --pmc-summarize FETCH.csv WRITE.csv   # -> profiles/traffic_*.json
+
+Power-limited MFMA ceiling (context for roofline.frac, a separate run):
+    python bench.py --mfma-ceiling         # pure MFMA loop on zero / constant / random data
 """
 from __future__ import annotations
 
@@ -248,6 +251,55 @@ def pmc_summarize(fetch_csv, write_csv):
     print(json.dumps(res, indent=1))
 
 
+def mfma_ceiling():
+    """Sustained rate of a pure MFMA loop (no memory traffic) on zero, constant and
+    random operand data, per dtype.  The matrix cores' power grows with the
+    operands' bit activity; under the board power limit the clock drops, so random
+    data sets a lower ceiling than the published peak.  One JSON line per case."""
+    import ctypes
+    import torch
+    from swiglu_gemm_amd import build
+    if not os.path.exists(build.DIAG_LIB):
+        raise SystemExit("diagnostic library missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(build.DIAG_LIB)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks, iters = 1024, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    nsrc = 8192                                     # 16-byte operand chunks
+    gen = torch.Generator(device="cuda:0").manual_seed(7)
+    for kind, dt in ((0, "f16"), (1, "bf16"), (2, "e4m3")):
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}[dt]
+        per = 16 // torch.empty(0, dtype=tdt).element_size()
+        datas = {
+            "zero": torch.zeros(nsrc * per, device="cuda:0"),
+            "constant_1.0": torch.ones(nsrc * per, device="cuda:0"),
+            "random_normal": torch.randn(nsrc * per, device="cuda:0", generator=gen) *
+            (1.0 if dt == "e4m3" else 1.0 / 90.5),
+        }
+        for name, v in datas.items():
+            src = v.to(tdt).contiguous()
+            f = lambda: lib.sg_diag_mfma_loop(kind, blocks, ctypes.c_void_p(src.data_ptr()), nsrc,
+                                              iters, ctypes.c_void_p(out.data_ptr()), st)
+            assert f() == 0
+            torch.cuda.synchronize()
+            t_end = time.perf_counter() + 0.3
+            while time.perf_counter() < t_end:
+                f()
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            flops = blocks * 4 * iters * 8 * 2 * 32 * 32 * (64 if kind == 2 else 16)
+            tf = flops / (ms * 1e-3) / 1e12
+            print(json.dumps({"mfma_ceiling": dt, "operands": name, "ms": round(ms, 4),
+                              "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK[dt], 4)}),
+                  flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +310,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--pmc-probe", action="store_true")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--mfma-ceiling", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only (the library is single-GPU); --gpus %d is not "
@@ -268,6 +321,9 @@ def main():
         return
     if args.pmc_probe:
         pmc_probe()
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
 
     import torch

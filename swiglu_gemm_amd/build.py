@@ -13,6 +13,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libswiglu_gemm.so")
+# diagnostic library (not the GEMM path): a pure MFMA loop for the power-limited
+# MFMA ceiling that bench.py --mfma-ceiling reports
+DIAG_SRC = os.path.join(HERE, "diag", "mfma_loop.hip")
+DIAG_LIB = os.path.join(HERE, "libswiglu_gemm_diag.so")
 SOURCES = ["api.hip"] + ["inst_%s_%s.hip" % (d, t) for d in ("f16", "bf16", "e4m3")
                         for t in ("nn", "nt", "tn", "tt")]
 ARCH = "gfx950"
@@ -49,7 +53,7 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError("hipcc failed on %s" % src)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 8)) as ex:
         objs = list(ex.map(one, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
@@ -58,6 +62,13 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed linking libswiglu_gemm.so")
     os.replace(tmp, LIB)
+    tmp = DIAG_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run([hipcc()] + _flags() + ["-shared", DIAG_SRC, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on diag/mfma_loop.hip")
+    os.replace(tmp, DIAG_LIB)
     return LIB
 
 

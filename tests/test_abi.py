@@ -107,3 +107,17 @@ def test_product_path_does_not_import_oracle():
                 text = open(os.path.join(root, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "oracle." not in text.replace(
                     "the oracle", ""), f
+
+
+def test_diagnostic_library_is_separate():
+    """The MFMA-ceiling probe lives in its own library: the GEMM library does not
+    export it and the diagnostic library exports only the probe."""
+    import ctypes
+    from swiglu_gemm_amd import build
+    if not os.path.exists(build.DIAG_LIB):
+        pytest.skip("diagnostic library not built")
+    d = ctypes.CDLL(build.DIAG_LIB)
+    assert hasattr(d, "sg_diag_mfma_loop")
+    assert not hasattr(d, "sg_gemm")
+    import swiglu_gemm_amd as sg
+    assert not hasattr(sg.lib(), "sg_diag_mfma_loop")
