@@ -12,11 +12,15 @@ ramped, W untimed warm-up steps, then exactly K timed steps between two
 synchronisations.  Three input sets are rotated so the 256 MB
 last-level cache cannot keep one set resident across steps.
 
-Also reported, same run: the fused SwiGLU-GEMM (bf16: A[M x 896], W_fused[896 x
-9728], M in {128, 512, 2048, 8192}; e4m3 with per-tensor scales: A[M x 4096],
-W_fused[4096 x 22016], M in {1, 16, 256, 4096}) against this library's unfused
-path (two sg_gemm calls writing Gate and Up, then sg_silu_mul) and torch eager as
-context; and the fp64 CPU oracle timed on a bounded sample of the GEMM rows.
+Also reported, same run: per-step median / min / p90 of the headline; the same
+GEMM in bf16; the ragged bf16 GEMMs (1000^3 and 4097x3001x2049, every transpose
+pair); the fused SwiGLU-GEMM (bf16: A[M x 896], W_fused[896 x 9728], M in {128,
+512, 2048, 8192}; e4m3 with per-tensor scales: A[M x 4096], W_fused[4096 x 22016],
+M in {1, 16, 256, 4096}) with cold weights (copies rotated past the last-level
+cache) and hot, against this library's unfused path (two sg_gemm calls writing
+Gate and Up, then sg_silu_mul), the split-weight entry point (separate W1, W2:
+w12_ms) and torch eager as context; and the fp64 CPU oracle timed on a bounded
+sample of the GEMM rows.
 
 Prints ONE JSON line.
 
@@ -128,37 +132,55 @@ def cpu_baseline(p, M, N, K, budget_s=12.0):
                       "oracle incl. decode, %.1f s" % (done, M, M, N, K, t_total)}
 
 
+COLD_BYTES = 512 * 1024 * 1024     # rotate operand copies past the 256 MB last-level cache
+
+
 def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True):
-    """Fused vs this library's unfused path (vs torch eager) for one SwiGLU size."""
+    """Fused vs this library's unfused path (vs torch eager) for one SwiGLU size.
+    Cold: the weights rotate through enough device copies (> 512 MB in all) that
+    W_fused comes from HBM each step; hot: two copies, which the last-level cache
+    keeps.  Two seeded problems; the further copies are device clones."""
     workload = 4 if dtype == "bf16" else 5
-    nsets = 2
-    sets = []
-    for r in range(nsets):
+    base = []
+    for r in range(2):
         pb = inputs.swiglu_problem(workload, M, N, K, dtype) if r == 0 else \
             inputs.swiglu_problem(100 + workload, M, N, K, dtype)
         A = to_dev(pb["A"], dtype, torch)
         W1 = to_dev(pb["W1"], dtype, torch)
         W2 = to_dev(pb["W2"], dtype, torch)
         Wf = sg.interleave_gate_up(W1, W2)
-        sets.append((A, W1, W2, Wf, pb["scale_a"], pb["scale_w"]))
+        base.append((A, W1, W2, Wf, pb["scale_a"], pb["scale_w"]))
+    esz = 1 if dtype == "e4m3" else 2
+    per_set = (M * K + 2 * K * 2 * N) * esz           # A, W1 + W2, W_fused
+    ncold = max(4, -(-COLD_BYTES // per_set))
+    sets = [base[r % 2] if r < 2 else tuple(x.clone() if torch.is_tensor(x) else x
+                                            for x in base[r % 2]) for r in range(ncold)]
     Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     G = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
     U = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
 
-    def fused(i):
-        A, _, _, Wf, sa, sw = sets[i % nsets]
-        sg.swiglu_gemm(A, Wf, Y, sa, sw)
+    def fused_over(pool):
+        def fn(i):
+            A, _, _, Wf, sa, sw = pool[i % len(pool)]
+            sg.swiglu_gemm(A, Wf, Y, sa, sw)
+        return fn
 
     def unfused(i):
-        A, W1, W2, _, sa, sw = sets[i % nsets]
+        A, W1, W2, _, sa, sw = sets[i % ncold]
         sg.gemm(A, W1, G, alpha=sa * sw)
         sg.gemm(A, W2, U, alpha=sa * sw)
         sg.silu_mul(G, U, Y)
 
-    t_fused = time_steps(fused, steps, warmup, torch)
+    def w12(i):
+        A, W1, W2, _, sa, sw = sets[i % ncold]
+        sg.swiglu_gemm_w12(A, W1, W2, Y, sa, sw)
+
+    t_fused = time_steps(fused_over(sets), steps, warmup, torch)
     cfg = sg.last_config()
+    t_hot = time_steps(fused_over(base), steps, warmup, torch)
+    t_w12 = time_steps(w12, steps, warmup, torch)
+    cfg_w12 = sg.last_config()
     t_unfused = time_steps(unfused, steps, warmup, torch)
-    esz = 1 if dtype == "e4m3" else 2
     flops = 4.0 * M * N * K
     nbytes = M * K * esz + K * 2 * N * esz + M * N * 2
     tf = flops / (t_fused * 1e-3) / 1e12
@@ -166,16 +188,84 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True):
     out = {"dtype": dtype, "M": M, "N": N, "K": K, "ms": round(t_fused, 5),
            "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK[dtype], 4),
            "hbm_gbs_algorithmic": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "weights": "cold: %d rotated copies, %.0f MB" % (ncold, ncold * per_set / 1e6),
+           "ms_hot": round(t_hot, 5),
            "unfused_ms": round(t_unfused, 5), "speedup_vs_unfused": round(t_unfused / t_fused, 3),
-           "kernel_config": cfg}
+           "kernel_config": cfg,
+           "w12_ms": round(t_w12, 5), "w12_kernel_config": cfg_w12}
     if eager and dtype == "bf16":
         def eager_fn(i):
-            A, W1, W2, _, _, _ = sets[i % nsets]
+            A, W1, W2, _, _, _ = sets[i % ncold]
             torch.nn.functional.silu(A @ W1) * (A @ W2)
         t_eager = time_steps(eager_fn, steps, warmup, torch)
         out["torch_eager_ms"] = round(t_eager, 5)
         out["speedup_vs_torch_eager"] = round(t_eager / t_fused, 3)
     return out
+
+
+def step_stats(fn, steps, torch):
+    """Per-step times (HIP events around each step) after the timed region: the
+    median, min and 90th percentile beside the contract's mean."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median_ms": round(float(np.median(t)), 5), "min_ms": round(float(t.min()), 5),
+            "p90_ms": round(float(np.percentile(t, 90)), 5), "steps": steps}
+
+
+def bench_gemm_bf16_8192(torch, sg, steps, warmup):
+    """The headline shape in bf16 (same distribution, three rotated sets)."""
+    M = N = K = 8192
+    sets = []
+    for r in range(3):
+        g = torch.Generator(device="cuda:0").manual_seed(300 + r)
+        A = (torch.randn(M, K, device="cuda:0", generator=g) / np.sqrt(K)).bfloat16()
+        B = (torch.randn(K, N, device="cuda:0", generator=g) / np.sqrt(K)).bfloat16()
+        sets.append((A, B, torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")))
+
+    def step(i):
+        A, B, C = sets[i % 3]
+        sg.gemm(A, B, C)
+    ms = time_steps(step, steps, warmup, torch)
+    tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 5), "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK["bf16"], 4),
+            "kernel_config": sg.last_config()}
+
+
+def bench_gemm_ragged(torch, sg, inputs, steps, warmup):
+    """bf16 GEMMs of the ragged parity shapes (alpha 0.7, beta 0.3, padded ld), every
+    transpose pair: TFLOP/s per variant.  With beta = 0.3 each step reads the C the
+    previous step wrote (a bounded recurrence); values do not change the time."""
+    out = []
+    for (M, N, K) in ((1000, 1000, 1000), (4097, 3001, 2049)):
+        for tr in ("NN", "NT", "TN", "TT"):
+            p = inputs.gemm_problem(3, tr[0], tr[1], M, N, K, "bf16", "normal", ld_mode="padded")
+            A, B, C = (to_dev(p["A"], "bf16", torch), to_dev(p["B"], "bf16", torch),
+                       to_dev(p["C"], "bf16", torch))
+
+            def step(i):
+                sg.gemm(A, B, C, alpha=0.7, beta=0.3, transA=tr[0], transB=tr[1], M=M, N=N, K=K,
+                        lda=p["lda"], ldb=p["ldb"], ldc=p["ldc"], dtype=2)
+            ms = time_steps(step, steps, warmup, torch)
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            out.append({"M": M, "N": N, "K": K, "trans": tr, "ms": round(ms, 5),
+                        "tflops": round(tf, 2), "kernel_config": sg.last_config()})
+    return out
+
+
+def env_info(torch):
+    props = torch.cuda.get_device_properties(0)
+    info = {"device": props.name, "compute_units": props.multi_processor_count,
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    for key in ("gcnArchName", "clock_rate"):
+        if hasattr(props, key):
+            info[key] = getattr(props, key)
+    return info
 
 
 def gemm_inputs(inputs, torch, M, N, K, nsets):
@@ -343,6 +433,7 @@ def main():
     print("bench: timing fp16 8192^3 GEMM", file=sys.stderr, flush=True)
     ms = time_steps(step, args.steps, args.warmup, torch)
     cfg = sg.last_config()
+    stats = step_stats(step, args.steps, torch)
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic()
@@ -360,7 +451,16 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK["f16"], 4),
                      "traffic": traffic, "kernel": "gemm_dma_kernel (one launch per step)",
                      "algorithmic_flops_per_launch": flops},
+        "step_stats": stats,
+        "env": env_info(torch),
     }
+    if not args.quick:
+        print("bench: bf16 8192^3 GEMM and the ragged bf16 GEMMs", file=sys.stderr, flush=True)
+        out["gemm_bf16_8192"] = bench_gemm_bf16_8192(torch, sg, max(10, args.steps // 2),
+                                                     args.warmup)
+        torch.cuda.empty_cache()
+        out["gemm_ragged_bf16"] = bench_gemm_ragged(torch, sg, inputs, 20, 3)
+        torch.cuda.empty_cache()
     sizes = [("bf16", 2048, 4864, 896)]
     if not args.quick:
         sizes = [("bf16", m, 4864, 896) for m in (128, 512, 2048, 8192)] + \

@@ -99,6 +99,34 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y,
                    float scale_a, float scale_w, void* stream);
 
 /*
+ * sg_swiglu_gemm_w12: the same Y = SiLU(s * A * W1) ⊙ (s * A * W2) from separate,
+ * non-interleaved W1 and W2 -- the weight layout of Kernel-1 in "Resumo Técnico:
+ * Sobreposição de Ativação em Nível de Tile para Inferência Eficiente de LLM"
+ * (Metodologia).  One work-group tile loads BN/2 columns of W1 and the same BN/2
+ * columns of W2 side by side, so gate and up of every output still meet in
+ * registers and never reach memory.  Results equal sg_swiglu_gemm on the
+ * interleaved W_fused to the same tolerance (and, for the same tile configuration,
+ * bit for bit).
+ *
+ *  1 A       M x K, contiguous (ld = K).
+ *  2 W1, 3 W2   K x N each, contiguous (ld = N).
+ *  4 Y       M x N, contiguous (ld = N).
+ *  5 M, 6 N, 7 K   >= 0.
+ *  8 dtype   as sg_swiglu_gemm.   9 scale_a, 10 scale_w   as sg_swiglu_gemm.
+ *  11 stream hipStream_t (void*).
+ * Shapes the direct kernel cannot take (K not a multiple of the K tile, rows not
+ * 16-byte multiples, unaligned pointers) are run by interleaving W1, W2 into a
+ * library-owned buffer (grown on demand, freed by sg_release) and calling
+ * sg_swiglu_gemm; calls on several streams of one device must not overlap then.
+ * Quick returns: M == 0 or N == 0 does nothing; K == 0 writes Y = 0.
+ * Invalid: NULL pointer (-1/-2/-3/-4), negative size (-5/-6/-7), unsupported dtype
+ * (-8), bad scale (-9/-10).
+ */
+int sg_swiglu_gemm_w12(const void* A, const void* W1, const void* W2, void* Y,
+                       int64_t M, int64_t N, int64_t K, int dtype,
+                       float scale_a, float scale_w, void* stream);
+
+/*
  * sg_interleave_gate_up: Wfused[k, 2n] = W1[k, n], Wfused[k, 2n+1] = W2[k, n]
  * (the W_fused layout of the same page's Kernel-2).  Bit-exact copy.
  *  1 W1, 2 W2   K x N contiguous; 3 Wfused  K x 2N contiguous;

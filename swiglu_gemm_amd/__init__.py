@@ -49,6 +49,9 @@ def lib() -> ctypes.CDLL:
         L.sg_gemm.restype = ctypes.c_int
         L.sg_swiglu_gemm.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, f32, f32, vp]
         L.sg_swiglu_gemm.restype = ctypes.c_int
+        L.sg_swiglu_gemm_w12.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, f32, f32,
+                                         vp]
+        L.sg_swiglu_gemm_w12.restype = ctypes.c_int
         L.sg_interleave_gate_up.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, vp]
         L.sg_interleave_gate_up.restype = ctypes.c_int
         L.sg_silu_mul.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, vp]
@@ -142,6 +145,19 @@ def swiglu_gemm(A, Wfused, Y, scale_a: float = 1.0, scale_w: float = 1.0):
                               ctypes.c_void_p(Y.data_ptr()), int(M), int(N), int(K),
                               _dtype_code(A), float(scale_a), float(scale_w), _stream(Y))
     _check(st, "sg_swiglu_gemm")
+    return Y
+
+
+def swiglu_gemm_w12(A, W1, W2, Y, scale_a: float = 1.0, scale_w: float = 1.0):
+    """Y = SiLU(s*A@W1) * (s*A@W2) from separate W1, W2 [K, N] (s = scale_a*scale_w);
+    A [M, K], Y [M, N], all contiguous."""
+    M, K = A.shape
+    N = W1.shape[1]
+    st = lib().sg_swiglu_gemm_w12(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(W1.data_ptr()),
+                                  ctypes.c_void_p(W2.data_ptr()), ctypes.c_void_p(Y.data_ptr()),
+                                  int(M), int(N), int(K), _dtype_code(A), float(scale_a),
+                                  float(scale_w), _stream(Y))
+    _check(st, "sg_swiglu_gemm_w12")
     return Y
 
 

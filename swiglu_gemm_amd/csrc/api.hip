@@ -53,15 +53,18 @@ struct Workspace {
     size_t bytes = 0;
 };
 std::mutex g_ws_mu;
-Workspace g_ws[64];
+// slot 0: split-K partials; slot 1: W_fused built from separate W1, W2 (the
+// split-weight SwiGLU's fallback for shapes its own kernel cannot take)
+constexpr int kSlots = 2;
+Workspace g_ws[kSlots][64];
 
-hipError_t workspace(size_t bytes, float** out) {
+hipError_t workspace(size_t bytes, float** out, int slot = 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lk(g_ws_mu);
-    Workspace& w = g_ws[dev];
+    Workspace& w = g_ws[slot][dev];
     if (w.bytes < bytes) {
         if (w.ptr) {
             e = hipDeviceSynchronize();
@@ -221,6 +224,7 @@ void set_last(const char* what, int cfg, int splits) {
 template <int DT>
 hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* out,
                  bool out_vec, const char* what, hipStream_t st, int* splits_used) {
+    if (!p.A || !p.B || !out) return hipErrorInvalidValue;           // never launch on NULL
     int cfg = 0, splits = 1;
     choose16(q, &cfg, &splits);
     if (cfg < 0) return hipErrorNotSupported;   // caller takes its generic path
@@ -345,6 +349,58 @@ hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alp
     if (!ta && tb) return launch_f32<false, true>(p, st);
     if (ta && !tb) return launch_f32<true, false>(p, st);
     return launch_f32<true, true>(p, st);
+}
+
+// ------------------------------------------------ split-weight SwiGLU (W1, W2)
+// Configurations that can run it (see w12_ok in launch16.hpp): 16-bit candidates
+// weighed with the same cost model as the interleaved kernel; e4m3 by rows.
+constexpr Cand16 kCandW12[] = {{10, 4.7}, {8, 4.7}, {6, 3.4}};
+
+bool w12_cfg_ok(const Cfg16& c, const Problem16& q_out) {
+    // c runs on [M, 2N, K]; each weight is a K x N row-contiguous operand of BN/2 columns
+    if (c.dma != 1 || (c.BN / c.WN / 32) % 2 != 0 || c.BN % 64 != 0) return false;
+    Cfg16 half = c;
+    half.BN = c.BN / 2;
+    return dma_ok(half, q_out, q_out.K);
+}
+
+int choose_w12(const Problem16& q_out) {
+    const bool e4m3 = q_out.esz == 1;
+    int cfg = -1, splits = 0;
+    const Problem16 q2{q_out.M, 2 * q_out.N, q_out.K, q_out.vec_a, q_out.vec_b, false, false,
+                       q_out.esz};
+    if (forced_config(&cfg, &splits) && cfg >= 0 && cfg < kNumCfg16 &&
+        (kCfg16[cfg].e4m3 != 0) == e4m3)
+        return w12_cfg_ok(kCfg16[cfg], q_out) ? cfg : -1;
+    if (e4m3) {
+        const int64_t big = cdiv(q2.M, 256) * cdiv(q2.N, 256);
+        cfg = big >= 2 * kNumCU ? 14 : (q_out.M >= 256 ? 33 : 16);
+        return w12_cfg_ok(kCfg16[cfg], q_out) ? cfg : -1;
+    }
+    cfg = -1;
+    double best = 0.0;
+    for (const Cand16& cand : kCandW12) {
+        const Cfg16& c = kCfg16[cand.id];
+        if (!w12_cfg_ok(c, q_out)) continue;
+        const double t = est_us(c, q2, 1, cand.tf_per_cu);
+        if (cfg < 0 || t < best) {
+            cfg = cand.id;
+            best = t;
+        }
+    }
+    return cfg;
+}
+
+template <int DT>
+hipError_t run_w12(int cfg, Gemm16Params p, hipStream_t st) {
+    if (!p.A || !p.B || !p.B2 || !p.C) return hipErrorInvalidValue;   // never launch on NULL
+    const Cfg16& c = kCfg16[cfg];
+    p.tiles_m = (int)cdiv(p.M, c.BM);
+    p.tiles_n = (int)cdiv(p.N, c.BN);
+    p.group_m = group_m();
+    p.k_per_split = (int)split_len(p.K, 1, c.BK);
+    std::snprintf(g_last_cfg, sizeof(g_last_cfg), "swiglu_w12 cfg=%d %s splits=1", cfg, c.name);
+    return launch16_dt<DT>(false, false, EPI_SWIGLU_W12, cfg, p, 1, st);
 }
 
 }  // namespace
@@ -492,6 +548,71 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
     return status_of(hipGetLastError());
 }
 
+int sg_swiglu_gemm_w12(const void* A, const void* W1, const void* W2, void* Y, int64_t M,
+                       int64_t N, int64_t K, int dtype, float scale_a, float scale_w,
+                       void* stream) {
+    if (!A) return -1;
+    if (!W1) return -2;
+    if (!W2) return -3;
+    if (!Y) return -4;
+    if (M < 0 || M > kMaxDim) return -5;
+    if (N < 0 || N > kMaxDim / 2) return -6;
+    if (K < 0 || K > kMaxDim) return -7;
+    if (dtype != SG_BF16 && dtype != SG_F16 && dtype != SG_F8E4M3) return -8;
+    if (!std::isfinite(scale_a) || !(scale_a > 0.0f)) return -9;
+    if (!std::isfinite(scale_w) || !(scale_w > 0.0f)) return -10;
+    if (dtype != SG_F8E4M3 && scale_a != 1.0f) return -9;
+    if (dtype != SG_F8E4M3 && scale_w != 1.0f) return -10;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (M == 0 || N == 0) return 0;
+    const int esz = dtype == SG_F8E4M3 ? 1 : 2;
+    if (K > 0) {
+        Problem16 q{M, N, K, aligned(A, 16) && (K * esz) % 16 == 0,
+                    aligned(W1, 16) && aligned(W2, 16) && (N * esz) % 16 == 0, false, false, esz};
+        const int cfg = choose_w12(q);
+        if (cfg >= 0) {
+            Gemm16Params p{};
+            p.A = reinterpret_cast<const uint16_t*>(A);
+            p.B = reinterpret_cast<const uint16_t*>(W1);
+            p.B2 = reinterpret_cast<const uint16_t*>(W2);
+            p.C = Y;
+            p.lda = K;
+            p.ldb = N;
+            p.ldc = N;
+            p.M = (int)M;
+            p.N = (int)(2 * N);
+            p.K = (int)K;
+            p.alpha = scale_a * scale_w;
+            p.vec_a = q.vec_a;
+            p.vec_b = q.vec_b;
+            p.vec_c = aligned(Y, 8) && (N % 4 == 0);
+            p.epi_flags = aligned(Y, 16) && N % 8 == 0 ? EPI_Y16 : 0;
+            hipError_t e;
+            if (dtype == SG_F8E4M3) e = run_w12<DT_E4M3>(cfg, p, st);
+            else if (dtype == SG_F16) e = run_w12<DT_F16>(cfg, p, st);
+            else e = run_w12<DT_BF16>(cfg, p, st);
+            return status_of(e);
+        }
+    }
+    // shapes the split-weight kernel cannot take (K tail, unaligned rows, K == 0):
+    // build W_fused in library scratch and take the interleaved path
+    float* ws = nullptr;
+    hipError_t e = workspace((size_t)(K > 0 ? K : 1) * 2 * N * esz, &ws, 1);
+    if (e != hipSuccess) return status_of(e);
+    int st_code = 0;
+    if (K > 0) {
+        st_code = sg_interleave_gate_up(W1, W2, ws, K, N, dtype, stream);
+        if (st_code != 0) return st_code;
+    }
+    st_code = sg_swiglu_gemm(A, ws, Y, M, N, K, dtype, scale_a, scale_w, stream);
+    if (st_code == 0) {
+        char tail[160];
+        std::snprintf(tail, sizeof(tail), "%s", g_last_cfg);
+        std::snprintf(g_last_cfg, sizeof(g_last_cfg), "swiglu_w12 via W_fused: %s", tail);
+    }
+    return st_code;
+}
+
 int sg_interleave_gate_up(const void* W1, const void* W2, void* Wfused, int64_t K, int64_t N,
                           int dtype, void* stream) {
     if (!W1) return -1;
@@ -568,14 +689,17 @@ void sg_release(void) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) cur = -1;
-    for (int d = 0; d < 64; ++d) {
-        if (g_ws[d].ptr) {
-            if (hipSetDevice(d) == hipSuccess) {
-                (void)hipDeviceSynchronize();
-                (void)hipFree(g_ws[d].ptr);
+    for (int slot = 0; slot < kSlots; ++slot) {
+        for (int d = 0; d < 64; ++d) {
+            Workspace& w = g_ws[slot][d];
+            if (w.ptr) {
+                if (hipSetDevice(d) == hipSuccess) {
+                    (void)hipDeviceSynchronize();
+                    (void)hipFree(w.ptr);
+                }
+                w.ptr = nullptr;
+                w.bytes = 0;
             }
-            g_ws[d].ptr = nullptr;
-            g_ws[d].bytes = 0;
         }
     }
     if (cur >= 0) (void)hipSetDevice(cur);

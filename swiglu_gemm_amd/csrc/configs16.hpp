@@ -49,6 +49,7 @@ constexpr Cfg16 kCfg16[] = {
     {0, 1, 128, 128, 64, 5, 2, 4, "dma 128x128x64 s5 2x4w"},
     {0, 1, 128, 128, 32, 8, 2, 2, "dma 128x128x32 s8 2x2w"},
     {0, 1, 128, 256, 64, 3, 2, 4, "dma 128x256x64 s3 2x4w"},
+    {1, 1, 128, 256, 128, 3, 2, 2, "e4m3 dma 128x256x128 s3 2x2w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
@@ -103,6 +104,7 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(16, 1, 32, 256, 128, 4, 1, 4)    \
     X(17, 1, 32, 128, 128, 4, 1, 4)    \
     X(21, 2, 256, 256, 128, 2, 4, 2)   \
-    X(23, 2, 128, 256, 128, 2, 2, 4)
+    X(23, 2, 128, 256, 128, 2, 2, 4)   \
+    X(33, 1, 128, 256, 128, 3, 2, 2)
 
 }  // namespace sg

@@ -147,8 +147,11 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
 // row-major [BM][BN/2] tile in LDS (rows padded by 8 bytes: 32 rows at one column
 // fall on distinct banks), then all threads copy whole 16-byte row pieces out.
 // Called by every thread of the work-group after the main loop (LDS is free once
-// every wave passed the barrier at the top).
-template <int DT, int FM, int FN, int BM, int BN, int NT>
+// every wave passed the barrier at the top).  W12: the tile's B columns were BN/2
+// of W1 then BN/2 of W2, so gate and up of one output sit at the same register of
+// fragments tn and tn + FN/2, and cb is the wave's first output column in the tile;
+// otherwise cb is its first fused column (outputs at half of it).
+template <int DT, int FM, int FN, int BM, int BN, int NT, bool W12>
 __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
                                                     f32x16 (&acc)[FN][FM], char* smem, int m0,
                                                     int n0, int rb, int cb, int lane) {
@@ -161,16 +164,36 @@ __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
 #pragma unroll
     for (int tm = 0; tm < FM; ++tm) {
         char* row = smem + (rb + tm * 32 + lm) * ROW;
+        if constexpr (W12) {
 #pragma unroll
-        for (int tn = 0; tn < FN; ++tn) {
+            for (int tn = 0; tn < FN / 2; ++tn) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // fused columns c..c+3 hold two (gate, up) pairs -> outputs c/2, c/2+1,
-                // at byte offset c of the staged row
-                const int c = cb + tn * 32 + 8 * g + lq;
-                const float y0 = silu(s * acc[tn][tm][4 * g]) * (s * acc[tn][tm][4 * g + 1]);
-                const float y1 = silu(s * acc[tn][tm][4 * g + 2]) * (s * acc[tn][tm][4 * g + 3]);
-                *reinterpret_cast<uint32_t*>(row + c) = pack2<DT>(y0, y1);
+                for (int g = 0; g < 4; ++g) {
+                    // outputs c..c+3 (gate in fragment tn, up in tn + FN/2), bytes 2c..
+                    const int c = cb + tn * 32 + 8 * g + lq;
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        y[e] = silu(s * acc[tn][tm][4 * g + e]) *
+                               (s * acc[tn + FN / 2][tm][4 * g + e]);
+                    *reinterpret_cast<u32x2*>(row + 2 * c) =
+                        u32x2{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int tn = 0; tn < FN; ++tn) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    // fused columns c..c+3 hold two (gate, up) pairs -> outputs c/2,
+                    // c/2+1, at byte offset c of the staged row
+                    const int c = cb + tn * 32 + 8 * g + lq;
+                    const float y0 =
+                        silu(s * acc[tn][tm][4 * g]) * (s * acc[tn][tm][4 * g + 1]);
+                    const float y1 =
+                        silu(s * acc[tn][tm][4 * g + 2]) * (s * acc[tn][tm][4 * g + 3]);
+                    *reinterpret_cast<uint32_t*>(row + c) = pack2<DT>(y0, y1);
+                }
             }
         }
     }

@@ -213,9 +213,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
     constexpr int KS = BK / KSTEP;
     static_assert(BK % KSTEP == 0 && KS % 2 == 0, "k-steps per tile must be even");
     constexpr bool KCA = !TA, KCB = TB;          // k-contiguous operands
+    // EPI_SWIGLU_W12: the B tile is BN/2 columns of W1 followed by the same BN/2
+    // columns of W2; a wave's fragments tn < FN/2 are gate, tn + FN/2 the matching up
+    constexpr bool W12 = EPI == EPI_SWIGLU_W12;
+    static_assert(!W12 || (!TA && !TB && FN % 2 == 0 && BN % 64 == 0), "split-weight SwiGLU tile");
+    constexpr int BNS = W12 ? BN / 2 : BN;       // columns per B source
+    constexpr int NBS = W12 ? 2 : 1;             // B sources
     using TA_ = DmaTile<KCA, BM, BK, ESZ>;
-    using TB_ = DmaTile<KCB, BN, BK, ESZ>;
-    constexpr int STAGE = TA_::BYTES + TB_::BYTES;
+    using TB_ = DmaTile<KCB, BNS, BK, ESZ>;
+    constexpr int STAGE = TA_::BYTES + NBS * TB_::BYTES;
     static_assert(S * STAGE <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
@@ -232,10 +238,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
     const int wm = wave % WM, wn = wave / WM;
 
     DmaStream<KCA, BM, BK, ESZ, NW> da;
-    DmaStream<KCB, BN, BK, ESZ, NW> db;
+    DmaStream<KCB, BNS, BK, ESZ, NW> db, db2;
     da.init(p.A, p.lda, m0, p.M, kbeg, wave, lane);
-    db.init(p.B, p.ldb, n0, p.N, kbeg, wave, lane);
-    constexpr int NL = DmaStream<KCA, BM, BK, ESZ, NW>::NI + DmaStream<KCB, BN, BK, ESZ, NW>::NI;
+    if constexpr (W12) {
+        db.init(p.B, p.ldb, n0 / 2, p.N / 2, kbeg, wave, lane);
+        db2.init(p.B2, p.ldb, n0 / 2, p.N / 2, kbeg, wave, lane);
+    } else {
+        db.init(p.B, p.ldb, n0, p.N, kbeg, wave, lane);
+    }
+    constexpr int NL =
+        DmaStream<KCA, BM, BK, ESZ, NW>::NI + NBS * DmaStream<KCB, BNS, BK, ESZ, NW>::NI;
 
     f32x16 acc[FN][FM];
 #pragma unroll
@@ -251,8 +263,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
         for (int tm = 0; tm < FM; ++tm)
             af[tm] = read_frag<KCA, BM, BK, ESZ>(st, wm * TM + tm * 32, s, lane);
 #pragma unroll
-        for (int tn = 0; tn < FN; ++tn)
-            bf[tn] = read_frag<KCB, BN, BK, ESZ>(st + TA_::BYTES, wn * TN + tn * 32, s, lane);
+        for (int tn = 0; tn < FN; ++tn) {
+            if constexpr (W12) {
+                constexpr int FH = FN / 2;
+                const char* half = st + TA_::BYTES + (tn / FH) * TB_::BYTES;
+                bf[tn] = read_frag<KCB, BNS, BK, ESZ>(half, wn * (TN / 2) + (tn % FH) * 32, s, lane);
+            } else {
+                bf[tn] = read_frag<KCB, BN, BK, ESZ>(st + TA_::BYTES, wn * TN + tn * 32, s, lane);
+            }
+        }
     };
     auto mfma_all = [&](const Frag (&af)[FM], const Frag (&bf)[FN]) {
 #pragma unroll
@@ -264,6 +283,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
         char* st = smem + (t % S) * STAGE;
         da.issue(st, t, wave);
         db.issue(st + TA_::BYTES, t, wave);
+        if constexpr (W12) db2.issue(st + TA_::BYTES + TB_::BYTES, t, wave);
     };
 
     if (nkt > 0) {
@@ -304,10 +324,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
         }
     }
 
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU || W12) {
         static_assert(BM * (BN + 8) <= S * STAGE, "staged SwiGLU tile fits the LDS ring");
-        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN>(p, acc, smem, m0, n0, wm * TM,
-                                                                       wn * TN, lane);
+        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN, W12>(
+            p, acc, smem, m0, n0, wm * TM, W12 ? wn * (TN / 2) : wn * TN, lane);
     } else {
         epilogue16<DT_OUT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
                                         lane);

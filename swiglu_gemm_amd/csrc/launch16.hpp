@@ -20,10 +20,27 @@ inline hipError_t launch_grid(Kern k, const Gemm16Params& p, int splits, int thr
     return hipGetLastError();
 }
 
+// Whether a configuration can run the split-weight SwiGLU (W1 and W2 separate):
+// the direct-to-LDS single-group kernel, NN, an even number of fragments per wave
+// along N (gate and up halves), and DMA-compatible half tiles of BN/2 columns.
+template <int DT, bool TA, bool TB, int DMA, int BM, int BN, int BK, int WM, int WN>
+constexpr bool w12_ok() {
+    constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
+    return (DMA == 1 || (DT == DT_E4M3 && DMA != 2)) && !TA && !TB && (BN / WN / 32) % 2 == 0 &&
+           BN % 64 == 0 && dma_tile_ok(true, BM, BK, ESZ, WM * WN) &&
+           dma_tile_ok(false, BN / 2, BK, ESZ, WM * WN);
+}
+
 template <int DT, bool TA, bool TB, int EPI, int DMA, int BM, int BN, int BK, int S, int WM, int WN>
 inline hipError_t launch_one(const Gemm16Params& p, int splits, hipStream_t st) {
     constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
-    if constexpr (DMA == 2) {
+    if constexpr (EPI == EPI_SWIGLU_W12) {
+        if constexpr (w12_ok<DT, TA, TB, DMA, BM, BN, BK, WM, WN>())
+            return launch_grid(gemm_dma_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
+                               64 * WM * WN, st);
+        else
+            return hipErrorInvalidValue;
+    } else if constexpr (DMA == 2) {
         if constexpr (dma_tile_ok(!TA, BM, BK, ESZ, 4) && dma_tile_ok(TB, BN, BK, ESZ, 4))
             return launch_grid(gemm_pp_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
                                64 * WM * WN, st);
@@ -58,11 +75,14 @@ hipError_t launch16_cfg(int cfg, const Gemm16Params& p, int splits, hipStream_t 
 #undef SG_CASE
 }
 
-// epi: EPI_GEMM / EPI_PARTIAL for any transpose pair; EPI_SWIGLU for NN only.
+// epi: EPI_GEMM / EPI_PARTIAL for any transpose pair; EPI_SWIGLU(_W12) for NN only.
 template <int DT, bool TA, bool TB>
 hipError_t launch16_tr(int epi, int cfg, const Gemm16Params& p, int splits, hipStream_t st) {
-    if constexpr (!TA && !TB)
+    if constexpr (!TA && !TB) {
         if (epi == EPI_SWIGLU) return launch16_cfg<DT, TA, TB, EPI_SWIGLU>(cfg, p, splits, st);
+        if (epi == EPI_SWIGLU_W12)
+            return launch16_cfg<DT, TA, TB, EPI_SWIGLU_W12>(cfg, p, splits, st);
+    }
     if (epi == EPI_GEMM) return launch16_cfg<DT, TA, TB, EPI_GEMM>(cfg, p, splits, st);
     if (epi == EPI_PARTIAL) return launch16_cfg<DT, TA, TB, EPI_PARTIAL>(cfg, p, splits, st);
     return hipErrorInvalidValue;

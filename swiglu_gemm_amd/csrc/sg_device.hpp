@@ -15,7 +15,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3 };
-enum : int { EPI_GEMM = 0, EPI_SWIGLU = 1, EPI_PARTIAL = 2 };
+enum : int { EPI_GEMM = 0, EPI_SWIGLU = 1, EPI_PARTIAL = 2, EPI_SWIGLU_W12 = 3 };
 
 // ---------------------------------------------------------------------------
 // 16-bit storage <-> fp32
@@ -48,10 +48,11 @@ __device__ __forceinline__ float silu(float x) {
 // Arguments of the 16-bit / 8-bit MFMA GEMM kernels.
 struct Gemm16Params {
     const uint16_t* A;   // storage of A (16-bit elements; e4m3 kernels reinterpret)
-    const uint16_t* B;
-    void* C;            // EPI_GEMM: C (dtype); EPI_SWIGLU: Y; EPI_PARTIAL: fp32 workspace
+    const uint16_t* B;   // EPI_SWIGLU_W12: W1
+    const uint16_t* B2;  // EPI_SWIGLU_W12: W2 (same shape and ld as W1)
+    void* C;            // EPI_GEMM: C (dtype); EPI_SWIGLU(_W12): Y; EPI_PARTIAL: fp32 workspace
     int64_t lda, ldb, ldc;
-    int M, N, K;        // N is the fused width 2*N_out for SwiGLU / its partials
+    int M, N, K;        // N is the fused width 2*N_out for SwiGLU (both forms) / partials
     float alpha, beta;  // SwiGLU: alpha = scale_a * scale_w
     int vec_a, vec_b, vec_c;
     int tiles_m, tiles_n, group_m;

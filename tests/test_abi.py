@@ -77,6 +77,23 @@ def test_swiglu_argument_validation(L):
     assert sw(M=0) == 0
 
 
+def test_swiglu_w12_argument_validation(L):
+    def sw(A=P, W1=P, W2=P, Y=P, M=2, N=2, K=2, dt=2, sa=1.0, sw_=1.0):
+        return L.sg_swiglu_gemm_w12(A, W1, W2, Y, M, N, K, dt, sa, sw_, NUL)
+    assert sw(A=NUL) == -1
+    assert sw(W1=NUL) == -2
+    assert sw(W2=NUL) == -3
+    assert sw(Y=NUL) == -4
+    assert sw(M=-1) == -5
+    assert sw(N=-1) == -6
+    assert sw(K=-1) == -7
+    assert sw(dt=0) == -8
+    assert sw(dt=3, sa=0.0) == -9
+    assert sw(dt=3, sw_=float("inf")) == -10
+    assert sw(dt=2, sw_=2.0) == -10                  # scales must be 1 for bf16
+    assert sw(N=0) == 0
+
+
 def test_other_entry_points_validation(L):
     assert L.sg_interleave_gate_up(NUL, P, P, 1, 1, 2, NUL) == -1
     assert L.sg_interleave_gate_up(P, P, P, -1, 1, 2, NUL) == -4

@@ -1,0 +1,128 @@
+"""GPU parity of the split-weight fused SwiGLU-GEMM (separate W1, W2; the
+non-interleaved weight layout of Kernel-1 in "Resumo Técnico: Sobreposição de
+Ativação em Nível de Tile ...", Metodologia) against the fp64 oracle, through the
+C ABI.  The oracle takes W_fused, so the reference interleaves W1, W2 on the CPU
+(oracle.interleave) -- a layout step with no arithmetic."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from swiglu_gemm_amd import inputs
+from helpers import assert_close, bits_equal, from_dev, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+W12_CFGS16 = [10, 8, 6]          # configurations that can take separate weights
+W12_CFGS8 = [14, 16, 33]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import swiglu_gemm_amd as sg
+    sg.lib()
+    yield
+    os.environ.pop("SG_FORCE_CONFIG", None)
+
+
+def run_w12(pb, M, N, K, dtype):
+    import swiglu_gemm_amd as sg
+    A = to_dev(pb["A"], dtype)
+    W1, W2 = to_dev(pb["W1"], dtype), to_dev(pb["W2"], dtype)
+    out = torch.bfloat16 if dtype in ("bf16", "e4m3") else torch.float16
+    Y = torch.full((M, N), float("nan"), dtype=out, device="cuda:0")
+    print("swiglu_w12 %s M=%d N=%d K=%d" % (dtype, M, N, K), flush=True)
+    sg.swiglu_gemm_w12(A, W1, W2, Y, pb.get("scale_a", 1.0), pb.get("scale_w", 1.0))
+    torch.cuda.synchronize()
+    return from_dev(Y), sg.last_config()
+
+
+def reference(pb, M, N, K, dtype):
+    Wf = oracle.interleave(pb["W1"], pb["W2"])
+    return oracle.swiglu(M, N, K, pb["A"], Wf, dtype, pb.get("scale_a", 1.0),
+                         pb.get("scale_w", 1.0))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(256, 512, 512), (300, 1000, 640), (2048, 4864, 128)])
+def test_w12_16bit(dtype, shape):
+    M, N, K = shape
+    pb = inputs.swiglu_problem(130, M, N, K, dtype)
+    y, cfg = run_w12(pb, M, N, K, dtype)
+    assert "swiglu_w12 cfg=" in cfg, cfg                  # the direct kernel, not the fallback
+    out = "f16" if dtype == "f16" else "bf16"
+    assert_close(oracle.decode(y, out), reference(pb, M, N, K, dtype), dtype, K, cfg)
+
+
+@pytest.mark.parametrize("cfg", W12_CFGS16)
+def test_w12_every_config_bit_equal_to_interleaved(cfg):
+    """Same tile configuration, same K order: the split-weight kernel and the
+    interleaved kernel produce identical bits; both meet the oracle."""
+    import swiglu_gemm_amd as sg
+    M, N, K = 384, 1280, 512
+    pb = inputs.swiglu_problem(140 + cfg, M, N, K, "bf16")
+    os.environ["SG_FORCE_CONFIG"] = "%d,1" % cfg
+    try:
+        y1, desc = run_w12(pb, M, N, K, "bf16")
+        A = to_dev(pb["A"], "bf16")
+        Wf = to_dev(oracle.interleave(pb["W1"], pb["W2"]), "bf16")
+        Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        sg.swiglu_gemm(A, Wf, Y)
+        torch.cuda.synchronize()
+        desc2 = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "swiglu_w12 cfg=%d " % cfg in desc, desc
+    assert "cfg=%d " % cfg in desc2, desc2
+    assert bits_equal(y1, from_dev(Y)), (desc, desc2)
+    assert_close(oracle.decode(y1, "bf16"), reference(pb, M, N, K, "bf16"), "bf16", K, desc)
+
+
+@pytest.mark.parametrize("cfg", W12_CFGS8)
+@pytest.mark.parametrize("M", [16, 300])
+def test_w12_e4m3(cfg, M):
+    N, K = 1536, 1024
+    pb = inputs.swiglu_problem(150 + cfg, M, N, K, "e4m3")
+    os.environ["SG_FORCE_CONFIG"] = "%d,1" % cfg
+    try:
+        y, desc = run_w12(pb, M, N, K, "e4m3")
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "swiglu_w12 cfg=%d " % cfg in desc, desc
+    assert_close(oracle.decode(y, "bf16"), reference(pb, M, N, K, "e4m3"), "e4m3", K, desc)
+
+
+@pytest.mark.parametrize("shape", [(37, 50, 70), (64, 101, 256), (5, 64, 8)])
+def test_w12_fallback_shapes(shape):
+    """K tails and rows that are not 16-byte multiples go through W_fused."""
+    M, N, K = shape
+    pb = inputs.swiglu_problem(160, M, N, K, "bf16")
+    y, cfg = run_w12(pb, M, N, K, "bf16")
+    assert "via W_fused" in cfg, cfg
+    assert_close(oracle.decode(y, "bf16"), reference(pb, M, N, K, "bf16"), "bf16", K, cfg)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_w12_one_hot_bit_exact(dtype):
+    """W1, W2 select columns of A: gate sources powers of two in [32, 256], up
+    sources integers in [-3, 3], so Y = g*u exactly."""
+    M, N, K = 128, 512, 1024
+    gen = np.random.default_rng(7)
+    half = K // 2
+    A = np.zeros((M, K))
+    A[:, :half] = 2.0 ** gen.integers(5, 9, size=(M, half))
+    A[:, half:] = gen.integers(-3, 4, size=(M, K - half))
+    pi1 = gen.integers(0, half, size=N)
+    pi2 = half + gen.integers(0, K - half, size=N)
+    W1 = np.zeros((K, N))
+    W2 = np.zeros((K, N))
+    W1[pi1, np.arange(N)] = 1.0
+    W2[pi2, np.arange(N)] = 1.0
+    pb = dict(A=inputs.to_storage(A, dtype), W1=inputs.to_storage(W1, dtype),
+              W2=inputs.to_storage(W2, dtype), scale_a=1.0, scale_w=1.0)
+    y, cfg = run_w12(pb, M, N, K, dtype)
+    assert np.array_equal(oracle.decode(y, "bf16"), A[:, pi1] * A[:, pi2]), cfg
