@@ -154,7 +154,7 @@ struct Cand16 {
     int id;
     double tf_per_cu;
 };
-constexpr Cand16 kCand16[] = {{10, 4.7}, {24, 5.0}, {13, 3.6}, {6, 3.4}};
+constexpr Cand16 kCand16[] = {{10, 4.7}, {24, 5.0}, {13, 3.6}, {32, 3.6}, {6, 3.4}};
 constexpr double kTileOverheadUs = 3.0;   // pipeline fill + epilogue per tile
 
 double est_us(const Cfg16& c, const Problem16& q, int splits, double tf_per_cu) {
@@ -173,14 +173,19 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
     const bool forced = forced_config(&cfg, &splits) && cfg >= 0 && cfg < kNumCfg16 &&
                         (kCfg16[cfg].e4m3 != 0) == e4m3;
     if (!forced) {
+        cfg = -1;   // a forced id of the other operand width is ignored entirely
         splits = 0;
         if (e4m3) {
             // measured on MI355X: 256x256 tiles once there are >= 2 full rounds of
-            // them, else 128x128 tiles while M allows two 128-row tiles, else
-            // 32-row tiles (256 wide when that still gives half a round)
+            // them; from M = 256, 128x256 tiles while they fit one round (the weights
+            // stream from HBM once, with a 3-deep ring), else 128x128; below, 32-row
+            // tiles (256 wide when that still gives half a round)
             const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
-            cfg = big >= 2 * kNumCU ? 14
-                                    : (q.M >= 256 ? 15 : (cdiv(q.N, 256) >= 128 ? 16 : 17));
+            const int64_t mid = cdiv(q.M, 128) * cdiv(q.N, 256);
+            cfg = big >= 2 * kNumCU
+                      ? 14
+                      : (q.M >= 256 ? (mid <= kNumCU ? 33 : 15)
+                                    : (cdiv(q.N, 256) >= 128 ? 16 : 17));
         } else {
             double best = 0.0;
             for (const Cand16& cand : kCand16) {
@@ -193,6 +198,12 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
                     best = t;
                 }
             }
+            // one round of 128x128 tiles: the 5-deep ring keeps more of the operand
+            // stream in flight (measured: 10.4 vs 13.3 us hot, 13.3 vs 18.2 us with the
+            // weights in HBM, bf16 SwiGLU M = 128)
+            if (cfg == 13 && cdiv(q.M, 128) * cdiv(q.N, 128) <= kNumCU &&
+                dma_ok(kCfg16[30], q, split_len(q.K, pick_splits(kCfg16[30], q), 64)))
+                cfg = 30;
             if (cfg < 0) cfg = cdiv(q.M, 256) * cdiv(q.N, 256) >= kNumCU ? 0 : 2;
         }
     }
@@ -354,7 +365,7 @@ hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alp
 // ------------------------------------------------ split-weight SwiGLU (W1, W2)
 // Configurations that can run it (see w12_ok in launch16.hpp): 16-bit candidates
 // weighed with the same cost model as the interleaved kernel; e4m3 by rows.
-constexpr Cand16 kCandW12[] = {{10, 4.7}, {8, 4.7}, {6, 3.4}};
+constexpr Cand16 kCandW12[] = {{10, 4.7}, {8, 4.7}, {32, 3.6}, {6, 3.4}};
 
 bool w12_cfg_ok(const Cfg16& c, const Problem16& q_out) {
     // c runs on [M, 2N, K]; each weight is a K x N row-contiguous operand of BN/2 columns
