@@ -30,6 +30,8 @@ Counter helpers (used to produce the committed HBM-traffic figure):
 
 Power-limited MFMA ceiling (context for roofline.frac, a separate run):
     python bench.py --mfma-ceiling         # pure MFMA loop on zero / constant / random data
+Pipeline-depth / tile study of the headline GEMM, with hipBLASLt beside it:
+    python bench.py --stage-sweep          # one JSON line per configuration
 """
 from __future__ import annotations
 
@@ -341,6 +343,138 @@ def pmc_summarize(fetch_csv, write_csv):
     print(json.dumps(res, indent=1))
 
 
+SWEEP_CFGS = (10, 8, 34, 35, 9, 27, 5, 41, 3, 40, 19, 42, 13, 36, 37, 30, 38, 39, 6, 31)
+
+
+def stage_sweep(steps):
+    """Pipeline-depth / tile study on the headline fp16 8192^3 NN GEMM: every listed
+    configuration forced in turn (SG_FORCE_CONFIG), three rotated input sets, HIP
+    events; then torch.mm (hipBLASLt) on the same inputs in fp16 and bf16.  One
+    JSON line per case.  Run under rocprofv3 --kernel-trace so the per-kernel
+    register and LDS use can be joined in (--stage-sweep-summarize)."""
+    import torch
+    import swiglu_gemm_amd as sg
+    from swiglu_gemm_amd import inputs
+    sg.lib()
+    M = N = K = 8192
+    _, sets = gemm_inputs(inputs, torch, M, N, K, 3)
+    flops = 2.0 * M * N * K
+    for cfg in SWEEP_CFGS:
+        os.environ["SG_FORCE_CONFIG"] = "%d,1" % cfg
+
+        def step(i):
+            A, B, C = sets[i % 3]
+            sg.gemm(A, B, C)
+        try:
+            ms = time_steps(step, steps, 3, torch)
+        finally:
+            os.environ.pop("SG_FORCE_CONFIG", None)
+        print(json.dumps({"stage_sweep": cfg, "kernel_config": sg.last_config(), "ms": round(ms, 5),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
+    for dt in (torch.float16, torch.bfloat16):
+        mats = [(A.to(dt), B.to(dt)) for A, B, _ in sets]
+
+        def lib_step(i):
+            A, B = mats[i % 3]
+            torch.mm(A, B)
+        ms = time_steps(lib_step, steps, 3, torch)
+        print(json.dumps({"stage_sweep": "torch.mm (hipBLASLt)", "dtype": str(dt).split(".")[-1],
+                          "ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}),
+              flush=True)
+        del mats
+
+
+STAGE_SWEEP_FILE = os.path.join(ROOT, "profiles", "stage_sweep_gemm16_f16_nn_8192.md")
+
+
+def stage_sweep_summarize(trace_csv, sweep_jsonl):
+    """Join the stage sweep's timings with the per-kernel VGPR / LDS use of the same
+    run (rocprofv3 --kernel-trace), compute occupancy, and fit the pipeline model
+    of the Ada Lovelace page (throughput proportional to S/(S+kappa)) alone and with
+    an occupancy factor W/(W+omega) (W = resident waves per SIMD), one tile
+    efficiency A per tile family.  Writes STAGE_SWEEP_FILE."""
+    import re
+    from scipy.optimize import least_squares
+    res = {}
+    for r in csv.DictReader(open(trace_csv)):
+        m = re.search(r"gemm_(dma|pp)_kernel<1, false, false, 0, (\d+), (\d+), (\d+), (\d+), (\d+), "
+                      r"(\d+)>", r["Kernel_Name"])
+        if not m:
+            continue
+        key = (m.group(1),) + tuple(int(x) for x in m.group(2, 3, 4, 5, 6, 7))
+        res[key] = (int(r["VGPR_Count"]) + int(r["Accum_VGPR_Count"]), int(r["LDS_Block_Size"]))
+    pts, lib = [], []
+    for line in open(sweep_jsonl):
+        if not line.startswith("{"):
+            continue
+        d = json.loads(line)
+        if not isinstance(d["stage_sweep"], int):
+            lib.append(d)
+            continue
+        m = re.search(r"(dma|pp) (\d+)x(\d+)x(\d+) s(\d+) (\d+)x(\d+)w", d["kernel_config"])
+        kind, BM, BN, BK, S, WM, WN = (m.group(1),) + tuple(int(x) for x in m.group(2, 3, 4, 5, 6, 7))
+        vgpr, lds = res[(kind, BM, BN, BK, S, WM, WN)]
+        waves = WM * WN
+        per_simd = -(-waves // 4)
+        alloc = -(-max(vgpr, 1) // 8) * 8
+        by_lds = (160 * 1024) // lds
+        by_regs = (512 // alloc) // per_simd
+        ctas = max(1, min(by_lds, by_regs, 8 // per_simd))
+        pts.append(dict(cfg=d["stage_sweep"], kind=kind, BM=BM, BN=BN, BK=BK, S=S, waves=waves,
+                        vgpr=vgpr, lds=lds, ctas=ctas, W=ctas * per_simd, tf=d["tflops"],
+                        fam="%s %dx%dx%d %dw" % (kind, BM, BN, BK, waves)))
+    fams = sorted(set(p_["fam"] for p_ in pts))
+    S = np.array([p_["S"] for p_ in pts], float)
+    W = np.array([p_["W"] for p_ in pts], float)
+    T = np.array([p_["tf"] for p_ in pts], float)
+    F = np.array([fams.index(p_["fam"]) for p_ in pts])
+
+    def model(x, occ):
+        A = x[:len(fams)][F]
+        kap = x[len(fams)]
+        om = x[len(fams) + 1] if occ else 0.0
+        return A * S / (S + kap) * (W / (W + om) if occ else 1.0)
+
+    fits = {}
+    for occ in (False, True):
+        x0 = [1300.0] * len(fams) + [0.5] + ([0.5] if occ else [])
+        lb = [0.0] * len(fams) + [0.0] + ([0.0] if occ else [])
+        r = least_squares(lambda x: (model(x, occ) - T) / T, x0, bounds=(lb, np.inf))
+        fits[occ] = r.x
+    lines = ["# Pipeline depth and tile study: fp16 8192^3 NN GEMM on one MI355X", "",
+             "Commands (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "```", "rocprofv3 --kernel-trace --output-format csv -d <out> -o sw -- "
+             "python <repo>/bench.py --stage-sweep > sweep.jsonl",
+             "python bench.py --stage-sweep-summarize <out>/sw_kernel_trace.csv sweep.jsonl", "```", "",
+             "Every configuration forced in turn, three rotated input sets, HIP events; VGPR "
+             "(arch + accumulation) and LDS per work-group from the kernel trace of the same run. "
+             "Work-groups per CU = min(160 KiB / LDS, 512 registers / VGPRs per wave / waves per "
+             "SIMD, 8 wave slots); W = resident waves per SIMD.", "",
+             "Model of the Ada Lovelace page: throughput = A * S/(S + kappa) (pipeline efficiency; "
+             "one A per tile family); extended with occupancy: * W/(W + omega). Fitted "
+             "(relative least squares) over all rows:", "",
+             "* S/(S+kappa): kappa = %.3f" % fits[False][len(fams)],
+             "* S/(S+kappa) * W/(W+omega): kappa = %.3f, omega = %.3f" % (fits[True][len(fams)],
+                                                                          fits[True][len(fams) + 1]),
+             "", "| family | S | LDS KiB | VGPR | WG/CU | W | TFLOP/s | S/(S+k) model | with occupancy |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    m0, m1 = model(fits[False], False), model(fits[True], True)
+    for i, p_ in enumerate(pts):
+        lines.append("| %s | %d | %d | %d | %d | %d | %.1f | %.1f (%+.1f%%) | %.1f (%+.1f%%) |" % (
+            p_["fam"], p_["S"], p_["lds"] // 1024, p_["vgpr"], p_["ctas"], p_["W"], p_["tf"],
+            m0[i], 100 * (m0[i] / p_["tf"] - 1), m1[i], 100 * (m1[i] / p_["tf"] - 1)))
+    err0 = np.abs(m0 / T - 1).mean() * 100
+    err1 = np.abs(m1 / T - 1).mean() * 100
+    lines += ["", "Mean absolute model error: %.1f %% (pipeline term only), %.1f %% (with occupancy)."
+              % (err0, err1), ""]
+    for d in lib:
+        lines.append("hipBLASLt (torch.mm, same inputs, same run), %s: %.1f TFLOP/s." %
+                     (d["dtype"], d["tflops"]))
+    with open(STAGE_SWEEP_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def mfma_ceiling():
     """Sustained rate of a pure MFMA loop (no memory traffic) on zero, constant and
     random operand data, per dtype.  The matrix cores' power grows with the
@@ -357,7 +491,8 @@ def mfma_ceiling():
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
     nsrc = 8192                                     # 16-byte operand chunks
     gen = torch.Generator(device="cuda:0").manual_seed(7)
-    for kind, dt in ((0, "f16"), (1, "bf16"), (2, "e4m3")):
+    for kind, dt, shape in ((0, "f16", "32x32x16"), (1, "bf16", "32x32x16"), (2, "e4m3", "32x32x64"),
+                            (3, "f16", "16x16x32"), (4, "bf16", "16x16x32")):
         tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}[dt]
         per = 16 // torch.empty(0, dtype=tdt).element_size()
         datas = {
@@ -385,7 +520,7 @@ def mfma_ceiling():
             ms = e0.elapsed_time(e1) / 5
             flops = blocks * 4 * iters * 8 * 2 * 32 * 32 * (64 if kind == 2 else 16)
             tf = flops / (ms * 1e-3) / 1e12
-            print(json.dumps({"mfma_ceiling": dt, "operands": name, "ms": round(ms, 4),
+            print(json.dumps({"mfma_ceiling": dt, "mfma": shape, "operands": name, "ms": round(ms, 4),
                               "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK[dt], 4)}),
                   flush=True)
 
@@ -401,6 +536,8 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--mfma-ceiling", action="store_true")
+    ap.add_argument("--stage-sweep", action="store_true")
+    ap.add_argument("--stage-sweep-summarize", nargs=2, metavar=("TRACE_CSV", "SWEEP_JSONL"))
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only (the library is single-GPU); --gpus %d is not "
@@ -409,11 +546,17 @@ def main():
     if args.pmc_summarize:
         pmc_summarize(*args.pmc_summarize)
         return
+    if args.stage_sweep_summarize:
+        stage_sweep_summarize(*args.stage_sweep_summarize)
+        return
     if args.pmc_probe:
         pmc_probe()
         return
     if args.mfma_ceiling:
         mfma_ceiling()
+        return
+    if args.stage_sweep:
+        stage_sweep(max(10, args.steps // 2))
         return
 
     import torch

@@ -50,10 +50,21 @@ constexpr Cfg16 kCfg16[] = {
     {0, 1, 128, 128, 32, 8, 2, 2, "dma 128x128x32 s8 2x2w"},
     {0, 1, 128, 256, 64, 3, 2, 4, "dma 128x256x64 s3 2x4w"},
     {1, 1, 128, 256, 128, 3, 2, 2, "e4m3 dma 128x256x128 s3 2x2w"},
+    // pipeline-depth study only (fp16 NN GEMM; never chosen automatically)
+    {0, 1, 256, 256, 32, 2, 4, 2, "sweep dma 256x256x32 s2 4x2w"},
+    {0, 1, 256, 256, 32, 3, 4, 2, "sweep dma 256x256x32 s3 4x2w"},
+    {0, 1, 128, 128, 64, 3, 2, 4, "sweep dma 128x128x64 s3 2x4w"},
+    {0, 1, 128, 128, 64, 4, 2, 4, "sweep dma 128x128x64 s4 2x4w"},
+    {0, 1, 128, 128, 32, 2, 2, 2, "sweep dma 128x128x32 s2 2x2w"},
+    {0, 1, 128, 128, 32, 3, 2, 2, "sweep dma 128x128x32 s3 2x2w"},
+    {0, 1, 256, 256, 32, 5, 2, 2, "sweep dma 256x256x32 s5 2x2w"},
+    {0, 1, 256, 256, 32, 3, 2, 2, "sweep dma 256x256x32 s3 2x2w"},
+    {0, 2, 256, 256, 32, 5, 4, 2, "sweep pp 256x256x32 s5 4x2w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
 constexpr int kFirstCfgE4M3 = 14;
+constexpr int kFirstSweepCfg = 34;   // ids >= this: the fp16 NN pipeline-depth study
 
 // Whether the direct-to-LDS kernel supports an operand tile: k-contiguous rows of
 // 64 or 128 bytes; row-contiguous rows of 128..1024 bytes made of an even number
@@ -96,6 +107,18 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(30, 1, 128, 128, 64, 5, 2, 4)    \
     X(31, 1, 128, 128, 32, 8, 2, 2)    \
     X(32, 1, 128, 256, 64, 3, 2, 4)
+
+// the pipeline-depth study rows, instantiated for fp16 NN EPI_GEMM only
+#define SG_CONFIGS_SWEEP(X)            \
+    X(34, 1, 256, 256, 32, 2, 4, 2)    \
+    X(35, 1, 256, 256, 32, 3, 4, 2)    \
+    X(36, 1, 128, 128, 64, 3, 2, 4)    \
+    X(37, 1, 128, 128, 64, 4, 2, 4)    \
+    X(38, 1, 128, 128, 32, 2, 2, 2)    \
+    X(39, 1, 128, 128, 32, 3, 2, 2)    \
+    X(40, 1, 256, 256, 32, 5, 2, 2)    \
+    X(41, 1, 256, 256, 32, 3, 2, 2)    \
+    X(42, 2, 256, 256, 32, 5, 4, 2)
 
 // the same for every e4m3 row (all direct-to-LDS)
 #define SG_CONFIGS_E4M3(X)             \

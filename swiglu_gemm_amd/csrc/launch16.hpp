@@ -69,8 +69,15 @@ hipError_t launch16_cfg(int cfg, const Gemm16Params& p, int splits, hipStream_t 
     } else {
         switch (cfg) {
             SG_CONFIGS(SG_CASE)
-            default: return hipErrorInvalidValue;
+            default: break;
         }
+        if constexpr (DT == DT_F16 && !TA && !TB && EPI == EPI_GEMM) {
+            switch (cfg) {
+                SG_CONFIGS_SWEEP(SG_CASE)
+                default: break;
+            }
+        }
+        return hipErrorInvalidValue;
     }
 #undef SG_CASE
 }

@@ -16,9 +16,11 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // KIND 0: v_mfma_f32_32x32x16_f16, 1: ..._bf16, 2: v_mfma_scale_f32_32x32x64_f8f6f4
-// (e4m3 operands, unit block scales)
+// (e4m3 operands, unit block scales); 3, 4: v_mfma_f32_16x16x32_{f16,bf16} (same
+// operand registers, sixteen 4-register accumulators so the work per round matches)
 template <int KIND>
 __global__ void __launch_bounds__(256) mfma_loop(const u32x4* src, int nsrc, int iters,
                                                  float* out) {
@@ -30,6 +32,28 @@ __global__ void __launch_bounds__(256) mfma_loop(const u32x4* src, int nsrc, int
         b[i] = src[(base + 4 + i) % nsrc];
     }
     f32x16 c[8] = {};
+    if constexpr (KIND >= 3) {
+        f32x4 d[16] = {};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const u32x4 x = a[u & 3], y = b[(u >> 2) & 3];
+                if constexpr (KIND == 3)
+                    d[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
+                                                                  __builtin_bit_cast(f16x8, y),
+                                                                  d[u], 0, 0, 0);
+                else
+                    d[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                                   __builtin_bit_cast(bf16x8, y),
+                                                                   d[u], 0, 0, 0);
+            }
+        }
+        float s4 = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s4 += d[u][threadIdx.x & 3];
+        out[blockIdx.x * 256 + threadIdx.x] = s4;
+        return;
+    }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -64,10 +88,11 @@ __global__ void __launch_bounds__(256) mfma_loop(const u32x4* src, int nsrc, int
 
 // Launches `blocks` work-groups of 4 waves.  src: nsrc 16-byte operand chunks
 // (device); out: blocks*256 floats (device).  Returns a hipError_t.  Work:
-// blocks*4*iters*8 MFMAs of 2*32*32*16 (kinds 0, 1) or 2*32*32*64 (kind 2) flops.
+// blocks*4*iters*8 MFMAs of 2*32*32*16 (kinds 0, 1) or 2*32*32*64 (kind 2) flops;
+// kinds 3, 4: blocks*4*iters*16 MFMAs of 2*16*16*32 flops (the same total).
 extern "C" int sg_diag_mfma_loop(int kind, int blocks, const void* src, int nsrc, int iters,
                                  void* out, void* stream) {
-    if (kind < 0 || kind > 2 || blocks <= 0 || nsrc <= 0 || iters < 0 || !src || !out)
+    if (kind < 0 || kind > 4 || blocks <= 0 || nsrc <= 0 || iters < 0 || !src || !out)
         return (int)hipErrorInvalidValue;
     hipStream_t st = (hipStream_t)stream;
     const u32x4* s = (const u32x4*)src;
@@ -75,5 +100,7 @@ extern "C" int sg_diag_mfma_loop(int kind, int blocks, const void* src, int nsrc
     if (kind == 0) hipLaunchKernelGGL(mfma_loop<0>, dim3(blocks), dim3(256), 0, st, s, nsrc, iters, o);
     if (kind == 1) hipLaunchKernelGGL(mfma_loop<1>, dim3(blocks), dim3(256), 0, st, s, nsrc, iters, o);
     if (kind == 2) hipLaunchKernelGGL(mfma_loop<2>, dim3(blocks), dim3(256), 0, st, s, nsrc, iters, o);
+    if (kind == 3) hipLaunchKernelGGL(mfma_loop<3>, dim3(blocks), dim3(256), 0, st, s, nsrc, iters, o);
+    if (kind == 4) hipLaunchKernelGGL(mfma_loop<4>, dim3(blocks), dim3(256), 0, st, s, nsrc, iters, o);
     return (int)hipGetLastError();
 }

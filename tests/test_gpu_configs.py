@@ -171,3 +171,28 @@ def test_wide_tiles_swiglu_and_identity(cfg):
         os.environ.pop("SG_FORCE_CONFIG", None)
     assert "cfg=%d " % cfg in desc, desc
     assert bits_equal(from_dev(C), Ab), desc
+
+
+@pytest.mark.parametrize("cfg", [34, 35, 36, 37, 38, 39, 40, 41, 42])
+def test_pipeline_study_configs_fp16_nn(cfg):
+    """The pipeline-depth study configurations (fp16 NN GEMM only) against the
+    oracle, on a ragged shape that spans several tiles; other dtypes reject them."""
+    import swiglu_gemm_amd as sg
+    M, N, K = 520, 1000, 640
+    p = inputs.gemm_problem(170 + cfg, "N", "N", M, N, K, "f16", "normal", ld_mode="padded")
+    A, B, C = to_dev(p["A"], "f16"), to_dev(p["B"], "f16"), to_dev(p["C"], "f16")
+    forced(cfg, 1)
+    print("study cfg %d" % cfg, flush=True)
+    try:
+        sg.gemm(A, B, C, alpha=0.7, beta=0.3, M=M, N=N, K=K, lda=p["lda"], ldb=p["ldb"],
+                ldc=p["ldc"], dtype=1)
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    ref = oracle.gemm("N", "N", M, N, K, 0.7, p["A"], p["lda"], p["B"], p["ldb"], 0.3, p["C"],
+                      p["ldc"], "f16")
+    cbits = from_dev(C)
+    assert bits_equal(cbits[:, N:], p["C"][:, N:]), "ld padding of C was written"
+    assert_close(oracle.decode(cbits, "f16")[:, :N], ref[:, :N], "f16", K, desc)
