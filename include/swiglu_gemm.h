@@ -70,6 +70,29 @@ int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K,
             float beta, void* C, int64_t ldc, int dtype, void* stream);
 
 /*
+ * sg_gemm_strided_batched: for b in [0, batch): C_b = alpha * op(A_b) * op(B_b)
+ * + beta * C_b, with X_b = X + b * strideX elements -- the same BLAS update as
+ * sg_gemm ("GEMM o Coração Matemático" §1, §2) over a batch of equally shaped
+ * problems in one launch: the batched products of the same page's §13.2, where
+ * attention's score and context steps are one GEMM per (sequence, head).
+ *
+ * Arguments 1-8 and 10, 11, 13-15, 18, 19 as sg_gemm (transA, transB, M, N, K,
+ * alpha, A, lda, B, ldb, beta, C, ldc, dtype, stream); 9 strideA, 12 strideB,
+ * 16 strideC: element distance between consecutive problems (>= 0; 0 repeats
+ * the operand for every problem; strideC must keep the outputs disjoint:
+ * >= (M-1)*ldc + N when batch > 1); 17 batch: number of problems, 0..65535.
+ * Split-K is not used inside a batch.  Quick returns as sg_gemm, per problem;
+ * batch == 0 does nothing.
+ * Invalid: as sg_gemm at the shifted positions (-1..-5, -7, -8, -10, -11, -14,
+ * -15, -18), negative stride (-9/-12), overlapping outputs (-16), batch (-17).
+ */
+int sg_gemm_strided_batched(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                            float alpha, const void* A, int64_t lda, int64_t strideA,
+                            const void* B, int64_t ldb, int64_t strideB, float beta, void* C,
+                            int64_t ldc, int64_t strideC, int64_t batch, int dtype,
+                            void* stream);
+
+/*
  * sg_swiglu_gemm: Y = SiLU(s * A * W1) ⊙ (s * A * W2), s = scale_a * scale_w.
  *
  * The gated MLP of "Resumo Técnico: Sobreposição de Ativação em Nível de Tile para

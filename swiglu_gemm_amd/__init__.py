@@ -47,6 +47,9 @@ def lib() -> ctypes.CDLL:
         L.sg_gemm.argtypes = [c, c, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
                               ctypes.c_int, vp]
         L.sg_gemm.restype = ctypes.c_int
+        L.sg_gemm_strided_batched.argtypes = [c, c, i64, i64, i64, f32, vp, i64, i64, vp, i64,
+                                              i64, f32, vp, i64, i64, i64, ctypes.c_int, vp]
+        L.sg_gemm_strided_batched.restype = ctypes.c_int
         L.sg_swiglu_gemm.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, f32, f32, vp]
         L.sg_swiglu_gemm.restype = ctypes.c_int
         L.sg_swiglu_gemm_w12.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, f32, f32,
@@ -133,6 +136,31 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N", tran
                        int(ldb), float(beta), ctypes.c_void_p(C.data_ptr()), int(ldc), code,
                        _stream(C))
     _check(st, "sg_gemm")
+    return C
+
+
+def gemm_strided_batched(A, B, C, batch, strideA, strideB, strideC, alpha: float = 1.0,
+                         beta: float = 0.0, transA: str = "N", transB: str = "N",
+                         dtype: int | None = None, M=None, N=None, K=None, lda=None, ldb=None,
+                         ldc=None):
+    """C_b = alpha * op(A_b) @ op(B_b) + beta * C_b for b < batch, X_b = X + b*strideX
+    elements (A, B, C: device tensors whose storage holds every problem; sizes and
+    leading dimensions default to those of the 2-D views given)."""
+    code = _dtype_code(A) if dtype is None else dtype
+    ta, tb = transA.upper(), transB.upper()
+    if M is None:
+        M = A.size(-1) if ta == "T" else A.size(-2)
+        K = A.size(-2) if ta == "T" else A.size(-1)
+        N = B.size(-2) if tb == "T" else B.size(-1)
+    lda = A.stride(-2) if lda is None else lda
+    ldb = B.stride(-2) if ldb is None else ldb
+    ldc = C.stride(-2) if ldc is None else ldc
+    st = lib().sg_gemm_strided_batched(ta.encode(), tb.encode(), int(M), int(N), int(K),
+                                       float(alpha), ctypes.c_void_p(A.data_ptr()), int(lda),
+                                       int(strideA), ctypes.c_void_p(B.data_ptr()), int(ldb),
+                                       int(strideB), float(beta), ctypes.c_void_p(C.data_ptr()),
+                                       int(ldc), int(strideC), int(batch), code, _stream(C))
+    _check(st, "sg_gemm_strided_batched")
     return C
 
 

@@ -111,6 +111,13 @@ struct Problem16 {
     bool vec_a, vec_b;    // 16-byte aligned base and ld*size % 16 == 0
     bool ta, tb;          // transposes
     int esz;              // operand element size (2: fp16/bf16, 1: e4m3)
+    int64_t batch = 1;    // problems of a strided batch (one launch, gridDim.z)
+};
+
+// A strided batch: n problems, operands sA / sB / sC bytes apart.
+struct Batch {
+    int64_t n = 1;
+    int64_t sA = 0, sB = 0, sC = 0;
 };
 
 // Whether a direct-to-LDS configuration can run the problem: no K tail, aligned
@@ -134,6 +141,7 @@ int64_t split_len(int64_t K, int splits, int bk) { return cdiv(cdiv(K, bk), spli
 // round trip through memory costs more than it saves otherwise (measured on
 // MI355X for the 128..512-row SwiGLU and 1..16-row e4m3 shapes).
 int pick_splits(const Cfg16& c, const Problem16& q) {
+    if (q.batch > 1) return 1;             // batches fill the GPU through gridDim.z
     const int64_t tiles = cdiv(q.M, c.BM) * cdiv(q.N, c.BN);
     int s = 1;
     if (tiles * 4 <= kNumCU && q.K >= 1024) {
@@ -158,7 +166,7 @@ constexpr Cand16 kCand16[] = {{10, 4.7}, {24, 5.0}, {13, 3.6}, {32, 3.6}, {6, 3.
 constexpr double kTileOverheadUs = 3.0;   // pipeline fill + epilogue per tile
 
 double est_us(const Cfg16& c, const Problem16& q, int splits, double tf_per_cu) {
-    const int64_t items = cdiv(q.M, c.BM) * cdiv(q.N, c.BN) * splits;
+    const int64_t items = cdiv(q.M, c.BM) * cdiv(q.N, c.BN) * splits * q.batch;
     const double waves = (double)cdiv(items, kNumCU);
     const double item_flops = 2.0 * c.BM * c.BN * (double)split_len(q.K, splits, c.BK);
     return waves * (item_flops / (tf_per_cu * 1e6) + kTileOverheadUs);
@@ -239,6 +247,7 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
     int cfg = 0, splits = 1;
     choose16(q, &cfg, &splits);
     if (cfg < 0) return hipErrorNotSupported;   // caller takes its generic path
+    if (p.batch > 1) splits = 1;                // no split-K inside a batch
     const Cfg16& c = kCfg16[cfg];
     p.tiles_m = (int)cdiv(q.M, c.BM);
     p.tiles_n = (int)cdiv(q.N, c.BN);
@@ -267,8 +276,12 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
 template <int DT>
 hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
                   const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
-                  int64_t ldc, hipStream_t st) {
+                  int64_t ldc, const Batch& bt, hipStream_t st) {
     Gemm16Params p{};
+    p.batch = (int)bt.n;
+    p.sA = bt.sA;
+    p.sB = bt.sB;
+    p.sC = bt.sC;
     p.A = reinterpret_cast<const uint16_t*>(A);
     p.B = reinterpret_cast<const uint16_t*>(B);
     p.lda = lda;
@@ -279,12 +292,13 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
     p.K = (int)K;
     p.alpha = alpha;
     p.beta = beta;
-    p.vec_a = aligned(A, 16) && (lda % 8 == 0);
-    p.vec_b = aligned(B, 16) && (ldb % 8 == 0);
-    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 2};
+    p.vec_a = aligned(A, 16) && (lda % 8 == 0) && (bt.sA % 16 == 0);
+    p.vec_b = aligned(B, 16) && (ldb % 8 == 0) && (bt.sB % 16 == 0);
+    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 2, bt.n};
     int splits = 1;
-    hipError_t e = run16<DT>(ta, tb, EPI_GEMM, q, p, C, aligned(C, 8) && (ldc % 4 == 0), "gemm16",
-                             st, &splits);
+    hipError_t e = run16<DT>(ta, tb, EPI_GEMM, q, p, C,
+                             aligned(C, 8) && (ldc % 4 == 0) && (bt.sC % 8 == 0), "gemm16", st,
+                             &splits);
     if (e != hipSuccess || splits <= 1) return e;
     float* ws = nullptr;
     e = workspace((size_t)splits * M * N * sizeof(float), &ws);
@@ -297,8 +311,12 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
 // e4m3 GEMM: A, B e4m3 codes, C bf16 (alpha carries the per-tensor scales).
 hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                  int64_t lda, const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
-                 hipStream_t st) {
+                 const Batch& bt, hipStream_t st) {
     Gemm16Params p{};
+    p.batch = (int)bt.n;
+    p.sA = bt.sA;
+    p.sB = bt.sB;
+    p.sC = bt.sC;
     p.A = reinterpret_cast<const uint16_t*>(A);
     p.B = reinterpret_cast<const uint16_t*>(B);
     p.lda = lda;
@@ -309,17 +327,21 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
     p.K = (int)K;
     p.alpha = alpha;
     p.beta = beta;
-    p.vec_a = aligned(A, 16) && (lda % 16 == 0);
-    p.vec_b = aligned(B, 16) && (ldb % 16 == 0);
-    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1};
+    p.vec_a = aligned(A, 16) && (lda % 16 == 0) && (bt.sA % 16 == 0);
+    p.vec_b = aligned(B, 16) && (ldb % 16 == 0) && (bt.sB % 16 == 0);
+    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1, bt.n};
     int splits = 1;
-    hipError_t e = run16<DT_E4M3>(ta, tb, EPI_GEMM, q, p, C, aligned(C, 8) && (ldc % 4 == 0),
-                                  "gemm8", st, &splits);
+    hipError_t e = run16<DT_E4M3>(ta, tb, EPI_GEMM, q, p, C,
+                                  aligned(C, 8) && (ldc % 4 == 0) && (bt.sC % 8 == 0), "gemm8",
+                                  st, &splits);
     if (e == hipErrorNotSupported) {
         std::snprintf(g_last_cfg, sizeof(g_last_cfg), "gemm8 generic splits=1");
-        hipLaunchKernelGGL(gemm_e4m3_generic, dim3(grid_1d(M * N)), dim3(256), 0, st,
-                           (const uint8_t*)A, (const uint8_t*)B, (uint16_t*)C, lda, ldb, ldc,
-                           (int)M, (int)N, (int)K, (int)ta, (int)tb, alpha, beta);
+        for (int64_t z = 0; z < bt.n; ++z) {   // rare path (K tails, odd alignment)
+            hipLaunchKernelGGL(gemm_e4m3_generic, dim3(grid_1d(M * N)), dim3(256), 0, st,
+                               (const uint8_t*)A + z * bt.sA, (const uint8_t*)B + z * bt.sB,
+                               (uint16_t*)((char*)C + z * bt.sC), lda, ldb, ldc, (int)M, (int)N,
+                               (int)K, (int)ta, (int)tb, alpha, beta);
+        }
         return hipGetLastError();
     }
     if (e != hipSuccess || splits <= 1) return e;
@@ -333,15 +355,20 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
 
 template <bool TA, bool TB>
 hipError_t launch_f32(const GemmF32Params& p, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>),
+                       dim3((unsigned)(p.tiles_m * p.tiles_n), 1, (unsigned)(p.batch > 1 ? p.batch : 1)),
                        dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
 hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
                     const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
-                    int64_t ldc, hipStream_t st) {
+                    int64_t ldc, const Batch& bt, hipStream_t st) {
     GemmF32Params p{};
+    p.batch = (int)bt.n;
+    p.sA = bt.sA;
+    p.sB = bt.sB;
+    p.sC = bt.sC;
     p.A = reinterpret_cast<const float*>(A);
     p.B = reinterpret_cast<const float*>(B);
     p.C = reinterpret_cast<float*>(C);
@@ -414,6 +441,51 @@ hipError_t run_w12(int cfg, Gemm16Params p, hipStream_t st) {
     return launch16_dt<DT>(false, false, EPI_SWIGLU_W12, cfg, p, 1, st);
 }
 
+// After validation: quick returns (scale only) and the per-dtype GEMM paths, for
+// one problem or a strided batch.
+int gemm_run(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+             int64_t lda, const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
+             int dtype, const Batch& bt, hipStream_t st) {
+    if (K == 0 || alpha == 0.0f) {
+        std::snprintf(g_last_cfg, sizeof(g_last_cfg), "scale_only");
+        const unsigned g = grid_1d(M * N);
+        for (int64_t z = 0; z < bt.n; ++z) {
+            void* Cz = reinterpret_cast<char*>(C) + z * bt.sC;
+            switch (dtype) {
+                case SG_F32:
+                    hipLaunchKernelGGL(scale_kernel<DT_F32>, dim3(g), dim3(256), 0, st, Cz, ldc,
+                                       (int)M, (int)N, beta);
+                    break;
+                case SG_F16:
+                    hipLaunchKernelGGL(scale_kernel<DT_F16>, dim3(g), dim3(256), 0, st, Cz, ldc,
+                                       (int)M, (int)N, beta);
+                    break;
+                default:  // bf16 output (SG_BF16 and SG_F8E4M3)
+                    hipLaunchKernelGGL(scale_kernel<DT_BF16>, dim3(g), dim3(256), 0, st, Cz,
+                                       ldc, (int)M, (int)N, beta);
+                    break;
+            }
+        }
+        return status_of(hipGetLastError());
+    }
+    hipError_t e;
+    switch (dtype) {
+        case SG_F32:
+            e = gemm_f32(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st);
+            break;
+        case SG_F16:
+            e = gemm16<DT_F16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st);
+            break;
+        case SG_BF16:
+            e = gemm16<DT_BF16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st);
+            break;
+        default:
+            e = gemm8(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st);
+            break;
+    }
+    return status_of(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -442,45 +514,52 @@ int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alp
     if (ldc < (N > 1 ? N : 1)) return -13;
     if (dtype < SG_F32 || dtype > SG_F8E4M3) return -14;
     if ((int64_t)M * N > ((int64_t)1 << 40)) return -3;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (M == 0 || N == 0) return 0;
+    return gemm_run(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, Batch{},
+                    reinterpret_cast<hipStream_t>(stream));
+}
 
-    if (!reads_ab) {
-        std::snprintf(g_last_cfg, sizeof(g_last_cfg), "scale_only");
-        const unsigned g = grid_1d(M * N);
-        switch (dtype) {
-            case SG_F32:
-                hipLaunchKernelGGL(scale_kernel<DT_F32>, dim3(g), dim3(256), 0, st, C, ldc,
-                                   (int)M, (int)N, beta);
-                break;
-            case SG_F16:
-                hipLaunchKernelGGL(scale_kernel<DT_F16>, dim3(g), dim3(256), 0, st, C, ldc,
-                                   (int)M, (int)N, beta);
-                break;
-            default:  // bf16 output (SG_BF16 and SG_F8E4M3)
-                hipLaunchKernelGGL(scale_kernel<DT_BF16>, dim3(g), dim3(256), 0, st, C, ldc,
-                                   (int)M, (int)N, beta);
-                break;
-        }
-        return status_of(hipGetLastError());
+int sg_gemm_strided_batched(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                            float alpha, const void* A, int64_t lda, int64_t strideA,
+                            const void* B, int64_t ldb, int64_t strideB, float beta, void* C,
+                            int64_t ldc, int64_t strideC, int64_t batch, int dtype,
+                            void* stream) {
+    if (!trans_ok(transA)) return -1;
+    if (!trans_ok(transB)) return -2;
+    if (M < 0 || M > kMaxDim) return -3;
+    if (N < 0 || N > kMaxDim) return -4;
+    if (K < 0 || K > kMaxDim) return -5;
+    const bool ta = is_t(transA), tb = is_t(transB);
+    const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f && batch > 0;
+    if (reads_ab && !A) return -7;
+    {
+        const int64_t need = ta ? M : K;
+        if (lda < (need > 1 ? need : 1)) return -8;
     }
-
-    hipError_t e;
-    switch (dtype) {
-        case SG_F32:
-            e = gemm_f32(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
-            break;
-        case SG_F16:
-            e = gemm16<DT_F16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
-            break;
-        case SG_BF16:
-            e = gemm16<DT_BF16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
-            break;
-        default:
-            e = gemm8(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, st);
-            break;
+    if (strideA < 0) return -9;
+    if (reads_ab && !B) return -10;
+    {
+        const int64_t need = tb ? K : N;
+        if (ldb < (need > 1 ? need : 1)) return -11;
     }
-    return status_of(e);
+    if (strideB < 0) return -12;
+    if (M > 0 && N > 0 && batch > 0 && !C) return -14;
+    if (ldc < (N > 1 ? N : 1)) return -15;
+    // outputs of different problems must not overlap (their writes would race)
+    if (batch > 1 && M > 0 && N > 0 && strideC < (M - 1) * ldc + N) return -16;
+    if (batch < 0 || batch > 65535) return -17;
+    if (dtype < SG_F32 || dtype > SG_F8E4M3) return -18;
+    if ((int64_t)M * N > ((int64_t)1 << 40)) return -3;
+    if (M == 0 || N == 0 || batch == 0) return 0;
+    const int64_t esz_ab = dtype == SG_F32 ? 4 : (dtype == SG_F8E4M3 ? 1 : 2);
+    const int64_t esz_c = dtype == SG_F32 ? 4 : 2;
+    Batch bt;
+    bt.n = batch;
+    bt.sA = strideA * esz_ab;
+    bt.sB = strideB * esz_ab;
+    bt.sC = strideC * esz_c;
+    return gemm_run(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, bt,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_t N, int64_t K,
@@ -681,8 +760,9 @@ const char* sg_status_string(int status) {
         "invalid argument 4", "invalid argument 5", "invalid argument 6", "invalid argument 7",
         "invalid argument 8", "invalid argument 9", "invalid argument 10",
         "invalid argument 11", "invalid argument 12", "invalid argument 13",
-        "invalid argument 14", "invalid argument 15"};
-    if (status <= 0 && status >= -15) return kArg[-status];
+        "invalid argument 14", "invalid argument 15", "invalid argument 16",
+        "invalid argument 17", "invalid argument 18"};
+    if (status <= 0 && status >= -18) return kArg[-status];
     if (status < 0) return "invalid argument";
     return hipGetErrorString(static_cast<hipError_t>(status));
 }

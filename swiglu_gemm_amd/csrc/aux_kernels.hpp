@@ -21,10 +21,19 @@ struct GemmF32Params {
     int M, N, K;
     float alpha, beta;
     int tiles_m, tiles_n;
+    int batch;           // strided batch over gridDim.z
+    int64_t sA, sB, sC;  // byte distance between consecutive problems
 };
 
 template <bool TA, bool TB>
-__global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmF32Params p) {
+__global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmF32Params p_) {
+    GemmF32Params p = p_;
+    {
+        const int64_t z = blockIdx.z;
+        p.A = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p_.A) + z * p_.sA);
+        p.B = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p_.B) + z * p_.sB);
+        p.C = reinterpret_cast<float*>(reinterpret_cast<char*>(p_.C) + z * p_.sC);
+    }
     constexpr int T = 64, BK = 16, PAD = 4;
     __shared__ float As[BK][T + PAD];
     __shared__ float Bs[BK][T + PAD];

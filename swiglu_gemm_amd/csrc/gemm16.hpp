@@ -161,7 +161,8 @@ struct LoadTrans {
 };
 
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_kernel(const Gemm16Params p) {
+__global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_kernel(const Gemm16Params p_) {
+    const Gemm16Params p = batch_item(p_);
     constexpr int NT = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;

@@ -202,7 +202,8 @@ __device__ __forceinline__ f32x16 mfma_op(const typename FragT<DT == DT_E4M3 ? 1
 
 // BK is in elements.  Output type: DT for 16-bit operands, bf16 for e4m3.
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16Params p) {
+__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16Params p_) {
+    const Gemm16Params p = batch_item(p_);
     constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
     constexpr int DT_OUT = DT == DT_E4M3 ? DT_BF16 : DT;
     constexpr int KSTEP = ESZ == 2 ? 16 : 64;

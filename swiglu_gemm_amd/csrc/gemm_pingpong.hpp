@@ -67,7 +67,8 @@ struct DmaStreamS {
 };
 
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
-__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const Gemm16Params p) {
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const Gemm16Params p_) {
+    const Gemm16Params p = batch_item(p_);
     static_assert(WM * WN == 8, "ping-pong runs 8 waves (two per SIMD)");
     constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
     constexpr int DT_OUT = DT == DT_E4M3 ? DT_BF16 : DT;

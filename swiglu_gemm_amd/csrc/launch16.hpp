@@ -15,7 +15,8 @@ namespace sg {
 template <typename Kern>
 inline hipError_t launch_grid(Kern k, const Gemm16Params& p, int splits, int threads,
                               hipStream_t st) {
-    dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)splits);
+    dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)splits,
+              (unsigned)(p.batch > 1 ? p.batch : 1));
     hipLaunchKernelGGL(k, grid, dim3(threads), 0, st, p);
     return hipGetLastError();
 }

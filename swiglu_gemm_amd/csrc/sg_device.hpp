@@ -58,7 +58,19 @@ struct Gemm16Params {
     int tiles_m, tiles_n, group_m;
     int k_per_split;    // a multiple of 64; gridDim.y splits
     int epi_flags;      // EPI_SWIGLU: EPI_Y16 (Y rows allow 16-byte stores)
+    int batch;          // strided batch: gridDim.z problems (0 or 1: one problem)
+    int64_t sA, sB, sC; // byte distance between consecutive problems' A, B, C
 };
+
+// The problem of work-group blockIdx.z in a strided batch (the identity for z = 0).
+__device__ __forceinline__ Gemm16Params batch_item(const Gemm16Params& q) {
+    Gemm16Params p = q;
+    const int64_t z = blockIdx.z;
+    p.A = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(q.A) + z * q.sA);
+    p.B = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(q.B) + z * q.sB);
+    p.C = reinterpret_cast<char*>(q.C) + z * q.sC;
+    return p;
+}
 
 enum { EPI_Y16 = 1 };
 

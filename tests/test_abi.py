@@ -94,6 +94,32 @@ def test_swiglu_w12_argument_validation(L):
     assert sw(N=0) == 0
 
 
+def test_gemm_strided_batched_validation(L):
+    def gb(ta=b"N", tb=b"N", M=2, N=2, K=2, A=P, lda=2, sA=4, B=P, ldb=2, sB=4, C=P, ldc=2,
+           sC=4, batch=2, dt=2, alpha=1.0, beta=0.0):
+        return L.sg_gemm_strided_batched(ta, tb, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta,
+                                         C, ldc, sC, batch, dt, NUL)
+    assert gb(ta=b"X") == -1
+    assert gb(tb=b"X") == -2
+    assert gb(M=-1) == -3
+    assert gb(N=-1) == -4
+    assert gb(K=-1) == -5
+    assert gb(A=NUL) == -7
+    assert gb(lda=1) == -8
+    assert gb(sA=-1) == -9
+    assert gb(B=NUL) == -10
+    assert gb(ldb=1) == -11
+    assert gb(sB=-1) == -12
+    assert gb(C=NUL) == -14
+    assert gb(ldc=1) == -15
+    assert gb(sC=3) == -16                           # outputs of the problems would overlap
+    assert gb(batch=-1) == -17
+    assert gb(dt=9) == -18
+    assert gb(batch=0) == 0
+    assert gb(M=0) == 0
+    assert sg.status_string(-18) == "invalid argument 18"
+
+
 def test_other_entry_points_validation(L):
     assert L.sg_interleave_gate_up(NUL, P, P, 1, 1, 2, NUL) == -1
     assert L.sg_interleave_gate_up(P, P, P, -1, 1, 2, NUL) == -4
