@@ -475,6 +475,153 @@ def stage_sweep_summarize(trace_csv, sweep_jsonl):
     print("\n".join(lines))
 
 
+DECODE_FILE = os.path.join(ROOT, "profiles", "decode_gemv_cold.md")
+# decode-shaped problems: (label, kind, dtype, M, N, K, weight layout)
+DECODE_CASES = [("bf16 GEMM 1x4096x4096 NT", "gemm", "bf16", 1, 4096, 4096, "T"),
+                ("bf16 GEMM 16x4096x4096 NT", "gemm", "bf16", 16, 4096, 4096, "T"),
+                ("bf16 GEMM 8x14336x4096 NT", "gemm", "bf16", 8, 14336, 4096, "T"),
+                ("bf16 GEMM 16x8192x8192 NN", "gemm", "bf16", 16, 8192, 8192, "N"),
+                ("bf16 GEMM 32x14336x4096 NN", "gemm", "bf16", 32, 14336, 4096, "N"),
+                ("bf16 SwiGLU 16x896x2*4864", "swiglu", "bf16", 16, 4864, 896, "N"),
+                ("e4m3 SwiGLU 1x4096x2*11008", "swiglu", "e4m3", 1, 11008, 4096, "N"),
+                ("e4m3 SwiGLU 16x4096x2*11008", "swiglu", "e4m3", 16, 11008, 4096, "N")]
+DECODE_PATHS = [("default", {}), ("large-tile", {"SG_FORCE_CONFIG": "-1"}),
+                ("decode", {"SG_FORCE_DECODE": "5"})]
+
+
+def decode_study(steps):
+    """Decode-shaped problems (1..32 rows) with the weights cold in HBM: the
+    library's default choice, the large-tile path and the stream-K decode path
+    forced in turn, and torch.mm (hipBLASLt) for the GEMMs.  Each (case, path) is
+    fenced in the kernel trace by torch's sleep kernel; one JSON line each with the
+    wall time per call (HIP events; includes launch gaps).  Run under rocprofv3
+    --kernel-trace and pass the trace to --decode-summarize for kernel times."""
+    import torch
+    import swiglu_gemm_amd as sg
+    from swiglu_gemm_amd import inputs
+    sg.lib()
+    dev = "cuda:0"
+
+    def timed(fn):
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        torch.cuda._sleep(2000000)          # marks the end of this case in the trace
+        torch.cuda.synchronize()
+        return us
+
+    for label, kind, dt, M, N, K, tb in DECODE_CASES:
+        esz = 1 if dt == "e4m3" else 2
+        wbytes = K * N * esz * (2 if kind == "swiglu" else 1)
+        ncold = max(4, -(-COLD_BYTES // wbytes))
+        if kind == "swiglu":
+            pb = inputs.swiglu_problem(4 if dt == "bf16" else 5, M, N, K, dt)
+            A = to_dev(pb["A"], dt, torch)
+            W0 = sg.interleave_gate_up(to_dev(pb["W1"], dt, torch), to_dev(pb["W2"], dt, torch))
+            Ws = [W0] + [W0.clone() for _ in range(ncold - 1)]
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            sa, sw = pb["scale_a"], pb["scale_w"]
+
+            def fn(i):
+                sg.swiglu_gemm(A, Ws[i % ncold], Y, sa, sw)
+            out_bytes = M * N * 2
+        else:
+            A = torch.randn((M, K), device=dev).to(torch.bfloat16)
+            W0 = (torch.randn((N, K) if tb == "T" else (K, N), device=dev) * 0.02).to(torch.bfloat16)
+            Ws = [W0] + [W0.clone() for _ in range(ncold - 1)]
+            C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+            def fn(i):
+                sg.gemm(A, Ws[i % ncold], C, transB=tb)
+            out_bytes = M * N * 2
+        nbytes = wbytes + M * K * esz + out_bytes
+        for path, env in DECODE_PATHS:
+            os.environ.update(env)
+            try:
+                us = timed(fn)
+                desc = sg.last_config()
+            finally:
+                for k in env:
+                    os.environ.pop(k, None)
+            print(json.dumps({"decode_case": label, "path": path, "wall_us": round(us, 2),
+                              "bytes": nbytes, "kernel_config": desc}), flush=True)
+        if kind == "gemm":
+            def lib_fn(i):
+                W = Ws[i % ncold]
+                torch.mm(A, W.t() if tb == "T" else W)
+            us = timed(lib_fn)
+            print(json.dumps({"decode_case": label, "path": "torch.mm (hipBLASLt)",
+                              "wall_us": round(us, 2), "bytes": nbytes, "kernel_config": "-"}),
+                  flush=True)
+        del Ws, W0
+
+
+def decode_summarize(trace_csv, jsonl):
+    """Kernel durations per (case, path) of a --decode run: the trace is cut at
+    torch's sleep kernels; the first 5 launches of each segment are warm-up.
+    Writes DECODE_FILE."""
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    segs, cur = [], []
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "sleep" in name.lower() or "spin" in name.lower():
+            if cur:
+                segs.append(cur)
+            cur = []
+            continue
+        cur.append(r)
+    # kernels of the problem itself: the library's, or hipBLASLt's for torch.mm
+    # (the one-time W_fused interleave before a SwiGLU case's first path is set-up)
+    def ours(name):
+        return ("sg::" in name and "interleave" not in name) or "Cijk" in name or \
+            "gemv" in name.lower()
+    segs = [[r for r in sg_ if ours(r["Kernel_Name"])] for sg_ in segs]
+    segs = [sg_ for sg_ in segs if sg_]
+    cases = [json.loads(l) for l in open(jsonl) if l.startswith('{"decode_case"')]
+    assert len(segs) == len(cases), (len(segs), len(cases))
+    lines = ["# Decode-shaped GEMM / SwiGLU (1..32 rows), weights cold in HBM, one MI355X", "",
+             "Commands (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "```", "rocprofv3 --kernel-trace --output-format csv -d <out> -o dec -- "
+             "python <repo>/bench.py --decode > decode.jsonl",
+             "python bench.py --decode-summarize <out>/dec_kernel_trace.csv decode.jsonl", "```", "",
+             "Weights rotate through > 512 MB of device copies so each call reads them from HBM. "
+             "Kernel time = mean duration per call of every kernel the call launches (the "
+             "stream-K kernel plus its fix-up kernel, or the large-tile kernel plus its split-K "
+             "reduction); GB/s = weight + token + output bytes / kernel time. Wall = HIP events "
+             "around back-to-back calls from Python without a clock spin-up: at these sizes it "
+             "is bound by the host-side cost of a call (about 30 us here), not by the GPU, so "
+             "such calls belong in a captured graph or a native caller.", "",
+             "| problem | path | kernels (mean us each) | kernel us | GB/s | wall us | configuration |",
+             "|---|---|---|---|---|---|---|"]
+    for c, seg in zip(cases, segs):
+        by = {}
+        for r in seg:
+            by.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        parts, tot = [], 0.0
+        for k, v in by.items():
+            v = v[5:] if len(v) > 5 else v
+            mean = sum(v) / len(v)
+            tot += mean
+            short = k.split("(")[0].replace("void ", "")
+            if short.startswith("Cijk"):
+                short = "hipBLASLt " + short.split("_MT")[1].split("_")[0] if "_MT" in short else short[:30]
+            parts.append("%s %.1f" % (short.replace("sg::", ""), mean))
+        lines.append("| %s | %s | %s | %.1f | %.0f | %.1f | %s |" % (
+            c["decode_case"], c["path"], "; ".join(parts), tot, c["bytes"] / (tot * 1e-6) / 1e9,
+            c["wall_us"], c["kernel_config"]))
+    with open(DECODE_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def mfma_ceiling():
     """Sustained rate of a pure MFMA loop (no memory traffic) on zero, constant and
     random operand data, per dtype.  The matrix cores' power grows with the
@@ -538,6 +685,9 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true")
     ap.add_argument("--stage-sweep", action="store_true")
     ap.add_argument("--stage-sweep-summarize", nargs=2, metavar=("TRACE_CSV", "SWEEP_JSONL"))
+    ap.add_argument("--decode", action="store_true",
+                    help="decode-shaped problems: default vs large-tile vs decode path")
+    ap.add_argument("--decode-summarize", nargs=2, metavar=("TRACE_CSV", "DECODE_JSONL"))
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only (the library is single-GPU); --gpus %d is not "
@@ -548,6 +698,12 @@ def main():
         return
     if args.stage_sweep_summarize:
         stage_sweep_summarize(*args.stage_sweep_summarize)
+        return
+    if args.decode_summarize:
+        decode_summarize(*args.decode_summarize)
+        return
+    if args.decode:
+        decode_study(40)
         return
     if args.pmc_probe:
         pmc_probe()

@@ -22,6 +22,11 @@
  *   device, grown on first need, released by sg_release().  Calls that need it and
  *   run concurrently on different streams of one device are serialised by the
  *   caller (the library does not order streams).
+ * - Problems with 1..32 rows of A ('N') may run on the decode kernels: a persistent
+ *   stream-K pass over the weight and, when a column tile is shared by several
+ *   work-groups, a second fix-up launch that adds their partial sums (a fixed
+ *   order: results are run-to-run identical).  Its partial sums live in the same
+ *   kind of library-owned workspace, with the same rule for concurrent streams.
  */
 #ifndef SWIGLU_GEMM_H
 #define SWIGLU_GEMM_H

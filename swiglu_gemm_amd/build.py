@@ -18,7 +18,8 @@ LIB = os.path.join(HERE, "libswiglu_gemm.so")
 DIAG_SRC = os.path.join(HERE, "diag", "mfma_loop.hip")
 DIAG_LIB = os.path.join(HERE, "libswiglu_gemm_diag.so")
 SOURCES = ["api.hip"] + ["inst_%s_%s.hip" % (d, t) for d in ("f16", "bf16", "e4m3")
-                        for t in ("nn", "nt", "tn", "tt")]
+                        for t in ("nn", "nt", "tn", "tt")] + \
+    ["inst_decode_%s.hip" % d for d in ("f16", "bf16", "e4m3")]
 ARCH = "gfx950"
 
 

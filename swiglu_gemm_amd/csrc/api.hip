@@ -14,6 +14,7 @@
 
 #include "aux_kernels.hpp"
 #include "configs16.hpp"
+#include "decode.hpp"
 #include "sg_device.hpp"
 #include "swiglu_gemm.h"
 
@@ -23,6 +24,11 @@ namespace sg {
 // defined in inst_<dtype>_<transposes>.hip
 template <int DT, bool TA, bool TB>
 hipError_t launch16_tr(int epi, int cfg, const Gemm16Params& p, int splits, hipStream_t st);
+
+// defined in inst_decode_<dtype>.hip
+template <int DT>
+hipError_t launch_decode_dt(bool tb, int epi, int cfg, const DecodeParams& p, bool split,
+                            hipStream_t st);
 
 template <int DT>
 hipError_t launch16_dt(bool ta, bool tb, int epi, int cfg, const Gemm16Params& p, int splits,
@@ -54,8 +60,9 @@ struct Workspace {
 };
 std::mutex g_ws_mu;
 // slot 0: split-K partials; slot 1: W_fused built from separate W1, W2 (the
-// split-weight SwiGLU's fallback for shapes its own kernel cannot take)
-constexpr int kSlots = 2;
+// split-weight SwiGLU's fallback for shapes its own kernel cannot take); slot 2:
+// partial sums of the decode path's split column tiles
+constexpr int kSlots = 3;
 Workspace g_ws[kSlots][64];
 
 hipError_t workspace(size_t bytes, float** out, int slot = 0) {
@@ -273,6 +280,102 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
     return launch16_dt<DT>(ta, tb, EPI_PARTIAL, cfg, p, splits, st);
 }
 
+// ------------------------------------------------ decode path (M <= 32 rows)
+// Streaming kernel + fix-up kernel of decode.hpp; partial sums of split column
+// tiles live in workspace slot 2.
+constexpr int kDecodeMaxM = 32;
+
+// SG_FORCE_DECODE=<id>: run decode-shaped problems with that configuration.
+int forced_decode() {
+    const char* s = std::getenv("SG_FORCE_DECODE");
+    if (!s || !*s) return -1;
+    const int c = std::atoi(s);
+    return c >= 0 && c < kNumDecodeCfg ? c : -1;
+}
+
+// Decode configuration: 128-column tiles with a 4-deep ring, one work-group per
+// CU (measured best or within 3 % on MI355X for 1..32 rows, weights cold in HBM);
+// the split-weight form needs two fragments per wave: 256 columns.
+int choose_decode(int epi) { return epi == EPI_SWIGLU_W12 ? 1 : 5; }
+
+// The decode path for M <= 32 rows: 'N' tokens A (M x K), weight 'N' (K x N) or
+// 'T' (N x K; GEMM only).  N is the fused width for both SwiGLU forms.  Returns
+// hipErrorNotSupported when the problem is not decode-shaped or eligible (the
+// large-tile paths take it), or when SG_FORCE_CONFIG is set (a large-tile config,
+// or a negative id: the large-tile paths with their own choice).
+template <int DT>
+hipError_t try_decode(bool tb, int epi, const void* A, int64_t lda, const void* B,
+                      const void* B2, int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N,
+                      int64_t K, float alpha, float beta, hipStream_t st) {
+    constexpr int esz = DT == DT_E4M3 ? 1 : 2;
+    int fc = -1, fs = 0;
+    if (forced_config(&fc, &fs)) return hipErrorNotSupported;
+    if (M < 1 || M > kDecodeMaxM || K <= 0 || K % (128 / esz) != 0) return hipErrorNotSupported;
+    if (!A || !B || !C || (epi == EPI_SWIGLU_W12 && !B2)) return hipErrorInvalidValue;
+    const int64_t nsrc = epi == EPI_SWIGLU_W12 ? N / 2 : N;   // columns of each weight source
+    if (!aligned(A, 16) || (lda * esz) % 16 != 0) return hipErrorNotSupported;
+    if (!aligned(B, 16) || (ldb * esz) % 16 != 0) return hipErrorNotSupported;
+    if (B2 && !aligned(B2, 16)) return hipErrorNotSupported;
+    if (!tb && (nsrc * esz) % 16 != 0) return hipErrorNotSupported;
+    int cfg = forced_decode();
+    if (cfg < 0) {
+        // The decode kernel replaces the large-tile path where that path splits K:
+        // both then need a second (reduction / fix-up) launch, and the stream-K
+        // kernel streams the weight faster (measured on MI355X, weights cold: 14.2
+        // vs 16.7 us for 1 x 4096 x 4096 bf16, 33.1 vs 41.2 us for 16 x 8192 x
+        // 8192).  Where the large-tile path runs as one kernel it is the faster one
+        // (e4m3 SwiGLU 1 x 4096 x 2*11008: 19.3 vs 23.6 us).
+        int oc = -1, os = 1;
+        choose16(Problem16{M, N, K, true, true, false, tb, esz}, &oc, &os);
+        if (oc >= 0 && os <= 1) return hipErrorNotSupported;
+        cfg = choose_decode(epi);
+    }
+    const DecodeCfg& c = kDecodeCfg[cfg];
+    if (epi == EPI_SWIGLU_W12 && (c.BN / c.NW / 32) % 2 != 0) return hipErrorNotSupported;
+    const int64_t tiles = cdiv(N, c.BN), nkb = K / (128 / esz);
+    if (tiles * nkb >= ((int64_t)1 << 31) - 1) return hipErrorNotSupported;
+    const int units = (int)(tiles * nkb);
+    int grid = units < kNumCU * c.occ ? units : kNumCU * c.occ;
+    if (const char* g = std::getenv("SG_DECODE_GRID")) {   // tuning override: grid cap
+        const int cap = std::atoi(g);
+        if (cap > 0 && cap < grid) grid = cap;
+    }
+    // a column tile is split when its first and last unit lie in different runs
+    bool split = false;
+    for (int64_t t = 0; t < tiles && !split; ++t) {
+        const int64_t u0 = t * nkb, u1 = (t + 1) * nkb - 1;
+        split = ((u0 + 1) * grid - 1) / units != ((u1 + 1) * grid - 1) / units;
+    }
+    float* part = nullptr;
+    if (split) {
+        const hipError_t e = workspace((size_t)grid * 2 * c.BN * 32 * sizeof(float), &part, 2);
+        if (e != hipSuccess) return e;
+    }
+    DecodeParams p{};
+    p.A = reinterpret_cast<const char*>(A);
+    p.B = reinterpret_cast<const char*>(B);
+    p.B2 = reinterpret_cast<const char*>(B2);
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.alpha = alpha;
+    p.beta = beta;
+    if (epi == EPI_SWIGLU) p.vec_c = aligned(C, 4) && ldc % 2 == 0;
+    else p.vec_c = aligned(C, 8) && ldc % 4 == 0;
+    p.tiles = (int)tiles;
+    p.nkb = (int)nkb;
+    p.units = units;
+    p.part = part;
+    p.grid = grid;
+    std::snprintf(g_last_cfg, sizeof(g_last_cfg), "decode cfg=%d %s grid=%d units=%d%s", cfg,
+                  c.name, grid, units, split ? " fixup" : "");
+    return launch_decode_dt<DT>(tb, epi, cfg, p, split, st);
+}
+
 template <int DT>
 hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
                   const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
@@ -292,6 +395,11 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
     p.K = (int)K;
     p.alpha = alpha;
     p.beta = beta;
+    if (bt.n == 1 && !ta) {
+        const hipError_t d = try_decode<DT>(tb, EPI_GEMM, A, lda, B, nullptr, ldb, C, ldc, M, N,
+                                            K, alpha, beta, st);
+        if (d != hipErrorNotSupported) return d;
+    }
     p.vec_a = aligned(A, 16) && (lda % 8 == 0) && (bt.sA % 16 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 8 == 0) && (bt.sB % 16 == 0);
     Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 2, bt.n};
@@ -327,6 +435,11 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
     p.K = (int)K;
     p.alpha = alpha;
     p.beta = beta;
+    if (bt.n == 1 && !ta) {
+        const hipError_t d = try_decode<DT_E4M3>(tb, EPI_GEMM, A, lda, B, nullptr, ldb, C, ldc, M,
+                                                 N, K, alpha, beta, st);
+        if (d != hipErrorNotSupported) return d;
+    }
     p.vec_a = aligned(A, 16) && (lda % 16 == 0) && (bt.sA % 16 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 16 == 0) && (bt.sB % 16 == 0);
     Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1, bt.n};
@@ -608,6 +721,19 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
     // Y stores are 4 or 8 bytes wide depending on the kernel: require the stricter
     const bool yvec = aligned(Y, 8) && (N % 4 == 0);
     p.epi_flags = aligned(Y, 16) && N % 8 == 0 ? EPI_Y16 : 0;
+    {
+        hipError_t d;
+        if (dtype == SG_F8E4M3)
+            d = try_decode<DT_E4M3>(false, EPI_SWIGLU, A, K, Wfused, nullptr, N2, Y, N, M, N2, K,
+                                    p.alpha, 0.0f, st);
+        else if (dtype == SG_F16)
+            d = try_decode<DT_F16>(false, EPI_SWIGLU, A, K, Wfused, nullptr, N2, Y, N, M, N2, K,
+                                   p.alpha, 0.0f, st);
+        else
+            d = try_decode<DT_BF16>(false, EPI_SWIGLU, A, K, Wfused, nullptr, N2, Y, N, M, N2, K,
+                                    p.alpha, 0.0f, st);
+        if (d != hipErrorNotSupported) return status_of(d);
+    }
     int splits = 1;
     hipError_t e;
     if (dtype == SG_F8E4M3) {
@@ -656,6 +782,20 @@ int sg_swiglu_gemm_w12(const void* A, const void* W1, const void* W2, void* Y, i
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (M == 0 || N == 0) return 0;
     const int esz = dtype == SG_F8E4M3 ? 1 : 2;
+    if (K > 0) {
+        const float s = scale_a * scale_w;
+        hipError_t d;
+        if (dtype == SG_F8E4M3)
+            d = try_decode<DT_E4M3>(false, EPI_SWIGLU_W12, A, K, W1, W2, N, Y, N, M, 2 * N, K, s,
+                                    0.0f, st);
+        else if (dtype == SG_F16)
+            d = try_decode<DT_F16>(false, EPI_SWIGLU_W12, A, K, W1, W2, N, Y, N, M, 2 * N, K, s,
+                                   0.0f, st);
+        else
+            d = try_decode<DT_BF16>(false, EPI_SWIGLU_W12, A, K, W1, W2, N, Y, N, M, 2 * N, K, s,
+                                    0.0f, st);
+        if (d != hipErrorNotSupported) return status_of(d);
+    }
     if (K > 0) {
         Problem16 q{M, N, K, aligned(A, 16) && (K * esz) % 16 == 0,
                     aligned(W1, 16) && aligned(W2, 16) && (N * esz) % 16 == 0, false, false, esz};

@@ -1,0 +1,5 @@
+// f16 instantiations of the decode-shaped (M <= 32) GEMM launchers.
+#include "decode.hpp"
+namespace sg {
+template hipError_t launch_decode_dt<DT_F16>(bool, int, int, const DecodeParams&, bool, hipStream_t);
+}
