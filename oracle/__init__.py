@@ -17,6 +17,16 @@ What is computed, with sources (page title, section):
   dequantisation of §12.4 of the first page.
 * ``interleave`` / ``deinterleave``: the W_fused layout of Kernel-2, bit-exact.
 * ``decode``: exact decoders of fp16, bf16 and OCP e4m3fn storage.
+* ``activation`` / ``gemm_epilogue``: the GEMM followed by the steps a fused
+  epilogue folds in before the accumulator is stored -- per-column bias, then an
+  activation (ReLU, GELU, SiLU) -- ("GEMM o Coração Matemático" §1, last
+  paragraph, and §13.3, last paragraph; "为什么 GEMM 是 CUDA 的必修课", the
+  optimisation list, item on epilogue fusion: bias, activation, scale, quantise).
+  GELU is x*Phi(x) with the normal CDF written through erf; the tanh form is the
+  common approximation of it.
+* ``quantize_e4m3``: a value to the OCP e4m3fn code of value/scale (per-tensor
+  scale with zero point 0, §12.4), nearest code, ties to the even code,
+  saturating at +-448; found by search over the decoded code table.
 
 Inputs are raw storage arrays (numpy ``uint16`` for fp16/bf16, ``uint8`` for
 e4m3, ``float32`` for fp32); outputs are float64.
@@ -24,6 +34,7 @@ e4m3, ``float32`` for fp32); outputs are float64.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 import threading
@@ -223,3 +234,70 @@ def deinterleave(Wf: np.ndarray):
         lib.oracle_deinterleave(Wf.ctypes.data, W1.ctypes.data, W2.ctypes.data, K, N,
                                 Wf.dtype.itemsize)
     return W1, W2
+
+
+ACTIVATIONS = ("none", "relu", "gelu", "gelu_tanh", "silu")
+
+
+def activation(x, act: str) -> np.ndarray:
+    """Elementwise activation in fp64 (see the module docstring for the sources).
+
+    relu(x) = max(x, 0); gelu(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2));
+    gelu_tanh(x) = x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)));
+    silu(x) = x / (1 + e^-x)."""
+    x = np.asarray(x, dtype=np.float64)
+    if act == "none":
+        return x.copy()
+    if act == "relu":
+        return np.where(x > 0, x, 0.0)
+    if act == "gelu":
+        # Phi(x) = (1 + erf(x/sqrt 2))/2 = erfc(-x/sqrt 2)/2; the erfc form keeps full
+        # relative accuracy in the negative tail, where 1 + erf cancels
+        erfc = np.frompyfunc(math.erfc, 1, 1)
+        return 0.5 * x * erfc(-x / math.sqrt(2.0)).astype(np.float64)
+    if act == "gelu_tanh":
+        c = math.sqrt(2.0 / math.pi)
+        return 0.5 * x * (1.0 + np.tanh(c * (x + 0.044715 * x ** 3)))
+    if act == "silu":
+        with np.errstate(over="ignore"):
+            return x / (1.0 + np.exp(-x))
+    raise ValueError("unknown activation %r" % act)
+
+
+def gemm_epilogue(transA, transB, M, N, K, alpha, A_bits, lda, B_bits, ldb, beta, C_bits, ldc,
+                  dtype, c_dtype=None, bias_bits=None, bias_dtype=None, act="none",
+                  nthreads=None):
+    """fp64 value of act(alpha*op(A)*op(B) + beta*C_old + bias[n]) for every (m, n),
+    shape (M, N): the GEMM of ``gemm`` followed by the per-column bias and the
+    activation, before any output rounding or quantisation."""
+    V = gemm(transA, transB, M, N, K, alpha, A_bits, lda, B_bits, ldb, beta, C_bits, ldc,
+             dtype, c_dtype=c_dtype, nthreads=nthreads)
+    V = np.ascontiguousarray(V.reshape(-1)[: M * ldc].reshape(M, ldc)[:, :N]) if M else \
+        np.zeros((0, N))
+    if bias_bits is not None:
+        V = V + decode(np.ascontiguousarray(bias_bits).ravel()[:N], bias_dtype)[None, :]
+    return activation(V, act)
+
+
+def _e4m3_table():
+    """Decoded values of the non-negative finite e4m3fn codes 0x00..0x7E (0x7F is NaN)."""
+    return decode(np.arange(0x7F, dtype=np.uint8), "e4m3")
+
+
+def quantize_e4m3(values, scale: float) -> np.ndarray:
+    """OCP e4m3fn codes of values/scale (division in fp64): the nearest finite code,
+    ties to the code with an even mantissa (even code number), magnitudes past 448
+    saturate to 448, NaN gives 0x7F; the sign goes to bit 7 (also for zero)."""
+    v = np.asarray(values, dtype=np.float64) / float(scale)
+    table = _e4m3_table()                       # increasing, 127 entries
+    a = np.abs(v)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, len(table) - 1)
+    lo = np.clip(hi - 1, 0, len(table) - 1)
+    d_hi = np.abs(table[hi] - a)
+    d_lo = np.abs(a - table[lo])
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi).astype(np.uint8)
+    code = np.where(a >= table[-1], np.uint8(0x7E), code)
+    code = code | np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
+    code = np.where(np.isnan(v), np.uint8(0x7F), code)
+    return code.astype(np.uint8)
