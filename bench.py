@@ -260,6 +260,51 @@ def bench_gemm_ragged(torch, sg, inputs, steps, warmup):
     return out
 
 
+def bench_epilogue(torch, sg, steps, warmup):
+    """Fused GEMM epilogue (sg_gemm_ex) on a 2048 x 896 x 4864 bf16 projection (the
+    MLP shape of the SwiGLU rows, here as a plain Linear): the GEMM alone, with bias
+    + GELU fused (bf16 out), with bias + GELU + e4m3 output quantisation fused, and
+    the unfused sequences: this library's GEMM followed by torch's bias add, GELU
+    (and float8 cast) as separate kernels."""
+    M, N, K = 2048, 4864, 896
+    A = torch.randn((M, K), device="cuda:0").to(torch.bfloat16)
+    W = (torch.randn((K, N), device="cuda:0") * 0.03).to(torch.bfloat16)
+    bias = torch.randn((N,), device="cuda:0").to(torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    C8 = torch.empty((M, N), dtype=torch.uint8, device="cuda:0")
+    s8 = 0.05
+    F = torch.nn.functional
+
+    def plain(i):
+        sg.gemm(A, W, C)
+
+    def fused(i):
+        sg.gemm_ex(A, W, C, bias=bias, activation="gelu")
+
+    def fused8(i):
+        sg.gemm_ex(A, W, C8, bias=bias, activation="gelu", out_scale=s8)
+
+    def unfused(i):
+        sg.gemm(A, W, C)
+        F.gelu(C + bias)
+
+    def unfused8(i):
+        sg.gemm(A, W, C)
+        (F.gelu(C + bias) / s8).to(torch.float8_e4m3fn)
+
+    out = {"shape": "bf16 M=%d K=%d N=%d, bias + GELU" % (M, K, N)}
+    for name, fn in (("gemm_ms", plain), ("fused_bias_gelu_ms", fused),
+                     ("fused_bias_gelu_e4m3_out_ms", fused8), ("unfused_bias_gelu_ms", unfused),
+                     ("unfused_bias_gelu_e4m3_out_ms", unfused8)):
+        out[name] = round(time_steps(fn, steps, warmup, torch), 5)
+        if name.startswith("fused"):
+            out[name.replace("_ms", "_config")] = sg.last_config()
+    out["fused_vs_unfused"] = round(out["unfused_bias_gelu_ms"] / out["fused_bias_gelu_ms"], 3)
+    out["fused_vs_unfused_e4m3_out"] = round(out["unfused_bias_gelu_e4m3_out_ms"] /
+                                             out["fused_bias_gelu_e4m3_out_ms"], 3)
+    return out
+
+
 def env_info(torch):
     props = torch.cuda.get_device_properties(0)
     info = {"device": props.name, "compute_units": props.multi_processor_count,
@@ -759,6 +804,9 @@ def main():
                                                      args.warmup)
         torch.cuda.empty_cache()
         out["gemm_ragged_bf16"] = bench_gemm_ragged(torch, sg, inputs, 20, 3)
+        torch.cuda.empty_cache()
+        print("bench: fused GEMM epilogue", file=sys.stderr, flush=True)
+        out["gemm_epilogue"] = bench_epilogue(torch, sg, max(10, args.steps // 2), args.warmup)
         torch.cuda.empty_cache()
     sizes = [("bf16", 2048, 4864, 896)]
     if not args.quick:

@@ -74,6 +74,56 @@ int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K,
             float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
             float beta, void* C, int64_t ldc, int dtype, void* stream);
 
+/* Activations of the GEMM epilogue (sg_epilogue.activation). */
+typedef enum {
+    SG_ACT_NONE = 0,
+    SG_ACT_RELU = 1,      /* max(x, 0) */
+    SG_ACT_GELU = 2,      /* x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)) */
+    SG_ACT_GELU_TANH = 3, /* x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3))) */
+    SG_ACT_SILU = 4       /* x / (1 + e^-x) */
+} sg_activation;
+
+/* Extra steps of the GEMM epilogue, applied before the single store. */
+typedef struct {
+    const void* bias;   /* NULL, or N values (device memory), one per column of C */
+    int bias_dtype;     /* SG_F32, SG_F16 or SG_BF16 (ignored when bias is NULL) */
+    int activation;     /* sg_activation, applied after the bias */
+    int out_dtype;      /* -1: C has sg_gemm's output type; SG_F8E4M3: C holds e4m3 codes */
+    float out_scale;    /* SG_F8E4M3 output: per-tensor scale s_C > 0 (finite; its fp32
+                           reciprocal must be finite too) */
+} sg_epilogue;
+
+/*
+ * sg_gemm_ex: sg_gemm with the steps a fused GEMM epilogue folds in before the
+ * accumulator is stored ("GEMM o Coração Matemático" §1, closing paragraph, and
+ * §13.3, closing paragraph: bias and activations in the epilogue; "为什么 GEMM 是
+ * CUDA 的必修课", list of optimisations, epilogue fusion of bias, activation,
+ * scale and quantisation):
+ *     v = alpha * op(A) * op(B) + beta * C_old
+ *     y = act(v + bias[n])
+ *     C[m, n] = y rounded once to the output type, or, with out_dtype SG_F8E4M3,
+ *               the OCP e4m3fn code of y * r, r = 1/out_scale rounded to fp32
+ *               (round to nearest, ties to even, saturating at +-448, NaN to 0x7F;
+ *               the per-tensor scale of §12.4; exact division for power-of-two
+ *               scales).
+ * Attention scores QK^T / sqrt(d_h) are the plain call with transB = 'T' and
+ * alpha = 1/sqrt(d_h) (§1); the fused Q, K, V projection is one call on the
+ * concatenated weight [W_Q W_K W_V] (N = 3d, §13.1).
+ *
+ * Arguments 1-14 and 16 as sg_gemm (15 there is the stream):
+ *  15 epi    NULL or the steps above; NULL, or no bias, SG_ACT_NONE and
+ *            out_dtype -1, is exactly sg_gemm.
+ *  16 stream hipStream_t (void*).
+ * With an e4m3 output C is M x N bytes (ldc in elements = bytes) and beta must
+ * be 0.  Quick returns as sg_gemm: K == 0 or alpha == 0 gives
+ * C = out(act(beta * C_old + bias)).
+ * Invalid: as sg_gemm; beta != 0 with an e4m3 output (-11); an unknown
+ * activation, bias dtype or out_dtype, or out_scale not finite and > 0 (-15).
+ */
+int sg_gemm_ex(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
+               const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+               int64_t ldc, int dtype, const sg_epilogue* epi, void* stream);
+
 /*
  * sg_gemm_strided_batched: for b in [0, batch): C_b = alpha * op(A_b) * op(B_b)
  * + beta * C_b, with X_b = X + b * strideX elements -- the same BLAS update as

@@ -7,6 +7,7 @@ in the library's HIP kernels.  There is no fallback: if the library is missing o
 fails to load, every call raises.
 
     gemm(A, B, C, alpha=1, beta=0, transA='N', transB='N')   # C updated in place
+    gemm_ex(A, B, C, ..., bias=None, activation='gelu', out_scale=None)  # + epilogue
     swiglu_gemm(A, Wfused, Y, scale_a=1, scale_w=1)          # Y written in place
     interleave_gate_up(W1, W2, out=None) -> Wfused
     silu_mul(G, U, Y)                                        # unfused activation
@@ -23,6 +24,14 @@ LIB_PATH = os.path.join(HERE, "libswiglu_gemm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "swiglu_gemm.h")
 
 SG_F32, SG_F16, SG_BF16, SG_F8E4M3 = 0, 1, 2, 3
+ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2, "gelu_tanh": 3, "silu": 4}
+
+
+class Epilogue(ctypes.Structure):
+    """sg_epilogue of include/swiglu_gemm.h."""
+    _fields_ = [("bias", ctypes.c_void_p), ("bias_dtype", ctypes.c_int),
+                ("activation", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("out_scale", ctypes.c_float)]
 
 _lib = None
 _lock = threading.Lock()
@@ -47,6 +56,9 @@ def lib() -> ctypes.CDLL:
         L.sg_gemm.argtypes = [c, c, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
                               ctypes.c_int, vp]
         L.sg_gemm.restype = ctypes.c_int
+        L.sg_gemm_ex.argtypes = [c, c, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
+                                 ctypes.c_int, ctypes.POINTER(Epilogue), vp]
+        L.sg_gemm_ex.restype = ctypes.c_int
         L.sg_gemm_strided_batched.argtypes = [c, c, i64, i64, i64, f32, vp, i64, i64, vp, i64,
                                               i64, f32, vp, i64, i64, i64, ctypes.c_int, vp]
         L.sg_gemm_strided_batched.restype = ctypes.c_int
@@ -136,6 +148,37 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N", tran
                        int(ldb), float(beta), ctypes.c_void_p(C.data_ptr()), int(ldc), code,
                        _stream(C))
     _check(st, "sg_gemm")
+    return C
+
+
+def gemm_ex(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N",
+            transB: str = "N", bias=None, activation: str = "none", out_scale=None,
+            dtype: int | None = None, M=None, N=None, K=None, lda=None, ldb=None, ldc=None):
+    """C = out(act(alpha * op(A) @ op(B) + beta * C_old + bias[n])), in place on C.
+    bias: None or a device vector of N values (fp32 / fp16 / bf16).  activation:
+    'none', 'relu', 'gelu', 'gelu_tanh' or 'silu'.  out_scale: None (C has gemm's
+    output type) or the per-tensor scale of an e4m3 output (C an e4m3 / uint8
+    tensor holding the codes of y / out_scale; beta must be 0)."""
+    code = _dtype_code(A) if dtype is None else dtype
+    ta, tb = transA.upper(), transB.upper()
+    if M is None:
+        M = A.size(1) if ta == "T" else A.size(0)
+        K = A.size(0) if ta == "T" else A.size(1)
+        N = B.size(0) if tb == "T" else B.size(1)
+    lda = _ld(A) if lda is None else lda
+    ldb = _ld(B) if ldb is None else ldb
+    ldc = _ld(C) if ldc is None else ldc
+    if activation not in ACTIVATIONS:
+        raise ValueError("unknown activation %r" % activation)
+    epi = Epilogue(ctypes.c_void_p(bias.data_ptr()) if bias is not None else None,
+                   _dtype_code(bias) if bias is not None else SG_F32, ACTIVATIONS[activation],
+                   SG_F8E4M3 if out_scale is not None else -1,
+                   float(out_scale) if out_scale is not None else 1.0)
+    st = lib().sg_gemm_ex(ta.encode(), tb.encode(), int(M), int(N), int(K), float(alpha),
+                          ctypes.c_void_p(A.data_ptr()), int(lda), ctypes.c_void_p(B.data_ptr()),
+                          int(ldb), float(beta), ctypes.c_void_p(C.data_ptr()), int(ldc), code,
+                          ctypes.byref(epi), _stream(C))
+    _check(st, "sg_gemm_ex")
     return C
 
 

@@ -247,12 +247,34 @@ void set_last(const char* what, int cfg, int splits) {
                   cfg >= 0 && cfg < kNumCfg16 ? kCfg16[cfg].name : "-", splits);
 }
 
+// The configuration compiled with the extra epilogue steps (EPI_GEMM_EX) that is
+// nearest to cfg: the same kernel family and tile size where possible, else the
+// register-staged kernel (any shape); -1 for e4m3 without one (generic kernel).
+int ex_cfg(int cfg, const Problem16& q, int64_t kps) {
+    static const int k16[] = {2, 6, 10, 13, 24, 30, 32};
+    static const int k8[] = {14, 15, 16, 17, 33};
+    const bool e4m3 = q.esz == 1;
+    const int* list = e4m3 ? k8 : k16;
+    const int n = e4m3 ? 5 : 7;
+    for (int i = 0; i < n; ++i)
+        if (list[i] == cfg) return cfg;
+    const Cfg16& c = kCfg16[cfg];
+    int alt;
+    if (e4m3) alt = c.BM >= 256 ? 14 : 33;
+    else if (!c.dma) alt = 2;
+    else alt = c.BM >= 256 ? 10 : (c.BN >= 256 ? 32 : 13);
+    if (kCfg16[alt].dma && !dma_ok(kCfg16[alt], q, kps)) alt = e4m3 ? -1 : 2;
+    return alt;
+}
+
 template <int DT>
 hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* out,
                  bool out_vec, const char* what, hipStream_t st, int* splits_used) {
     if (!p.A || !p.B || !out) return hipErrorInvalidValue;           // never launch on NULL
     int cfg = 0, splits = 1;
     choose16(q, &cfg, &splits);
+    if (cfg >= 0 && epi == EPI_GEMM_EX && splits <= 1)
+        cfg = ex_cfg(cfg, q, split_len(q.K, 1, kCfg16[cfg].BK));
     if (cfg < 0) return hipErrorNotSupported;   // caller takes its generic path
     if (p.batch > 1) splits = 1;                // no split-K inside a batch
     const Cfg16& c = kCfg16[cfg];
@@ -306,7 +328,8 @@ int choose_decode(int epi) { return epi == EPI_SWIGLU_W12 ? 1 : 5; }
 template <int DT>
 hipError_t try_decode(bool tb, int epi, const void* A, int64_t lda, const void* B,
                       const void* B2, int64_t ldb, void* C, int64_t ldc, int64_t M, int64_t N,
-                      int64_t K, float alpha, float beta, hipStream_t st) {
+                      int64_t K, float alpha, float beta, hipStream_t st,
+                      const EpiEx& ex = EpiEx{}) {
     constexpr int esz = DT == DT_E4M3 ? 1 : 2;
     int fc = -1, fs = 0;
     if (forced_config(&fc, &fs)) return hipErrorNotSupported;
@@ -330,6 +353,7 @@ hipError_t try_decode(bool tb, int epi, const void* A, int64_t lda, const void* 
         if (oc >= 0 && os <= 1) return hipErrorNotSupported;
         cfg = choose_decode(epi);
     }
+    if (ex.on) cfg = 5;                         // the tile compiled with the extra steps
     const DecodeCfg& c = kDecodeCfg[cfg];
     if (epi == EPI_SWIGLU_W12 && (c.BN / c.NW / 32) % 2 != 0) return hipErrorNotSupported;
     const int64_t tiles = cdiv(N, c.BN), nkb = K / (128 / esz);
@@ -371,16 +395,24 @@ hipError_t try_decode(bool tb, int epi, const void* A, int64_t lda, const void* 
     p.units = units;
     p.part = part;
     p.grid = grid;
+    p.ex = ex;
     std::snprintf(g_last_cfg, sizeof(g_last_cfg), "decode cfg=%d %s grid=%d units=%d%s", cfg,
                   c.name, grid, units, split ? " fixup" : "");
-    return launch_decode_dt<DT>(tb, epi, cfg, p, split, st);
+    return launch_decode_dt<DT>(tb, ex.on ? EPI_GEMM_EX : epi, cfg, p, split, st);
+}
+
+// C's stores are 8 bytes wide (four 16-bit values) or, for an e4m3 output, 4 bytes
+bool c_vec_ok(const void* C, int64_t ldc, int64_t sC, const EpiEx& ex) {
+    return ex.out_fp8 ? aligned(C, 4) && ldc % 4 == 0 && sC % 4 == 0
+                      : aligned(C, 8) && ldc % 4 == 0 && sC % 8 == 0;
 }
 
 template <int DT>
 hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
                   const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
-                  int64_t ldc, const Batch& bt, hipStream_t st) {
+                  int64_t ldc, const Batch& bt, hipStream_t st, const EpiEx& ex) {
     Gemm16Params p{};
+    p.ex = ex;
     p.batch = (int)bt.n;
     p.sA = bt.sA;
     p.sB = bt.sB;
@@ -397,30 +429,30 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
     p.beta = beta;
     if (bt.n == 1 && !ta) {
         const hipError_t d = try_decode<DT>(tb, EPI_GEMM, A, lda, B, nullptr, ldb, C, ldc, M, N,
-                                            K, alpha, beta, st);
+                                            K, alpha, beta, st, ex);
         if (d != hipErrorNotSupported) return d;
     }
     p.vec_a = aligned(A, 16) && (lda % 8 == 0) && (bt.sA % 16 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 8 == 0) && (bt.sB % 16 == 0);
     Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 2, bt.n};
     int splits = 1;
-    hipError_t e = run16<DT>(ta, tb, EPI_GEMM, q, p, C,
-                             aligned(C, 8) && (ldc % 4 == 0) && (bt.sC % 8 == 0), "gemm16", st,
-                             &splits);
+    hipError_t e = run16<DT>(ta, tb, ex.on ? EPI_GEMM_EX : EPI_GEMM, q, p, C,
+                             c_vec_ok(C, ldc, bt.sC, ex), "gemm16", st, &splits);
     if (e != hipSuccess || splits <= 1) return e;
     float* ws = nullptr;
     e = workspace((size_t)splits * M * N * sizeof(float), &ws);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_gemm_kernel<DT>, dim3(grid_1d(M * N)), dim3(256), 0, st, ws, splits,
-                       (int)M, (int)N, C, ldc, alpha, beta);
+                       (int)M, (int)N, C, ldc, alpha, beta, ex);
     return hipGetLastError();
 }
 
 // e4m3 GEMM: A, B e4m3 codes, C bf16 (alpha carries the per-tensor scales).
 hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                  int64_t lda, const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
-                 const Batch& bt, hipStream_t st) {
+                 const Batch& bt, hipStream_t st, const EpiEx& ex) {
     Gemm16Params p{};
+    p.ex = ex;
     p.batch = (int)bt.n;
     p.sA = bt.sA;
     p.sB = bt.sB;
@@ -437,23 +469,22 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
     p.beta = beta;
     if (bt.n == 1 && !ta) {
         const hipError_t d = try_decode<DT_E4M3>(tb, EPI_GEMM, A, lda, B, nullptr, ldb, C, ldc, M,
-                                                 N, K, alpha, beta, st);
+                                                 N, K, alpha, beta, st, ex);
         if (d != hipErrorNotSupported) return d;
     }
     p.vec_a = aligned(A, 16) && (lda % 16 == 0) && (bt.sA % 16 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 16 == 0) && (bt.sB % 16 == 0);
     Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1, bt.n};
     int splits = 1;
-    hipError_t e = run16<DT_E4M3>(ta, tb, EPI_GEMM, q, p, C,
-                                  aligned(C, 8) && (ldc % 4 == 0) && (bt.sC % 8 == 0), "gemm8",
-                                  st, &splits);
+    hipError_t e = run16<DT_E4M3>(ta, tb, ex.on ? EPI_GEMM_EX : EPI_GEMM, q, p, C,
+                                  c_vec_ok(C, ldc, bt.sC, ex), "gemm8", st, &splits);
     if (e == hipErrorNotSupported) {
         std::snprintf(g_last_cfg, sizeof(g_last_cfg), "gemm8 generic splits=1");
         for (int64_t z = 0; z < bt.n; ++z) {   // rare path (K tails, odd alignment)
             hipLaunchKernelGGL(gemm_e4m3_generic, dim3(grid_1d(M * N)), dim3(256), 0, st,
                                (const uint8_t*)A + z * bt.sA, (const uint8_t*)B + z * bt.sB,
-                               (uint16_t*)((char*)C + z * bt.sC), lda, ldb, ldc, (int)M, (int)N,
-                               (int)K, (int)ta, (int)tb, alpha, beta);
+                               (void*)((char*)C + z * bt.sC), lda, ldb, ldc, (int)M, (int)N,
+                               (int)K, (int)ta, (int)tb, alpha, beta, ex);
         }
         return hipGetLastError();
     }
@@ -462,7 +493,7 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
     e = workspace((size_t)splits * M * N * sizeof(float), &ws);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_gemm_kernel<DT_BF16>, dim3(grid_1d(M * N)), dim3(256), 0, st, ws,
-                       splits, (int)M, (int)N, C, ldc, alpha, beta);
+                       splits, (int)M, (int)N, C, ldc, alpha, beta, ex);
     return hipGetLastError();
 }
 
@@ -476,8 +507,9 @@ hipError_t launch_f32(const GemmF32Params& p, hipStream_t st) {
 
 hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
                     const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
-                    int64_t ldc, const Batch& bt, hipStream_t st) {
+                    int64_t ldc, const Batch& bt, hipStream_t st, const EpiEx& ex) {
     GemmF32Params p{};
+    p.ex = ex;
     p.batch = (int)bt.n;
     p.sA = bt.sA;
     p.sB = bt.sB;
@@ -558,10 +590,23 @@ hipError_t run_w12(int cfg, Gemm16Params p, hipStream_t st) {
 // one problem or a strided batch.
 int gemm_run(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
              int64_t lda, const void* B, int64_t ldb, float beta, void* C, int64_t ldc,
-             int dtype, const Batch& bt, hipStream_t st) {
+             int dtype, const Batch& bt, hipStream_t st, const EpiEx& ex = EpiEx{}) {
     if (K == 0 || alpha == 0.0f) {
         std::snprintf(g_last_cfg, sizeof(g_last_cfg), "scale_only");
         const unsigned g = grid_1d(M * N);
+        if (ex.on) {   // one problem (no batch with the extra epilogue steps)
+            std::snprintf(g_last_cfg, sizeof(g_last_cfg), "epilogue_only");
+            if (dtype == SG_F32)
+                hipLaunchKernelGGL(epilogue_only_kernel<DT_F32>, dim3(g), dim3(256), 0, st, C, ldc,
+                                   (int)M, (int)N, beta, ex);
+            else if (dtype == SG_F16)
+                hipLaunchKernelGGL(epilogue_only_kernel<DT_F16>, dim3(g), dim3(256), 0, st, C, ldc,
+                                   (int)M, (int)N, beta, ex);
+            else
+                hipLaunchKernelGGL(epilogue_only_kernel<DT_BF16>, dim3(g), dim3(256), 0, st, C,
+                                   ldc, (int)M, (int)N, beta, ex);
+            return status_of(hipGetLastError());
+        }
         for (int64_t z = 0; z < bt.n; ++z) {
             void* Cz = reinterpret_cast<char*>(C) + z * bt.sC;
             switch (dtype) {
@@ -584,16 +629,16 @@ int gemm_run(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, con
     hipError_t e;
     switch (dtype) {
         case SG_F32:
-            e = gemm_f32(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st);
+            e = gemm_f32(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st, ex);
             break;
         case SG_F16:
-            e = gemm16<DT_F16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st);
+            e = gemm16<DT_F16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st, ex);
             break;
         case SG_BF16:
-            e = gemm16<DT_BF16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st);
+            e = gemm16<DT_BF16>(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st, ex);
             break;
         default:
-            e = gemm8(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st);
+            e = gemm8(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bt, st, ex);
             break;
     }
     return status_of(e);
@@ -630,6 +675,57 @@ int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alp
     if (M == 0 || N == 0) return 0;
     return gemm_run(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, Batch{},
                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int sg_gemm_ex(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
+               const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+               int64_t ldc, int dtype, const sg_epilogue* epi, void* stream) {
+    EpiEx ex{};
+    if (epi) {
+        const bool out8 = epi->out_dtype == SG_F8E4M3;
+        if (epi->out_dtype != -1 && !out8) return -15;
+        if (epi->activation < SG_ACT_NONE || epi->activation > SG_ACT_SILU) return -15;
+        if (epi->bias && epi->bias_dtype != SG_F32 && epi->bias_dtype != SG_F16 &&
+            epi->bias_dtype != SG_BF16)
+            return -15;
+        if (out8 && (!std::isfinite(epi->out_scale) || !(epi->out_scale > 0.0f) ||
+                     !std::isfinite(1.0f / epi->out_scale)))
+            return -15;
+        if (out8 && beta != 0.0f) return -11;           // C_old would be e4m3 codes
+        ex.bias = epi->bias;
+        ex.bias_dt = epi->bias_dtype == SG_F32 ? DT_F32
+                                               : (epi->bias_dtype == SG_F16 ? DT_F16 : DT_BF16);
+        ex.act = epi->activation;
+        ex.out_fp8 = out8 ? 1 : 0;
+        ex.inv_scale = out8 ? 1.0f / epi->out_scale : 1.0f;
+        ex.on = (epi->bias != nullptr) || epi->activation != SG_ACT_NONE || out8;
+    }
+    if (!ex.on) return sg_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                               dtype, stream);
+    if (!trans_ok(transA)) return -1;
+    if (!trans_ok(transB)) return -2;
+    if (M < 0 || M > kMaxDim) return -3;
+    if (N < 0 || N > kMaxDim) return -4;
+    if (K < 0 || K > kMaxDim) return -5;
+    const bool ta = is_t(transA), tb = is_t(transB);
+    const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
+    if (reads_ab && !A) return -7;
+    {
+        const int64_t need = ta ? M : K;
+        if (lda < (need > 1 ? need : 1)) return -8;
+    }
+    if (reads_ab && !B) return -9;
+    {
+        const int64_t need = tb ? K : N;
+        if (ldb < (need > 1 ? need : 1)) return -10;
+    }
+    if (M > 0 && N > 0 && !C) return -12;
+    if (ldc < (N > 1 ? N : 1)) return -13;
+    if (dtype < SG_F32 || dtype > SG_F8E4M3) return -14;
+    if ((int64_t)M * N > ((int64_t)1 << 40)) return -3;
+    if (M == 0 || N == 0) return 0;
+    return gemm_run(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, Batch{},
+                    reinterpret_cast<hipStream_t>(stream), ex);
 }
 
 int sg_gemm_strided_batched(char transA, char transB, int64_t M, int64_t N, int64_t K,

@@ -23,6 +23,7 @@ struct GemmF32Params {
     int tiles_m, tiles_n;
     int batch;           // strided batch over gridDim.z
     int64_t sA, sB, sC;  // byte distance between consecutive problems
+    EpiEx ex;            // bias / activation / e4m3 output (ex.on == 0: none)
 };
 
 template <bool TA, bool TB>
@@ -84,12 +85,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmF32Params p_) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < p.M) {
-            float* c = p.C + (int64_t)m * p.ldc + n;
-            float v = p.alpha * acc[r];
-            if (p.beta != 0.0f) v += p.beta * *c;
-            *c = v;
-        }
+        if (m < p.M) store_elem<DT_F32>(p.C, (int64_t)m * p.ldc + n, n, p.alpha * acc[r], p.beta, p.ex);
     }
 }
 
@@ -115,6 +111,19 @@ __global__ void __launch_bounds__(256) scale_kernel(void* C, int64_t ldc, int M,
     }
 }
 
+// The same update with the EpiEx steps: y = act(beta*C_old + bias[n]) (C_old
+// read only when beta != 0), stored in DT_OUT or as e4m3 codes.
+template <int DT_OUT>
+__global__ void __launch_bounds__(256) epilogue_only_kernel(void* C, int64_t ldc, int M, int N,
+                                                            float beta, const EpiEx ex) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t m = i / N, n = i - m * N;
+        store_elem<DT_OUT>(C, m * ldc + n, (int)n, 0.0f, beta, ex);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Split-K reductions: sum the fp32 partials of every split in split order (a
 // fixed order, so results are run-to-run identical), then the epilogue.
@@ -123,7 +132,7 @@ __global__ void __launch_bounds__(256) scale_kernel(void* C, int64_t ldc, int M,
 template <int DT_OUT>
 __global__ void __launch_bounds__(256) reduce_gemm_kernel(const float* ws, int splits, int M, int N,
                                                           void* C, int64_t ldc, float alpha,
-                                                          float beta) {
+                                                          float beta, const EpiEx ex) {
     const int64_t total = (int64_t)M * N;
     const int64_t plane = total;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
@@ -131,17 +140,7 @@ __global__ void __launch_bounds__(256) reduce_gemm_kernel(const float* ws, int s
         float s = 0.0f;
         for (int k = 0; k < splits; ++k) s += ws[k * plane + i];
         const int64_t m = i / N, n = i - m * N;
-        if constexpr (DT_OUT == DT_F32) {
-            float* c = reinterpret_cast<float*>(C) + m * ldc + n;
-            float v = alpha * s;
-            if (beta != 0.0f) v += beta * *c;
-            *c = v;
-        } else {
-            uint16_t* c = reinterpret_cast<uint16_t*>(C) + m * ldc + n;
-            float v = alpha * s;
-            if (beta != 0.0f) v += beta * to_f32<DT_OUT>(*c);
-            *c = from_f32<DT_OUT>(v);
-        }
+        store_elem<DT_OUT>(C, m * ldc + n, (int)n, alpha * s, beta, ex);
     }
 }
 
@@ -223,9 +222,10 @@ __device__ __forceinline__ float e4m3_to_f32(uint8_t q) {
 }
 
 __global__ void __launch_bounds__(256) gemm_e4m3_generic(const uint8_t* A, const uint8_t* B,
-                                                         uint16_t* C, int64_t lda, int64_t ldb,
+                                                         void* C, int64_t lda, int64_t ldb,
                                                          int64_t ldc, int M, int N, int K, int ta,
-                                                         int tb, float alpha, float beta) {
+                                                         int tb, float alpha, float beta,
+                                                         const EpiEx ex) {
     const int64_t total = (int64_t)M * N;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * 256) {
@@ -236,10 +236,7 @@ __global__ void __launch_bounds__(256) gemm_e4m3_generic(const uint8_t* A, const
             const uint8_t b = tb ? B[(int64_t)n * ldb + k] : B[(int64_t)k * ldb + n];
             s += e4m3_to_f32(a) * e4m3_to_f32(b);
         }
-        uint16_t* c = C + (int64_t)m * ldc + n;
-        float v = alpha * s;
-        if (beta != 0.0f) v += beta * to_f32<DT_BF16>(*c);
-        *c = from_f32<DT_BF16>(v);
+        store_elem<DT_BF16>(C, (int64_t)m * ldc + n, n, alpha * s, beta, ex);
     }
 }
 

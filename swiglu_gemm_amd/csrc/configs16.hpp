@@ -120,6 +120,25 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(41, 1, 256, 256, 32, 3, 2, 2)    \
     X(42, 2, 256, 256, 32, 5, 4, 2)
 
+// the configurations the library chooses by itself, also compiled with the extra
+// epilogue steps (EPI_GEMM_EX); any other one maps to the nearest of these (the
+// register-staged 256 x 256 tile holds 256 accumulators per lane: no room left)
+#define SG_CONFIGS_EX(X)               \
+    X(2, 0, 128, 128, 64, 2, 2, 2)     \
+    X(6, 1, 128, 128, 32, 4, 2, 2)     \
+    X(10, 1, 256, 256, 64, 2, 4, 2)    \
+    X(13, 1, 128, 128, 64, 2, 2, 4)    \
+    X(24, 1, 256, 320, 64, 2, 4, 2)    \
+    X(30, 1, 128, 128, 64, 5, 2, 4)    \
+    X(32, 1, 128, 256, 64, 3, 2, 4)
+
+#define SG_CONFIGS_E4M3_EX(X)          \
+    X(14, 1, 256, 256, 128, 2, 4, 2)   \
+    X(15, 1, 128, 128, 128, 2, 2, 4)   \
+    X(16, 1, 32, 256, 128, 4, 1, 4)    \
+    X(17, 1, 32, 128, 128, 4, 1, 4)    \
+    X(33, 1, 128, 256, 128, 3, 2, 2)
+
 // the same for every e4m3 row (all direct-to-LDS)
 #define SG_CONFIGS_E4M3(X)             \
     X(14, 1, 256, 256, 128, 2, 4, 2)   \

@@ -44,6 +44,7 @@ struct DecodeParams {
     int units;          // tiles * nkb
     float* part;        // partial sums: [work-groups][2 slots][BN * 32] fp32
     int grid;           // work-groups of the streaming kernel
+    EpiEx ex;           // EPI_GEMM_EX: bias / activation / e4m3 output
 };
 
 // First unit of work-group w when `units` are dealt to G work-groups.
@@ -67,7 +68,20 @@ __device__ __forceinline__ void decode_store(const DecodeParams& p, const f32x16
     const int lq = (lane >> 5) * 4;
     uint16_t* out = reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc;
     const float a = p.alpha;
-    if constexpr (EPI == EPI_GEMM) {
+    if constexpr (EPI == EPI_GEMM_EX) {
+        // the EpiEx steps, element by element; C is indexed in its own element size
+        // (2 bytes, or 1 for an e4m3 output)
+        void* C = reinterpret_cast<char*>(p.C) + (int64_t)m * p.ldc * (p.ex.out_fp8 ? 1 : 2);
+#pragma unroll
+        for (int tn = 0; tn < FN; ++tn)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = t * BN + wave * TN + tn * 32 + 8 * g + lq + e;
+                    if (n < p.N) store_elem<DT_OUT>(C, n, n, a * acc[tn][4 * g + e], p.beta, p.ex);
+                }
+    } else if constexpr (EPI == EPI_GEMM) {
         const float beta = p.beta;
 #pragma unroll
         for (int tn = 0; tn < FN; ++tn)
@@ -400,6 +414,8 @@ constexpr int kNumDecodeCfg = sizeof(kDecodeCfg) / sizeof(kDecodeCfg[0]);
     X(5, 128, 4, 4)          \
     X(6, 128, 2, 4)
 
+#define SG_DECODE_CONFIGS_EX(X) X(5, 128, 4, 4)
+
 // The streaming kernel on p.grid work-groups, then (split: some column tile is
 // shared by several runs) the fix-up kernel over the column tiles.
 template <int DT, bool TB, int EPI>
@@ -416,20 +432,31 @@ hipError_t launch_decode_cfg(int cfg, const DecodeParams& p, bool split, hipStre
         } else {                                                                            \
             return hipErrorInvalidValue;                                                    \
         }
-    switch (cfg) {
-        SG_DECODE_CONFIGS(SG_DCASE)
-        default: return hipErrorInvalidValue;
+    if constexpr (EPI == EPI_GEMM_EX) {   // the extra epilogue steps: the default tile only
+        switch (cfg) {
+            SG_DECODE_CONFIGS_EX(SG_DCASE)
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (cfg) {
+            SG_DECODE_CONFIGS(SG_DCASE)
+            default: return hipErrorInvalidValue;
+        }
     }
 #undef SG_DCASE
 }
 
-// epi: EPI_GEMM ('N' or 'T' weight), EPI_SWIGLU and EPI_SWIGLU_W12 ('N' only).
+// epi: EPI_GEMM / EPI_GEMM_EX ('N' or 'T' weight), EPI_SWIGLU and EPI_SWIGLU_W12
+// ('N' only).
 template <int DT>
 hipError_t launch_decode_dt(bool tb, int epi, int cfg, const DecodeParams& p, bool split,
                             hipStream_t st) {
     if (epi == EPI_GEMM)
         return tb ? launch_decode_cfg<DT, true, EPI_GEMM>(cfg, p, split, st)
                   : launch_decode_cfg<DT, false, EPI_GEMM>(cfg, p, split, st);
+    if (epi == EPI_GEMM_EX)
+        return tb ? launch_decode_cfg<DT, true, EPI_GEMM_EX>(cfg, p, split, st)
+                  : launch_decode_cfg<DT, false, EPI_GEMM_EX>(cfg, p, split, st);
     if (tb) return hipErrorInvalidValue;
     if (epi == EPI_SWIGLU) return launch_decode_cfg<DT, false, EPI_SWIGLU>(cfg, p, split, st);
     if (epi == EPI_SWIGLU_W12)

@@ -17,6 +17,8 @@
 //   EPI_PARTIAL  raw fp32 sums of one K split into workspace [split][M][N].
 #pragma once
 
+#include <type_traits>
+
 #include "sg_device.hpp"
 
 namespace sg {
@@ -26,12 +28,122 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return (uint32_t)from_f32<DT>(a) | ((uint32_t)from_f32<DT>(b) << 16);
 }
 
+// EPI_GEMM_EX: y = act(alpha*acc + beta*C_old + bias[n]), stored in DT or, for an
+// e4m3 output, as the e4m3fn code of y * inv_scale.  Each wave stages one 32 x 32
+// fp32 fragment at a time in a region of the (by now idle) LDS ring of its own, and
+// a rolled loop then finishes four consecutive columns per lane (row-contiguous
+// stores).  The accumulator is only ever indexed by constants: with the
+// activation code inlined into every register quad instead, the epilogue exceeds
+// the unroll limit, the loop stays rolled, and the whole accumulator array --
+// main loop included -- is moved to scratch memory.
+// f(std::integral_constant<int, I>) for I = B .. E-1, expanded at compile time (the
+// index is a constant inside f whether or not the unroller would unroll a loop).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+template <int DT, int FM, int FN>
+__device__ __forceinline__ void epilogue_gemm_ex_lds(const Gemm16Params& p, f32x16 (&acc)[FN][FM],
+                                                     char* smem, int mb, int nb, int wave,
+                                                     int lane) {
+    constexpr int LD = 36;                                 // floats per staged row (+4 pad)
+    float* frag = reinterpret_cast<float*>(smem) + wave * (32 * LD);
+    const EpiEx& ex = p.ex;
+    const float alpha = p.alpha, beta = ex.out_fp8 ? 0.0f : p.beta;
+    const int lm = lane & 31, lq = (lane >> 5) * 4;
+    // a lane finishes columns c4..c4+3 of every fragment (quads q = lane + 64j share
+    // q & 7): its bias values are loaded once, before the fragments
+    const int c4 = (lane & 7) * 4;
+    f32x4 bq[FN];
+#pragma unroll
+    for (int tn = 0; tn < FN; ++tn)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = nb + tn * 32 + c4 + e;
+            bq[tn][e] = n < p.N ? ex_bias(ex, n) : 0.0f;
+        }
+    static_for<0, FM * FN>([&](auto fi) __attribute__((always_inline)) {
+        constexpr int tm = decltype(fi)::value / FN, tn = decltype(fi)::value % FN;
+        {
+            // D^T layout: register quad g of lane l holds row l%32, columns 8g + 4(l/32) + 0..3
+            static_for<0, 4>([&](auto gi) __attribute__((always_inline)) {
+                constexpr int g = decltype(gi)::value;
+                *reinterpret_cast<f32x4*>(frag + lm * LD + 8 * g + lq) =
+                    f32x4{acc[tn][tm][4 * g], acc[tn][tm][4 * g + 1], acc[tn][tm][4 * g + 2],
+                          acc[tn][tm][4 * g + 3]};
+            });
+            __builtin_amdgcn_wave_barrier();
+            const int n = nb + tn * 32 + c4;
+            const int valid = p.N - n < 4 ? p.N - n : 4;
+#pragma unroll 2
+            for (int j = 0; j < 4; ++j) {   // two independent quads per pass overlap
+                const int r = (lane >> 3) + 8 * j;         // quad q = lane + 64j: row q/8
+                const int m = mb + tm * 32 + r;
+                if (m >= p.M || valid <= 0) continue;
+                const int64_t idx = (int64_t)m * p.ldc + n;
+                f32x4 v = *reinterpret_cast<const f32x4*>(frag + r * LD + c4);
+                const bool vec = p.vec_c && valid == 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= alpha;
+                if (beta != 0.0f) {
+                    const uint16_t* c = reinterpret_cast<const uint16_t*>(p.C) + idx;
+                    if (vec) {
+                        const u32x2 old = *reinterpret_cast<const u32x2*>(c);
+                        v[0] += beta * to_f32<DT>((uint16_t)(old.x & 0xffff));
+                        v[1] += beta * to_f32<DT>((uint16_t)(old.x >> 16));
+                        v[2] += beta * to_f32<DT>((uint16_t)(old.y & 0xffff));
+                        v[3] += beta * to_f32<DT>((uint16_t)(old.y >> 16));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (e < valid) v[e] += beta * to_f32<DT>(c[e]);
+                    }
+                }
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = ex_act(ex.act, v[e] + bq[tn][e]);
+                if (ex.out_fp8) {
+                    uint8_t* c8 = reinterpret_cast<uint8_t*>(p.C) + idx;
+                    const float ys[4] = {y[0] * ex.inv_scale, y[1] * ex.inv_scale,
+                                         y[2] * ex.inv_scale, y[3] * ex.inv_scale};
+                    const uint32_t w = e4m3_code4(ys);
+                    if (vec) {
+                        *reinterpret_cast<uint32_t*>(c8) = w;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (e < valid) c8[e] = (uint8_t)(w >> (8 * e));
+                    }
+                } else {
+                    uint16_t* c = reinterpret_cast<uint16_t*>(p.C) + idx;
+                    if (vec) {
+                        u32x2 o;
+                        o.x = pack2<DT>(y[0], y[1]);
+                        o.y = pack2<DT>(y[2], y[3]);
+                        *reinterpret_cast<u32x2*>(c) = o;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (e < valid) c[e] = from_f32<DT>(y[e]);
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    });
+}
+
 template <int DT, int EPI, int FM, int FN>
 __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[FN][FM], int m0,
                                            int n0, int BM, int BN, int mb, int nb, int lane) {
     const int lm = lane & 31, lq = (lane >> 5) * 4;
     const bool inside = (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
+    static_assert(EPI != EPI_GEMM_EX, "EPI_GEMM_EX uses epilogue_gemm_ex_lds");
     if constexpr (EPI == EPI_GEMM) {
         uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
         const bool full_c = inside && p.vec_c;

@@ -291,7 +291,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm16_kernel(const Gemm16Par
         for (; kt < nkt; ++kt) body(kt, std::false_type{});
     }
 
-    epilogue16<DT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN, lane);
+    if constexpr (EPI == EPI_GEMM_EX) {
+        static_assert(2 * STAGE >= (NT / 64) * 32 * 36 * 4, "EX staging fits the LDS ring");
+        __syncthreads();
+        epilogue_gemm_ex_lds<DT, FM, FN>(p, acc, smem, m0 + wm * TM, n0 + wn * TN,
+                                         threadIdx.x >> 6, lane);
+    } else {
+        epilogue16<DT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN, lane);
+    }
 }
 
 }  // namespace sg

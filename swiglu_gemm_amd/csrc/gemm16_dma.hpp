@@ -329,6 +329,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
         static_assert(BM * (BN + 8) <= S * STAGE, "staged SwiGLU tile fits the LDS ring");
         epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN, W12>(
             p, acc, smem, m0, n0, wm * TM, W12 ? wn * (TN / 2) : wn * TN, lane);
+    } else if constexpr (EPI == EPI_GEMM_EX) {
+        static_assert(S * STAGE >= NW * 32 * 36 * 4, "EX staging fits the LDS ring");
+        __syncthreads();
+        epilogue_gemm_ex_lds<DT_OUT, FM, FN>(p, acc, smem, m0 + wm * TM, n0 + wn * TN, wave, lane);
     } else {
         epilogue16<DT_OUT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
                                         lane);

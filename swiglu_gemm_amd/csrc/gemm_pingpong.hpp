@@ -187,6 +187,11 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const Gemm16Params p_) 
         static_assert(BM * (BN + 8) <= S * STAGE, "staged SwiGLU tile fits the LDS ring");
         epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 512, false>(p, acc, smem, m0, n0, wm * TM,
                                                                      wn * TN, lane);
+    } else if constexpr (EPI == EPI_GEMM_EX) {
+        static_assert(S * STAGE >= 8 * 32 * 36 * 4, "EX staging fits the LDS ring");
+        __syncthreads();
+        epilogue_gemm_ex_lds<DT_OUT, FM, FN>(p, acc, smem, m0 + wm * TM, n0 + wn * TN,
+                                             threadIdx.x >> 6, lane);
     } else {
         epilogue16<DT_OUT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
                                         lane);

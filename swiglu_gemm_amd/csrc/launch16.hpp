@@ -62,7 +62,19 @@ template <int DT, bool TA, bool TB, int EPI>
 hipError_t launch16_cfg(int cfg, const Gemm16Params& p, int splits, hipStream_t st) {
 #define SG_CASE(ID, DMA, BM, BN, BK, S, WM, WN) \
     case ID: return launch_one<DT, TA, TB, EPI, DMA, BM, BN, BK, S, WM, WN>(p, splits, st);
-    if constexpr (DT == DT_E4M3) {
+    if constexpr (EPI == EPI_GEMM_EX) {
+        if constexpr (DT == DT_E4M3) {
+            switch (cfg) {
+                SG_CONFIGS_E4M3_EX(SG_CASE)
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (cfg) {
+                SG_CONFIGS_EX(SG_CASE)
+                default: return hipErrorInvalidValue;
+            }
+        }
+    } else if constexpr (DT == DT_E4M3) {
         switch (cfg) {
             SG_CONFIGS_E4M3(SG_CASE)
             default: return hipErrorInvalidValue;
@@ -83,7 +95,8 @@ hipError_t launch16_cfg(int cfg, const Gemm16Params& p, int splits, hipStream_t 
 #undef SG_CASE
 }
 
-// epi: EPI_GEMM / EPI_PARTIAL for any transpose pair; EPI_SWIGLU(_W12) for NN only.
+// epi: EPI_GEMM / EPI_GEMM_EX / EPI_PARTIAL for any transpose pair; EPI_SWIGLU(_W12)
+// for NN only.
 template <int DT, bool TA, bool TB>
 hipError_t launch16_tr(int epi, int cfg, const Gemm16Params& p, int splits, hipStream_t st) {
     if constexpr (!TA && !TB) {
@@ -92,6 +105,7 @@ hipError_t launch16_tr(int epi, int cfg, const Gemm16Params& p, int splits, hipS
             return launch16_cfg<DT, TA, TB, EPI_SWIGLU_W12>(cfg, p, splits, st);
     }
     if (epi == EPI_GEMM) return launch16_cfg<DT, TA, TB, EPI_GEMM>(cfg, p, splits, st);
+    if (epi == EPI_GEMM_EX) return launch16_cfg<DT, TA, TB, EPI_GEMM_EX>(cfg, p, splits, st);
     if (epi == EPI_PARTIAL) return launch16_cfg<DT, TA, TB, EPI_PARTIAL>(cfg, p, splits, st);
     return hipErrorInvalidValue;
 }

@@ -15,7 +15,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3 };
-enum : int { EPI_GEMM = 0, EPI_SWIGLU = 1, EPI_PARTIAL = 2, EPI_SWIGLU_W12 = 3 };
+// EPI_GEMM_EX: EPI_GEMM plus the EpiEx steps (compiled for the configurations the
+// library chooses, see SG_CONFIGS_EX / SG_CONFIGS_E4M3_EX)
+enum : int { EPI_GEMM = 0, EPI_SWIGLU = 1, EPI_PARTIAL = 2, EPI_SWIGLU_W12 = 3, EPI_GEMM_EX = 4 };
 
 // ---------------------------------------------------------------------------
 // 16-bit storage <-> fp32
@@ -45,6 +47,105 @@ __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// ---------------------------------------------------------------------------
+// Extra epilogue steps of the GEMM ("GEMM o Coração Matemático" §1 and §13.3:
+// bias and activations folded into the GEMM's epilogue; "为什么 GEMM 是 CUDA 的必修课",
+// optimisation list: bias, activation, scale, quantise before the store).  With
+// v = alpha*acc + beta*C_old:  y = act(v + bias[n]);  the stored value is y in
+// the output type, or the e4m3fn code of y * (1/out_scale) (per-tensor scale,
+// §12.4; the reciprocal rounded to fp32 once, on the host).
+// ---------------------------------------------------------------------------
+enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_GELU_TANH = 3, ACT_SILU = 4 };
+
+struct EpiEx {
+    const void* bias;  // nullptr, or N values (bias_dt), one per column
+    int bias_dt;       // DT_F32, DT_F16 or DT_BF16
+    int act;           // ACT_*
+    int out_fp8;       // 1: C holds e4m3fn codes of y * inv_scale (beta == 0)
+    float inv_scale;   // fp32 reciprocal of the output's per-tensor scale
+    int on;            // any step present (0: the plain GEMM epilogue)
+};
+
+__device__ __forceinline__ float ex_bias(const EpiEx& ex, int n) {
+    if (!ex.bias) return 0.0f;
+    if (ex.bias_dt == DT_F32) return reinterpret_cast<const float*>(ex.bias)[n];
+    const uint16_t b = reinterpret_cast<const uint16_t*>(ex.bias)[n];
+    return ex.bias_dt == DT_F16 ? to_f32<DT_F16>(b) : to_f32<DT_BF16>(b);
+}
+
+// GELU(x) = x * Phi(x) = x/2 * erfc(-x / sqrt 2), with erfc(u) for u >= 0 from
+// Abramowitz & Stegun 7.1.26 (t = 1/(1 + p u), erfc(u) ~ t*(a1 + t*(a2 + ... a5 t))
+// * e^(-u^2), absolute error <= 1.5e-7) and erfc(-u) = 2 - erfc(u): no cancellation
+// in the negative tail, one reciprocal and one exp2 instead of a library erfc.
+// The tanh form: x/2 * (1 + tanh z) = x * sigma(2z) exactly (sigma the logistic
+// function), z = sqrt(2/pi) * (x + 0.044715 x^3), evaluated like SiLU.
+__device__ __forceinline__ float ex_act(int act, float x) {
+    constexpr float kLog2e = 1.44269504088896341f;
+    switch (act) {
+        case ACT_RELU: return x > 0.0f ? x : 0.0f;
+        case ACT_GELU: {
+            const float u = x * -0.70710678118654752f;
+            const float a = __builtin_fabsf(u);
+            const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
+            const float poly =
+                t * (0.254829592f +
+                     t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+            const float q = poly * __builtin_amdgcn_exp2f(-a * a * kLog2e);
+            return 0.5f * x * (u >= 0.0f ? q : 2.0f - q);
+        }
+        case ACT_GELU_TANH: {
+            const float z = 0.79788456080286536f * (x + 0.044715f * x * x * x);
+            return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.0f * kLog2e * z));
+        }
+        case ACT_SILU: return silu(x);
+        default: return x;
+    }
+}
+
+// OCP e4m3fn codes of four values (byte e of the result = code of x[e]): round to
+// nearest, ties to even, |x| >= 448 (and inf) to +-448, NaN to 0x7F.  gfx950's
+// v_cvt_pk_fp8_f32 rounds to e4m3fn to nearest-even (checked against the exact
+// code-table search on every midpoint of the grid); the clamp turns its overflow
+// into saturation, and NaN, which the clamp would map to -448, is selected back.
+__device__ __forceinline__ uint32_t e4m3_code4(const float (&x)[4]) {
+    float c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = __builtin_fminf(__builtin_fmaxf(x[e], -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+    uint32_t u = (uint32_t)w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (!(x[e] == x[e])) u = (u & ~(0xFFu << (8 * e))) | (0x7Fu << (8 * e));
+    return u;
+}
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+    const float q[4] = {x, 0.0f, 0.0f, 0.0f};
+    return e4m3_code4(q) & 0xFFu;
+}
+
+// Store one output element: v = alpha * sum; adds beta * C_old (read only when
+// beta != 0; never with an e4m3 output), applies the EpiEx steps, rounds once to
+// the output type (DT_OUT: DT_F32, DT_F16 or DT_BF16) or quantises to e4m3.
+template <int DT_OUT>
+__device__ __forceinline__ void store_elem(void* C, int64_t idx, int n, float v, float beta,
+                                           const EpiEx& ex) {
+    if (ex.out_fp8) {
+        const float y = ex_act(ex.act, v + ex_bias(ex, n));
+        reinterpret_cast<uint8_t*>(C)[idx] = (uint8_t)e4m3_code(y * ex.inv_scale);
+        return;
+    }
+    if constexpr (DT_OUT == DT_F32) {
+        float* c = reinterpret_cast<float*>(C) + idx;
+        if (beta != 0.0f) v += beta * *c;
+        *c = ex.on ? ex_act(ex.act, v + ex_bias(ex, n)) : v;
+    } else {
+        uint16_t* c = reinterpret_cast<uint16_t*>(C) + idx;
+        if (beta != 0.0f) v += beta * to_f32<DT_OUT>(*c);
+        *c = from_f32<DT_OUT>(ex.on ? ex_act(ex.act, v + ex_bias(ex, n)) : v);
+    }
+}
+
 // Arguments of the 16-bit / 8-bit MFMA GEMM kernels.
 struct Gemm16Params {
     const uint16_t* A;   // storage of A (16-bit elements; e4m3 kernels reinterpret)
@@ -60,6 +161,7 @@ struct Gemm16Params {
     int epi_flags;      // EPI_SWIGLU: EPI_Y16 (Y rows allow 16-byte stores)
     int batch;          // strided batch: gridDim.z problems (0 or 1: one problem)
     int64_t sA, sB, sC; // byte distance between consecutive problems' A, B, C
+    EpiEx ex;           // EPI_GEMM_EX: bias / activation / e4m3 output
 };
 
 // The problem of work-group blockIdx.z in a strided batch (the identity for z = 0).

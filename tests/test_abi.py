@@ -60,6 +60,36 @@ def test_gemm_argument_validation(L):
     assert gemm(L, N=0, A=NUL, B=NUL, C=NUL, ldb=1, ldc=1) == 0
 
 
+def test_gemm_ex_argument_validation(L):
+    def gx(epi, beta=0.0, **kw):
+        args = dict(ta=b"N", tb=b"N", M=2, N=2, K=2, alpha=1.0, A=P, lda=2, B=P, ldb=2, C=P,
+                    ldc=2, dtype=2)
+        args.update(kw)
+        ref = ctypes.byref(epi) if epi is not None else None
+        return L.sg_gemm_ex(args["ta"], args["tb"], args["M"], args["N"], args["K"],
+                            args["alpha"], args["A"], args["lda"], args["B"], args["ldb"], beta,
+                            args["C"], args["ldc"], args["dtype"], ref, NUL)
+    E = sg.Epilogue
+    gelu = E(None, 0, 2, -1, 1.0)
+    assert gx(gelu, ta=b"X") == -1
+    assert gx(gelu, M=-1) == -3
+    assert gx(gelu, A=NUL) == -7
+    assert gx(gelu, ldb=1) == -10
+    assert gx(gelu, C=NUL) == -12
+    assert gx(gelu, dtype=9) == -14
+    assert gx(E(None, 0, 5, -1, 1.0)) == -15                 # unknown activation
+    assert gx(E(None, 0, -1, -1, 1.0)) == -15
+    assert gx(E(P, 3, 0, -1, 1.0)) == -15                    # e4m3 is not a bias type
+    assert gx(E(None, 0, 0, 2, 1.0)) == -15                  # out_dtype: -1 or e4m3 only
+    assert gx(E(None, 0, 0, 3, 0.0)) == -15                  # out_scale > 0
+    assert gx(E(None, 0, 0, 3, float("nan"))) == -15
+    assert gx(E(None, 0, 0, 3, 1.0), beta=0.5) == -11       # C_old would be e4m3 codes
+    # no steps: exactly sg_gemm (its own validation)
+    assert gx(None, A=NUL) == -7
+    assert gx(E(None, 0, 0, -1, 1.0), ldc=1) == -13
+    assert gx(gelu, M=0, A=NUL, B=NUL, C=NUL) == 0           # quick return
+
+
 def test_swiglu_argument_validation(L):
     def sw(A=P, W=P, Y=P, M=2, N=2, K=2, dt=2, sa=1.0, sw_=1.0):
         return L.sg_swiglu_gemm(A, W, Y, M, N, K, dt, sa, sw_, NUL)
