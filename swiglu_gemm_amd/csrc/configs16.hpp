@@ -60,11 +60,14 @@ constexpr Cfg16 kCfg16[] = {
     {0, 1, 256, 256, 32, 5, 2, 2, "sweep dma 256x256x32 s5 2x2w"},
     {0, 1, 256, 256, 32, 3, 2, 2, "sweep dma 256x256x32 s3 2x2w"},
     {0, 2, 256, 256, 32, 5, 4, 2, "sweep pp 256x256x32 s5 4x2w"},
+    // 64-row tiles: twice the work-groups of 128-row tiles for 65..128-row problems
+    {0, 1, 64, 256, 64, 3, 1, 4, "dma 64x256x64 s3 1x4w"},
+    {0, 1, 64, 128, 64, 4, 1, 4, "dma 64x128x64 s4 1x4w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
 constexpr int kFirstCfgE4M3 = 14;
-constexpr int kFirstSweepCfg = 34;   // ids >= this: the fp16 NN pipeline-depth study
+constexpr int kFirstSweepCfg = 34;   // ids 34..42: the fp16 NN pipeline-depth study
 
 // Whether the direct-to-LDS kernel supports an operand tile: k-contiguous rows of
 // 64 or 128 bytes; row-contiguous rows of 128..1024 bytes made of an even number
@@ -106,7 +109,9 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(29, 2, 256, 256, 32, 5, 4, 2)    \
     X(30, 1, 128, 128, 64, 5, 2, 4)    \
     X(31, 1, 128, 128, 32, 8, 2, 2)    \
-    X(32, 1, 128, 256, 64, 3, 2, 4)
+    X(32, 1, 128, 256, 64, 3, 2, 4)    \
+    X(43, 1, 64, 256, 64, 3, 1, 4)     \
+    X(44, 1, 64, 128, 64, 4, 1, 4)
 
 // the pipeline-depth study rows, instantiated for fp16 NN EPI_GEMM only
 #define SG_CONFIGS_SWEEP(X)            \

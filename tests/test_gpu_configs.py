@@ -14,7 +14,7 @@ from helpers import assert_close, bits_equal, from_dev, split_count, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-CFGS16 = list(range(14)) + [18, 19, 20, 22] + list(range(24, 33))   # every 16-bit configuration id
+CFGS16 = list(range(14)) + [18, 19, 20, 22] + list(range(24, 33)) + [43, 44]   # every 16-bit id
 WIDE = [24, 25, 26]                # 320-column tiles (640-byte LDS rows)
 TRANS = ["NN", "NT", "TN", "TT"]
 

@@ -15,7 +15,7 @@ from helpers import assert_close, bits_equal, from_dev, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-W12_CFGS16 = [10, 8, 32, 6]      # configurations that can take separate weights
+W12_CFGS16 = [10, 8, 32, 6, 43]  # configurations that can take separate weights
 W12_CFGS8 = [14, 16, 33]
 
 
