@@ -688,28 +688,7 @@ int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alp
 int sg_gemm_ex(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
                const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
                int64_t ldc, int dtype, const sg_epilogue* epi, void* stream) {
-    EpiEx ex{};
-    if (epi) {
-        const bool out8 = epi->out_dtype == SG_F8E4M3;
-        if (epi->out_dtype != -1 && !out8) return -15;
-        if (epi->activation < SG_ACT_NONE || epi->activation > SG_ACT_SILU) return -15;
-        if (epi->bias && epi->bias_dtype != SG_F32 && epi->bias_dtype != SG_F16 &&
-            epi->bias_dtype != SG_BF16)
-            return -15;
-        if (out8 && (!std::isfinite(epi->out_scale) || !(epi->out_scale > 0.0f) ||
-                     !std::isfinite(1.0f / epi->out_scale)))
-            return -15;
-        if (out8 && beta != 0.0f) return -11;           // C_old would be e4m3 codes
-        ex.bias = epi->bias;
-        ex.bias_dt = epi->bias_dtype == SG_F32 ? DT_F32
-                                               : (epi->bias_dtype == SG_F16 ? DT_F16 : DT_BF16);
-        ex.act = epi->activation;
-        ex.out_fp8 = out8 ? 1 : 0;
-        ex.inv_scale = out8 ? 1.0f / epi->out_scale : 1.0f;
-        ex.on = (epi->bias != nullptr) || epi->activation != SG_ACT_NONE || out8;
-    }
-    if (!ex.on) return sg_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                               dtype, stream);
+    // arguments in order, as sg_gemm; then the epilogue (-15) and its one conflict (-11)
     if (!trans_ok(transA)) return -1;
     if (!trans_ok(transB)) return -2;
     if (M < 0 || M > kMaxDim) return -3;
@@ -730,6 +709,26 @@ int sg_gemm_ex(char transA, char transB, int64_t M, int64_t N, int64_t K, float 
     if (M > 0 && N > 0 && !C) return -12;
     if (ldc < (N > 1 ? N : 1)) return -13;
     if (dtype < SG_F32 || dtype > SG_F8E4M3) return -14;
+    EpiEx ex{};
+    if (epi) {
+        const bool out8 = epi->out_dtype == SG_F8E4M3;
+        if (epi->out_dtype != -1 && !out8) return -15;
+        if (epi->activation < SG_ACT_NONE || epi->activation > SG_ACT_SILU) return -15;
+        if (epi->bias && epi->bias_dtype != SG_F32 && epi->bias_dtype != SG_F16 &&
+            epi->bias_dtype != SG_BF16)
+            return -15;
+        if (out8 && (!std::isfinite(epi->out_scale) || !(epi->out_scale > 0.0f) ||
+                     !std::isfinite(1.0f / epi->out_scale)))
+            return -15;
+        if (out8 && beta != 0.0f) return -11;           // C_old would be e4m3 codes
+        ex.bias = epi->bias;
+        ex.bias_dt = epi->bias_dtype == SG_F32 ? DT_F32
+                                               : (epi->bias_dtype == SG_F16 ? DT_F16 : DT_BF16);
+        ex.act = epi->activation;
+        ex.out_fp8 = out8 ? 1 : 0;
+        ex.inv_scale = out8 ? 1.0f / epi->out_scale : 1.0f;
+        ex.on = (epi->bias != nullptr) || epi->activation != SG_ACT_NONE || out8;
+    }
     if ((int64_t)M * N > ((int64_t)1 << 40)) return -3;
     if (M == 0 || N == 0) return 0;
     return gemm_run(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, Batch{},

@@ -84,6 +84,8 @@ def test_gemm_ex_argument_validation(L):
     assert gx(E(None, 0, 0, 3, 0.0)) == -15                  # out_scale > 0
     assert gx(E(None, 0, 0, 3, float("nan"))) == -15
     assert gx(E(None, 0, 0, 3, 1.0), beta=0.5) == -11       # C_old would be e4m3 codes
+    assert gx(E(None, 0, 9, -1, 1.0), ta=b"X") == -1         # lowest invalid argument first
+    assert gx(E(None, 0, 0, 3, 1e-45)) == -15                # 1/out_scale overflows
     # no steps: exactly sg_gemm (its own validation)
     assert gx(None, A=NUL) == -7
     assert gx(E(None, 0, 0, -1, 1.0), ldc=1) == -13
