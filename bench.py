@@ -388,6 +388,118 @@ def pmc_summarize(fetch_csv, write_csv):
     print(json.dumps(res, indent=1))
 
 
+SWIGLU_COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_swiglu_kernels.md")
+# (label, dtype, M, N, K) of the SwiGLU workloads the counter probe runs
+SWIGLU_PROBES = [("e4m3 SwiGLU M=1", "e4m3", 1, 11008, 4096),
+                 ("e4m3 SwiGLU M=16", "e4m3", 16, 11008, 4096),
+                 ("bf16 SwiGLU M=2048", "bf16", 2048, 4864, 896)]
+
+
+def pmc_probe_swiglu():
+    """Run under rocprofv3 --pmc: the calibration copy of pmc_probe, then each SwiGLU
+    workload of SWIGLU_PROBES three times, every launch on a fresh copy of W_fused
+    (weights in HBM, as in the cold timing), torch's sleep kernel between workloads."""
+    import torch
+    import swiglu_gemm_amd as sg
+    from swiglu_gemm_amd import inputs
+    sg.lib()
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for label, dt, M, N, K in SWIGLU_PROBES:
+        pb = inputs.swiglu_problem(4 if dt == "bf16" else 5, M, N, K, dt)
+        A = to_dev(pb["A"], dt, torch)
+        W0 = sg.interleave_gate_up(to_dev(pb["W1"], dt, torch), to_dev(pb["W2"], dt, torch))
+        Ws = [W0.clone() for _ in range(3)]
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        flush = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        for W in Ws:
+            flush.fill_(0.0)                     # evicts W from the last-level cache
+            torch.cuda.synchronize()
+            sg.swiglu_gemm(A, W, Y, pb["scale_a"], pb["scale_w"])
+            torch.cuda.synchronize()
+        torch.cuda._sleep(2000000)
+        torch.cuda.synchronize()
+        del Ws, W0, flush
+
+
+def pmc_swiglu_summarize(fetch_csv, write_csv, sq_csv):
+    """Per-launch HBM bytes (FETCH_SIZE / WRITE_SIZE, calibrated by the copy as in
+    pmc_summarize) and SQ counters of the SwiGLU kernels of a --pmc-probe-swiglu run
+    set; writes SWIGLU_COUNTERS_FILE."""
+    def dispatches(path):
+        rows = list(csv.DictReader(open(path)))
+        agg = {}
+        for r in rows:
+            key = int(r["Dispatch_Id"])
+            d = agg.setdefault(key, {"name": r["Kernel_Name"], "t0": int(r["Start_Timestamp"]),
+                                     "t1": int(r["End_Timestamp"]),
+                                     "grid": int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [agg[k] for k in sorted(agg)]
+
+    def swiglu_launches(ds):
+        # the SwiGLU kernels in launch order, three per workload
+        ks = [d for d in ds if "sg::gemm_dma_kernel" in d["name"] or "sg::decode" in d["name"]]
+        if len(ks) != 3 * len(SWIGLU_PROBES):
+            raise SystemExit("expected %d SwiGLU launches, found %d" % (3 * len(SWIGLU_PROBES),
+                                                                       len(ks)))
+        return [ks[3 * i:3 * i + 3] for i in range(len(SWIGLU_PROBES))]
+
+    fd, wd, sd = dispatches(fetch_csv), dispatches(write_csv), dispatches(sq_csv)
+    scale = {}
+    for counter, ds in (("FETCH_SIZE", fd), ("WRITE_SIZE", wd)):
+        copy = [d[counter] for d in ds if "copybuffer" in d["name"].lower()]
+        scale[counter] = COPY_BYTES / (max(copy) * 1024.0)
+    lines = ["# Counters of the fused SwiGLU kernels (HBM bytes, MFMA busy, LDS), one MI355X", "",
+             "Commands (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`),",
+             "one counter set per run:", "", "```",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/f -o f -- "
+             "python <repo>/bench.py --pmc-probe-swiglu",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/w -o w -- "
+             "python <repo>/bench.py --pmc-probe-swiglu",
+             "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES "
+             "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT --output-format csv -d <out>/s -o s -- "
+             "python <repo>/bench.py --pmc-probe-swiglu",
+             "python bench.py --pmc-swiglu-summarize <out>/f/f_counter_collection.csv "
+             "<out>/w/w_counter_collection.csv <out>/s/s_counter_collection.csv", "```", "",
+             "Each launch reads a fresh copy of W_fused after a 512 MiB fill (weights in HBM). HBM "
+             "bytes = counter KiB x the factor that maps the counter of a 512 MiB device copy in the "
+             "same run onto its bytes (FETCH_SIZE x%.2f, WRITE_SIZE x%.2f). Algorithmic bytes = A + "
+             "W_fused + Y. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs "
+             "x 4 SIMDs). Means of the three launches."
+             % (scale["FETCH_SIZE"], scale["WRITE_SIZE"]), "",
+             "Durations under counter collection are longer than in normal runs (the unprofiled "
+             "kernel times are in the bench line and bench_default_kernel_stats.md), so rates are "
+             "not derived from them; the clock is not given for these short launches (the "
+             "GRBM-based estimate is not meaningful below ~100 us); MFMA busy shares that "
+             "denominator and so understates them.", "",
+             "| workload | kernel | HBM read MB | HBM write MB | algorithmic MB | read / algorithmic | "
+             "MFMA busy | LDS bank-conflict cycles per work-group |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (label, dt, M, N, K), f3, w3, s3 in zip(SWIGLU_PROBES, swiglu_launches(fd),
+                                               swiglu_launches(wd), swiglu_launches(sd)):
+        esz = 1 if dt == "e4m3" else 2
+        alg = (M * K + K * 2 * N) * esz + M * N * 2
+        rd = sum(d["FETCH_SIZE"] for d in f3) / 3 * 1024 * scale["FETCH_SIZE"]
+        wr = sum(d["WRITE_SIZE"] for d in w3) / 3 * 1024 * scale["WRITE_SIZE"]
+        grbm = sum(d["GRBM_GUI_ACTIVE"] for d in s3) / 3
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in s3) / 3 / (grbm / 8 * 256 * 4)
+        conf = sum(d["SQ_LDS_BANK_CONFLICT"] for d in s3) / 3
+        name = f3[0]["name"].split("(")[0].replace("void ", "").replace("sg::", "")
+        wgs = int(s3[0].get("grid", 0)) or None
+        lines.append("| %s | `%s` | %.1f | %.2f | %.1f | %.3f | %.3f | %s |" % (
+            label, name, rd / 1e6, wr / 1e6, alg / 1e6, rd / alg, busy,
+            "%.0f" % (conf / wgs) if wgs else "%.0f (total)" % conf))
+    with open(SWIGLU_COUNTERS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 SWEEP_CFGS = (10, 8, 34, 35, 9, 27, 5, 41, 3, 40, 19, 42, 13, 36, 37, 30, 38, 39, 6, 31)
 
 
@@ -727,6 +839,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--pmc-probe", action="store_true")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--pmc-probe-swiglu", action="store_true")
+    ap.add_argument("--pmc-swiglu-summarize", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "SQ_CSV"))
     ap.add_argument("--mfma-ceiling", action="store_true")
     ap.add_argument("--stage-sweep", action="store_true")
     ap.add_argument("--stage-sweep-summarize", nargs=2, metavar=("TRACE_CSV", "SWEEP_JSONL"))
@@ -752,6 +866,12 @@ def main():
         return
     if args.pmc_probe:
         pmc_probe()
+        return
+    if args.pmc_probe_swiglu:
+        pmc_probe_swiglu()
+        return
+    if args.pmc_swiglu_summarize:
+        pmc_swiglu_summarize(*args.pmc_swiglu_summarize)
         return
     if args.mfma_ceiling:
         mfma_ceiling()
