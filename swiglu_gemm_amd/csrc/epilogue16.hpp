@@ -23,9 +23,18 @@
 
 namespace sg {
 
+// two round-to-nearest-even conversions packed into one word (a in the low half):
+// one v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)from_f32<DT>(a) | ((uint32_t)from_f32<DT>(b) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    if constexpr (DT == DT_F16) {
+        typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, h2_t));
+    } else {
+        typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, b2_t));
+    }
 }
 
 // EPI_GEMM_EX: y = act(alpha*acc + beta*C_old + bias[n]), stored in DT or, for an
@@ -258,21 +267,37 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
 // per instruction; here each wave first writes its packed output pairs into a
 // row-major [BM][BN/2] tile in LDS (rows padded by 8 bytes: 32 rows at one column
 // fall on distinct banks), then all threads copy whole 16-byte row pieces out.
+// This runs one 32-row block of every wave at a time (block tm: rows wm*TM + tm*32
+// + 0..31 of each wave row wm), so the stores of a block drain while the next
+// block's SiLU is computed; each block has its own rows of the staged tile, and
+// the barrier between blocks orders LDS only.
 // Called by every thread of the work-group after the main loop (LDS is free once
 // every wave passed the barrier at the top).  W12: the tile's B columns were BN/2
 // of W1 then BN/2 of W2, so gate and up of one output sit at the same register of
 // fragments tn and tn + FN/2, and cb is the wave's first output column in the tile;
-// otherwise cb is its first fused column (outputs at half of it).
-template <int DT, int FM, int FN, int BM, int BN, int NT, bool W12>
+// otherwise cb is its first fused column (outputs at half of it).  SCALED: the
+// inputs were e4m3 and gate and up are multiplied by s = sA*sW first; 16-bit
+// inputs always have s = 1 (the C ABI rejects other scales for them).
+template <bool SCALED>
+__device__ __forceinline__ float swiglu_pair(float g, float u, float s) {
+    return SCALED ? silu(s * g) * (s * u) : silu(g) * u;
+}
+
+template <int DT, int FM, int FN, int BM, int BN, int NT, bool W12, bool SCALED>
 __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
                                                     f32x16 (&acc)[FN][FM], char* smem, int m0,
                                                     int n0, int rb, int cb, int lane) {
     constexpr int ROW = BN + 8;        // bytes per staged row: BN/2 outputs of 2 bytes + pad
     constexpr int CPR = BN / 16;       // 16-byte pieces (8 outputs) per row
+    constexpr int WMS = BM / (32 * FM);            // wave rows of the tile
+    constexpr int PB = WMS * 32 * CPR;             // pieces per 32-row block
     static_assert(BN % 16 == 0, "whole 16-byte row pieces");
-    __syncthreads();
     const int lm = lane & 31, lq = (lane >> 5) * 4;
     const float s = p.alpha;
+    uint16_t* Y = reinterpret_cast<uint16_t*>(p.C);
+    const int nout = p.N >> 1, o0 = n0 >> 1;
+    const bool v16 = (p.epi_flags & EPI_Y16) != 0;
+    __syncthreads();
 #pragma unroll
     for (int tm = 0; tm < FM; ++tm) {
         char* row = smem + (rb + tm * 32 + lm) * ROW;
@@ -286,8 +311,8 @@ __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
                     float y[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        y[e] = silu(s * acc[tn][tm][4 * g + e]) *
-                               (s * acc[tn + FN / 2][tm][4 * g + e]);
+                        y[e] = swiglu_pair<SCALED>(acc[tn][tm][4 * g + e],
+                                                   acc[tn + FN / 2][tm][4 * g + e], s);
                     *reinterpret_cast<u32x2*>(row + 2 * c) =
                         u32x2{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
                 }
@@ -300,34 +325,32 @@ __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
                     // fused columns c..c+3 hold two (gate, up) pairs -> outputs c/2,
                     // c/2+1, at byte offset c of the staged row
                     const int c = cb + tn * 32 + 8 * g + lq;
-                    const float y0 =
-                        silu(s * acc[tn][tm][4 * g]) * (s * acc[tn][tm][4 * g + 1]);
+                    const float y0 = swiglu_pair<SCALED>(acc[tn][tm][4 * g], acc[tn][tm][4 * g + 1], s);
                     const float y1 =
-                        silu(s * acc[tn][tm][4 * g + 2]) * (s * acc[tn][tm][4 * g + 3]);
+                        swiglu_pair<SCALED>(acc[tn][tm][4 * g + 2], acc[tn][tm][4 * g + 3], s);
                     *reinterpret_cast<uint32_t*>(row + c) = pack2<DT>(y0, y1);
                 }
             }
         }
-    }
-    __syncthreads();
-    uint16_t* Y = reinterpret_cast<uint16_t*>(p.C);
-    const int nout = p.N >> 1, o0 = n0 >> 1;
-    const bool v16 = (p.epi_flags & EPI_Y16) != 0;
-    for (int idx = threadIdx.x; idx < BM * CPR; idx += NT) {
-        const int r = idx / CPR, c = idx - r * CPR;
-        const int m = m0 + r, o = o0 + c * 8;
-        if (m >= p.M || o >= nout) continue;
-        const char* src = smem + r * ROW + c * 16;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-        uint16_t* y = Y + (int64_t)m * nout + o;
-        if (v16 && o + 8 <= nout) {
-            *reinterpret_cast<u32x4*>(y) = u32x4{lo.x, lo.y, hi.x, hi.y};
-        } else {
-            const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+        __syncthreads();
+        // piece i of block tm: wave row i / (32 CPR), row (i / CPR) % 32 of its block
+        for (int i = threadIdx.x; i < PB; i += NT) {
+            const int rr = i / CPR, c = i - rr * CPR;
+            const int r = (rr >> 5) * (32 * FM) + tm * 32 + (rr & 31);
+            const int m = m0 + r, o = o0 + c * 8;
+            if (m >= p.M || o >= nout) continue;
+            const char* src = smem + r * ROW + c * 16;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
+            uint16_t* y = Y + (int64_t)m * nout + o;
+            if (v16 && o + 8 <= nout) {
+                *reinterpret_cast<u32x4*>(y) = u32x4{lo.x, lo.y, hi.x, hi.y};
+            } else {
+                const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (o + e < nout) y[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                for (int e = 0; e < 8; ++e)
+                    if (o + e < nout) y[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            }
         }
     }
 }

@@ -327,7 +327,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
 
     if constexpr (EPI == EPI_SWIGLU || W12) {
         static_assert(BM * (BN + 8) <= S * STAGE, "staged SwiGLU tile fits the LDS ring");
-        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN, W12>(
+        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN, W12, DT == DT_E4M3>(
             p, acc, smem, m0, n0, wm * TM, W12 ? wn * (TN / 2) : wn * TN, lane);
     } else if constexpr (EPI == EPI_GEMM_EX) {
         static_assert(S * STAGE >= NW * 32 * 36 * 4, "EX staging fits the LDS ring");

@@ -185,8 +185,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(const Gemm16Params p_) 
 
     if constexpr (EPI == EPI_SWIGLU) {
         static_assert(BM * (BN + 8) <= S * STAGE, "staged SwiGLU tile fits the LDS ring");
-        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 512, false>(p, acc, smem, m0, n0, wm * TM,
-                                                                     wn * TN, lane);
+        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 512, false, DT == DT_E4M3>(
+            p, acc, smem, m0, n0, wm * TM, wn * TN, lane);
     } else if constexpr (EPI == EPI_GEMM_EX) {
         static_assert(S * STAGE >= 8 * 32 * 36 * 4, "EX staging fits the LDS ring");
         __syncthreads();

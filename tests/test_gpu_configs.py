@@ -33,6 +33,54 @@ def forced(cfg, splits=0):
     os.environ["SG_FORCE_CONFIG"] = "%d,%d" % (cfg, splits)
 
 
+def rne16(x, dtype):
+    """Round-to-nearest-even 16-bit codes of float64 values that are exact in fp32
+    (numpy's half conversion; torch's CPU float -> bfloat16 cast)."""
+    if dtype == "f16":
+        return np.asarray(x).astype(np.float16).view(np.uint16)
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("cfg", CFGS16)
+def test_output_rounding_bit_exact(cfg, dtype):
+    """A holds one nonzero per row, so every output is a single product that the fp32
+    accumulator holds exactly: the stored code must be its round-to-nearest-even
+    16-bit code, bit for bit -- ties (checked to occur), fp16 subnormals, signs.
+    beta = 0 with NaN in C: the old C is not read."""
+    import swiglu_gemm_amd as sg
+    M, N, K = 512, 256, 64
+    gen = np.random.default_rng(900 + cfg)
+    a = gen.standard_normal(M) * np.where(gen.random(M) < 0.25, 1e-3, 1.0)
+    A = np.zeros((M, K))
+    A[np.arange(M), np.arange(M) % K] = a
+    B = gen.standard_normal((K, N))
+    A_bits, B_bits = rne16(A, dtype), rne16(B, dtype)
+    C_bits = np.full((M, N), 0x7E00 if dtype == "f16" else 0x7FC0, dtype=np.uint16)
+    ref = oracle.gemm("N", "N", M, N, K, 1.0, A_bits, K, B_bits, N, 0.0, C_bits, N, dtype)
+    r32 = ref.astype(np.float32)                       # exact: one 16-bit product
+    up = rne16(np.nextafter(r32, np.float32(np.inf)), dtype)
+    down = rne16(np.nextafter(r32, np.float32(-np.inf)), dtype)
+    assert np.count_nonzero((up != down) & (ref != 0)) > 0, "no rounding ties in the case"
+    C = to_dev(C_bits, dtype)
+    forced(cfg, 1)
+    print("rounding cfg %d %s" % (cfg, dtype), flush=True)
+    try:
+        sg.gemm(to_dev(A_bits, dtype), to_dev(B_bits, dtype), C, alpha=1.0, beta=0.0,
+                dtype={"f16": 1, "bf16": 2}[dtype])
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    got = from_dev(C)
+    want = rne16(ref, dtype)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "%s: %d codes differ, first at %s: got %#06x want %#06x (%r)" % (
+        desc, len(bad), bad[0], got[tuple(bad[0])], want[tuple(bad[0])], ref[tuple(bad[0])])
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("tr", TRANS)
 @pytest.mark.parametrize("cfg", CFGS16)
