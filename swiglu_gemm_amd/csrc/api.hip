@@ -191,16 +191,22 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
         cfg = -1;   // a forced id of the other operand width is ignored entirely
         splits = 0;
         if (e4m3) {
-            // measured on MI355X: 256x256 tiles once there are >= 2 full rounds of
-            // them; from M = 256, 128x256 tiles while they fit one round (the weights
-            // stream from HBM once, with a 3-deep ring), else 128x128; below, 32-row
-            // tiles (256 wide when that still gives half a round)
+            // measured on MI355X (SwiGLU, fused width 22016, K = 4096, weights cold
+            // in HBM): 256x256 tiles once there are >= 2 full rounds of them, and
+            // above 256 rows while they fill between half and all of one round
+            // (M = 384, 512: 57, 59 us against 62, 72 us for 128x128); above 128
+            // rows, 128x256 tiles while they fit one round (the weights stream from
+            // HBM once, with a 3-deep ring; M = 192: 39 us against 52 us for 32-row
+            // tiles), else 128x128; up to 128 rows, 32-row tiles (256 wide when
+            // that still gives half a round)
             const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
             const int64_t mid = cdiv(q.M, 128) * cdiv(q.N, 256);
-            cfg = big >= 2 * kNumCU
-                      ? 14
-                      : (q.M >= 256 ? (mid <= kNumCU ? 33 : 15)
-                                    : (cdiv(q.N, 256) >= 128 ? 16 : 17));
+            if (big >= 2 * kNumCU || (q.M > 256 && big <= kNumCU && 2 * big > kNumCU))
+                cfg = 14;
+            else if (q.M > 128)
+                cfg = mid <= kNumCU ? 33 : 15;
+            else
+                cfg = cdiv(q.N, 256) >= 128 ? 16 : 17;
         } else {
             double best = 0.0;
             for (const Cand16& cand : kCand16) {
