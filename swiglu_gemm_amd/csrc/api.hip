@@ -281,6 +281,41 @@ int ex_cfg(int cfg, const Problem16& q, int64_t kps) {
     return alt;
 }
 
+// Column split of a problem whose 256-row tiles take more than one round and
+// leave the last round at most half full: the chosen tile runs over the leading
+// columns that fill whole rounds and the 128 x 128 tile (two work-groups per CU)
+// over the remaining column strip -- two launches with disjoint outputs.  Measured
+// on MI355X: e4m3 4096 x 22016 x 4096 with 256 x 256 tiles (5.4 rounds) 394-423 us
+// in one launch, 375-378 us split at column 20480.  Not for split-K, batches, the
+// extra epilogue steps or a forced configuration.
+struct ColSplit {
+    int64_t n1 = 0;      // columns of the first launch (0: no split)
+    int cfg_tail = -1;
+};
+
+ColSplit plan_col_split(const Problem16& q, int cfg, int splits, int epi) {
+    ColSplit s;
+    int fc = -1, fs = 0;
+    if (splits > 1 || q.batch > 1 || (epi != EPI_GEMM && epi != EPI_SWIGLU) ||
+        forced_config(&fc, &fs))
+        return s;
+    const Cfg16& c = kCfg16[cfg];
+    if (c.BM < 256) return s;
+    const int64_t tm = cdiv(q.M, c.BM), tn = cdiv(q.N, c.BN), rest = (tm * tn) % kNumCU;
+    if (tm * tn <= kNumCU || rest == 0 || 2 * rest > kNumCU) return s;
+    const int64_t strip = cdiv(rest, tm);                // column tiles moved to the tail
+    if (strip >= tn) return s;
+    const int tail = q.esz == 1 ? 15 : 13;
+    const Cfg16& t = kCfg16[tail];
+    Problem16 qt = q;
+    qt.N = q.N - (tn - strip) * c.BN;
+    if (!dma_ok(t, qt, split_len(q.K, 1, t.BK))) return s;
+    if (cdiv(q.M, t.BM) * cdiv(qt.N, t.BN) > 2 * kNumCU) return s;   // one go, 2 per CU
+    s.n1 = (tn - strip) * c.BN;
+    s.cfg_tail = tail;
+    return s;
+}
+
 template <int DT>
 hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* out,
                  bool out_vec, const char* what, hipStream_t st, int* splits_used) {
@@ -304,6 +339,28 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
         p.C = out;
         p.vec_c = out_vec;
         p.k_per_split = (int)split_len(q.K, 1, c.BK);
+        const ColSplit cs = plan_col_split(q, cfg, splits, epi);
+        if (cs.n1 > 0) {
+            const Cfg16& t = kCfg16[cs.cfg_tail];
+            Gemm16Params pt = p;
+            p.N = (int)cs.n1;
+            p.tiles_n = (int)cdiv(cs.n1, c.BN);
+            pt.N = (int)(q.N - cs.n1);
+            pt.tiles_m = (int)cdiv(q.M, t.BM);
+            pt.tiles_n = (int)cdiv(pt.N, t.BN);
+            pt.k_per_split = (int)split_len(q.K, 1, t.BK);
+            // column n1 of op(B): element n1 of each row ('N') or row n1 ('T'); C (or
+            // Y, one output per fused column pair) holds 16-bit elements
+            const int64_t boff = (tb ? cs.n1 * p.ldb : cs.n1) * q.esz;
+            pt.B = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(p.B) + boff);
+            pt.C = static_cast<char*>(out) + (epi == EPI_SWIGLU ? cs.n1 / 2 : cs.n1) * 2;
+            std::snprintf(g_last_cfg, sizeof(g_last_cfg),
+                          "%s cfg=%d %s splits=1 columns 0..%lld, tail cfg=%d %s", what, cfg,
+                          c.name, (long long)cs.n1, cs.cfg_tail, t.name);
+            hipError_t e = launch16_dt<DT>(ta, tb, epi, cfg, p, 1, st);
+            if (e != hipSuccess) return e;
+            return launch16_dt<DT>(ta, tb, epi, cs.cfg_tail, pt, 1, st);
+        }
         set_last(what, cfg, 1);
         return launch16_dt<DT>(ta, tb, epi, cfg, p, 1, st);
     }

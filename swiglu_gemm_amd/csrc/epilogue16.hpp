@@ -211,7 +211,7 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int n = ob + q * 32 + 8 * g + lq;
-                        uint16_t* y = Y + (int64_t)m * nout + n;
+                        uint16_t* y = Y + (int64_t)m * p.ldc + n;
                         float v[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -342,7 +342,7 @@ __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
             const char* src = smem + r * ROW + c * 16;
             const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
             const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-            uint16_t* y = Y + (int64_t)m * nout + o;
+            uint16_t* y = Y + (int64_t)m * p.ldc + o;
             if (v16 && o + 8 <= nout) {
                 *reinterpret_cast<u32x4*>(y) = u32x4{lo.x, lo.y, hi.x, hi.y};
             } else {

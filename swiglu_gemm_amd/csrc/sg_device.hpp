@@ -152,7 +152,7 @@ struct Gemm16Params {
     const uint16_t* B;   // EPI_SWIGLU_W12: W1
     const uint16_t* B2;  // EPI_SWIGLU_W12: W2 (same shape and ld as W1)
     void* C;            // EPI_GEMM: C (dtype); EPI_SWIGLU(_W12): Y; EPI_PARTIAL: fp32 workspace
-    int64_t lda, ldb, ldc;
+    int64_t lda, ldb, ldc;   // SwiGLU: ldc is the row stride of Y (in outputs)
     int M, N, K;        // N is the fused width 2*N_out for SwiGLU (both forms) / partials
     float alpha, beta;  // SwiGLU: alpha = scale_a * scale_w
     int vec_a, vec_b, vec_c;

@@ -1,0 +1,98 @@
+"""The column split: a problem whose 256-row tiles take more than one round of the
+CUs and leave the last round at most half full runs as two launches -- the chosen
+tile over the leading columns that fill whole rounds, the 128 x 128 tile over the
+remaining column strip.  GEMM (B stored K x N and N x K, 16-bit and e4m3 operands,
+alpha and beta) and the fused SwiGLU against the fp64 oracle on sampled rows with
+every column (both launches and the seam between them), the routing itself, and no
+split under a forced configuration."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from swiglu_gemm_amd import inputs
+from helpers import assert_close, from_dev, gemm_oracle_rows, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# (dtype, M, N, K): 256-row tiles leave a last round 1/16 (e4m3, 256 x 256 tiles:
+# 16 x 33 = 528) or 3/8 (bf16, 256 x 320 tiles: 32 x 27 = 864) full
+SHAPES = {"bf16": (8192, 8448, 256), "e4m3": (4096, 8448, 256)}
+SEAM = {"bf16": 7680, "e4m3": 8192}     # first column of the tail launch
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import swiglu_gemm_amd as sg
+    sg.lib()
+    yield
+    os.environ.pop("SG_FORCE_CONFIG", None)
+
+
+def sample_rows(M, seed):
+    gen = np.random.default_rng(seed)
+    return sorted(set([0, 1, 127, 128, 255, 256, M // 2, M - 1] +
+                      list(gen.integers(0, M, size=8))))
+
+
+def run_gemm(dtype, tb, forced=None):
+    import swiglu_gemm_amd as sg
+    M, N, K = SHAPES[dtype]
+    od = "bf16"
+    p = inputs.gemm_problem(300, "N", tb, M, N, K, dtype, "normal", ld_mode="tight", c_dtype=od)
+    alpha = 0.7 * (p["scale_a"] * p["scale_b"] if dtype == "e4m3" else 1.0)
+    A, B, C = to_dev(p["A"], dtype), to_dev(p["B"], dtype), to_dev(p["C"], od)
+    if forced:
+        os.environ["SG_FORCE_CONFIG"] = forced
+    print("colsplit gemm %s N%s M=%d N=%d K=%d forced=%s" % (dtype, tb, M, N, K, forced),
+          flush=True)
+    try:
+        sg.gemm(A, B, C, alpha=alpha, beta=0.3, transA="N", transB=tb,
+                dtype={"bf16": 2, "e4m3": 3}[dtype])
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    rows = sample_rows(M, 7)
+    ref = gemm_oracle_rows(rows, p, "N", tb, M, N, K, alpha, 0.3, dtype)
+    got = oracle.decode(from_dev(C), od)[rows, :]
+    assert_close(got, ref, dtype, K, desc)
+    return desc
+
+
+@pytest.mark.parametrize("tb", ["N", "T"])
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_gemm_column_split(dtype, tb):
+    desc = run_gemm(dtype, tb)
+    assert "tail cfg=" in desc and "columns 0..%d," % SEAM[dtype] in desc, desc
+
+
+def test_forced_config_is_not_split():
+    desc = run_gemm("bf16", "N", forced="24,1")
+    assert "tail" not in desc and "cfg=24 " in desc, desc
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_swiglu_column_split(dtype):
+    import swiglu_gemm_amd as sg
+    M, N2, K = SHAPES[dtype]
+    N = N2 // 2
+    pb = inputs.swiglu_problem(310, M, N, K, dtype)
+    Wf = oracle.interleave(pb["W1"], pb["W2"])
+    A, W = to_dev(pb["A"], dtype), to_dev(Wf, dtype)
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    sa, sw = pb.get("scale_a", 1.0), pb.get("scale_w", 1.0)
+    print("colsplit swiglu %s M=%d N=%d K=%d" % (dtype, M, N, K), flush=True)
+    sg.swiglu_gemm(A, W, Y, sa, sw)
+    torch.cuda.synchronize()
+    desc = sg.last_config()
+    assert "tail cfg=" in desc and "columns 0..%d," % SEAM[dtype] in desc, desc
+    got = oracle.decode(from_dev(Y), "bf16")
+    assert np.all(np.isfinite(got)), desc           # every output written
+    rows = sample_rows(M, 8)
+    ref = oracle.swiglu(len(rows), N, K, pb["A"][rows, :], Wf, dtype, sa, sw)
+    assert_close(got[rows, :], ref, dtype, K, desc)
