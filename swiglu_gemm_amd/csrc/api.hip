@@ -164,19 +164,26 @@ int pick_splits(const Cfg16& c, const Problem16& q) {
 // CU on MI355X, random fp16/bf16 data).  A problem takes the eligible candidate
 // with the least  waves * (tile flops / rate + kTileOverheadUs), waves = the
 // number of rounds of one work-group per CU, which weighs tile size (operand
-// re-reads, MFMA efficiency) against the idle CUs of the last round.
+// re-reads, MFMA efficiency) against the idle CUs of the last round; split-K adds
+// the round trip of its fp32 partials and the reduction launch.  (64 x 128 tiles:
+// rate from bf16 512 x 4096 x 4096 NT, one round of 256 tiles in 30.6 us.)
 struct Cand16 {
     int id;
     double tf_per_cu;
 };
-constexpr Cand16 kCand16[] = {{10, 4.7}, {24, 5.0}, {13, 3.6}, {32, 3.6}, {6, 3.4}};
+constexpr Cand16 kCand16[] = {{10, 4.7}, {24, 5.0}, {13, 3.6}, {32, 3.6}, {6, 3.4}, {44, 2.43}};
 constexpr double kTileOverheadUs = 3.0;   // pipeline fill + epilogue per tile
+constexpr double kSplitBytesPerUs = 4e6;  // fp32 partials: written, then read back
+constexpr double kSplitLaunchUs = 5.0;    // the reduction kernel
 
 double est_us(const Cfg16& c, const Problem16& q, int splits, double tf_per_cu) {
     const int64_t items = cdiv(q.M, c.BM) * cdiv(q.N, c.BN) * splits * q.batch;
     const double waves = (double)cdiv(items, kNumCU);
     const double item_flops = 2.0 * c.BM * c.BN * (double)split_len(q.K, splits, c.BK);
-    return waves * (item_flops / (tf_per_cu * 1e6) + kTileOverheadUs);
+    double t = waves * (item_flops / (tf_per_cu * 1e6) + kTileOverheadUs);
+    if (splits > 1)
+        t += 8.0 * splits * (double)q.M * (double)q.N / kSplitBytesPerUs + kSplitLaunchUs;
+    return t;
 }
 
 // Choose a configuration and split count.  16-bit problems fall back to a

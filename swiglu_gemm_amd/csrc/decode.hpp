@@ -47,14 +47,6 @@ struct DecodeParams {
     EpiEx ex;           // EPI_GEMM_EX: bias / activation / e4m3 output
 };
 
-// First unit of work-group w when `units` are dealt to G work-groups.
-__device__ __forceinline__ int sk_start(int w, int units, int G) {
-    return (int)((int64_t)w * units / G);
-}
-// The work-group whose run holds unit u: the largest w with sk_start(w) <= u.
-__device__ __forceinline__ int sk_owner(int u, int units, int G) {
-    return (int)(((int64_t)(u + 1) * G - 1) / units);
-}
 
 // Register epilogue of one column tile t.  Accumulator layout as in epilogue16.hpp:
 // lane l, register r of fragment tn holds row m = l % 32 and tile column

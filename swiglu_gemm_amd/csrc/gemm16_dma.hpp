@@ -200,42 +200,51 @@ __device__ __forceinline__ f32x16 mfma_op(const typename FragT<DT == DT_E4M3 ? 1
     }
 }
 
-// BK is in elements.  Output type: DT for 16-bit operands, bf16 for e4m3.
+// Compile-time shape of the direct-to-LDS kernels.  BK is in elements.  Output
+// type: DT for 16-bit operands, bf16 for e4m3.
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
-__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16Params p_) {
-    const Gemm16Params p = batch_item(p_);
-    constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
-    constexpr int DT_OUT = DT == DT_E4M3 ? DT_BF16 : DT;
-    constexpr int KSTEP = ESZ == 2 ? 16 : 64;
-    using Frag = typename FragT<ESZ>::type;
-    constexpr int NW = WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int KS = BK / KSTEP;
+struct DmaShape {
+    static constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
+    static constexpr int DT_OUT = DT == DT_E4M3 ? DT_BF16 : DT;
+    static constexpr int KSTEP = ESZ == 2 ? 16 : 64;
+    static constexpr int NW = WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int KS = BK / KSTEP;
     static_assert(BK % KSTEP == 0 && KS % 2 == 0, "k-steps per tile must be even");
-    constexpr bool KCA = !TA, KCB = TB;          // k-contiguous operands
+    static constexpr bool KCA = !TA, KCB = TB;          // k-contiguous operands
     // EPI_SWIGLU_W12: the B tile is BN/2 columns of W1 followed by the same BN/2
     // columns of W2; a wave's fragments tn < FN/2 are gate, tn + FN/2 the matching up
-    constexpr bool W12 = EPI == EPI_SWIGLU_W12;
+    static constexpr bool W12 = EPI == EPI_SWIGLU_W12;
     static_assert(!W12 || (!TA && !TB && FN % 2 == 0 && BN % 64 == 0), "split-weight SwiGLU tile");
-    constexpr int BNS = W12 ? BN / 2 : BN;       // columns per B source
-    constexpr int NBS = W12 ? 2 : 1;             // B sources
+    static constexpr int BNS = W12 ? BN / 2 : BN;       // columns per B source
+    static constexpr int NBS = W12 ? 2 : 1;             // B sources
     using TA_ = DmaTile<KCA, BM, BK, ESZ>;
     using TB_ = DmaTile<KCB, BNS, BK, ESZ>;
-    constexpr int STAGE = TA_::BYTES + NBS * TB_::BYTES;
-    static_assert(S * STAGE <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+    static constexpr int STAGE = TA_::BYTES + NBS * TB_::BYTES;
+    static constexpr int LDS = S * STAGE;
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static constexpr int NL =
+        DmaStream<KCA, BM, BK, ESZ, NW>::NI + NBS * DmaStream<KCB, BNS, BK, ESZ, NW>::NI;
+    using Frag = typename FragT<ESZ>::type;
+    using Acc = f32x16[FN][FM];
+};
 
-    const int nblk = p.tiles_m * p.tiles_n;
-    const int lid = xcd_remap(blockIdx.x, nblk);
-    int tmi, tni;
-    tile_coords(lid, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
-    const int m0 = tmi * BM, n0 = tni * BN;
-    const int kbeg = blockIdx.y * p.k_per_split;
-    const int kend = min(p.K, kbeg + p.k_per_split);
-    const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
-
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+// acc += op(A) * op(B) over K tiles [kbeg, kbeg + nkt*BK) of the output tile at
+// (m0, n0): the S-stage direct-to-LDS ring feeding the MFMAs.  Every thread of the
+// work-group calls it; LDS is free on return only after a barrier (the last k-step
+// reads a stage without one).
+template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
+__device__ __forceinline__ void dma_mainloop(
+    const Gemm16Params& p, char* smem, int m0, int n0, int kbeg, int nkt,
+    typename DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>::Acc& acc, int wave, int lane) {
+    using D = DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>;
+    constexpr int ESZ = D::ESZ, FM = D::FM, FN = D::FN, KS = D::KS, TM = D::TM, TN = D::TN;
+    constexpr bool KCA = D::KCA, KCB = D::KCB, W12 = D::W12;
+    constexpr int BNS = D::BNS, NW = D::NW, STAGE = D::STAGE, NL = D::NL;
+    using TA_ = typename D::TA_;
+    using TB_ = typename D::TB_;
+    using Frag = typename D::Frag;
     const int wm = wave % WM, wn = wave / WM;
 
     DmaStream<KCA, BM, BK, ESZ, NW> da;
@@ -247,16 +256,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
     } else {
         db.init(p.B, p.ldb, n0, p.N, kbeg, wave, lane);
     }
-    constexpr int NL =
-        DmaStream<KCA, BM, BK, ESZ, NW>::NI + NBS * DmaStream<KCB, BNS, BK, ESZ, NW>::NI;
-
-    f32x16 acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     Frag fa[2][FM], fb[2][FN];
     auto read_all = [&](const char* st, int s, Frag (&af)[FM], Frag (&bf)[FN]) {
@@ -324,19 +323,57 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+}
 
+// The epilogue of one finished output tile (every thread of the work-group).
+template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
+__device__ __forceinline__ void dma_epilogue(
+    const Gemm16Params& p, typename DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>::Acc& acc,
+    char* smem, int m0, int n0, int wave, int lane) {
+    using D = DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>;
+    constexpr int DT_OUT = D::DT_OUT, FM = D::FM, FN = D::FN, TM = D::TM, TN = D::TN;
+    constexpr bool W12 = D::W12;
+    const int wm = wave % WM, wn = wave / WM;
     if constexpr (EPI == EPI_SWIGLU || W12) {
-        static_assert(BM * (BN + 8) <= S * STAGE, "staged SwiGLU tile fits the LDS ring");
+        static_assert(BM * (BN + 8) <= D::LDS, "staged SwiGLU tile fits the LDS ring");
         epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN, W12, DT == DT_E4M3>(
             p, acc, smem, m0, n0, wm * TM, W12 ? wn * (TN / 2) : wn * TN, lane);
     } else if constexpr (EPI == EPI_GEMM_EX) {
-        static_assert(S * STAGE >= NW * 32 * 36 * 4, "EX staging fits the LDS ring");
+        static_assert(D::LDS >= D::NW * 32 * 36 * 4, "EX staging fits the LDS ring");
         __syncthreads();
         epilogue_gemm_ex_lds<DT_OUT, FM, FN>(p, acc, smem, m0 + wm * TM, n0 + wn * TN, wave, lane);
     } else {
         epilogue16<DT_OUT, EPI, FM, FN>(p, acc, m0, n0, BM, BN, m0 + wm * TM, n0 + wn * TN,
                                         lane);
     }
+}
+
+template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16Params p_) {
+    using D = DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>;
+    const Gemm16Params p = batch_item(p_);
+    __shared__ __attribute__((aligned(1024))) char smem[D::LDS];
+
+    const int nblk = p.tiles_m * p.tiles_n;
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    int tmi, tni;
+    tile_coords(lid, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+    const int kbeg = blockIdx.y * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+
+    typename D::Acc acc;
+#pragma unroll
+    for (int i = 0; i < D::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < D::FM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    dma_mainloop<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, smem, m0, n0, kbeg, nkt, acc, wave,
+                                                         lane);
+    dma_epilogue<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, acc, smem, m0, n0, wave, lane);
 }
 
 }  // namespace sg

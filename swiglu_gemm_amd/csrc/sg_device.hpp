@@ -189,6 +189,15 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// First unit of work-group w when `units` are dealt to G work-groups.
+__device__ __forceinline__ int sk_start(int w, int units, int G) {
+    return (int)((int64_t)w * units / G);
+}
+// The work-group whose run holds unit u: the largest w with sk_start(w) <= u.
+__device__ __forceinline__ int sk_owner(int u, int units, int G) {
+    return (int)(((int64_t)(u + 1) * G - 1) / units);
+}
+
 // Grouped ("super-tile") order: walk GROUP_M tile-rows at a time so the tiles in
 // flight share A rows and B columns.
 __device__ __forceinline__ void tile_coords(int lid, int tiles_m, int tiles_n, int group_m,
