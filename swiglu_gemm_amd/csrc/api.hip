@@ -217,6 +217,9 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
         } else {
             double best = 0.0;
             for (const Cand16& cand : kCand16) {
+                // up to 32 rows the decode kernels stream the weight once wherever
+                // this model asks for split-K (measured against the decode path)
+                if (cand.id == 44 && q.M <= 32) continue;
                 const Cfg16& c = kCfg16[cand.id];
                 const int sp = pick_splits(c, q);
                 if (!dma_ok(c, q, split_len(q.K, sp, c.BK))) continue;
