@@ -392,6 +392,8 @@ SWIGLU_COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_swiglu_kernels.m
 # (label, dtype, M, N, K) of the SwiGLU workloads the counter probe runs
 SWIGLU_PROBES = [("e4m3 SwiGLU M=1", "e4m3", 1, 11008, 4096),
                  ("e4m3 SwiGLU M=16", "e4m3", 16, 11008, 4096),
+                 ("e4m3 SwiGLU M=256", "e4m3", 256, 11008, 4096),
+                 ("bf16 SwiGLU M=512", "bf16", 512, 4864, 896),
                  ("bf16 SwiGLU M=2048", "bf16", 2048, 4864, 896)]
 
 

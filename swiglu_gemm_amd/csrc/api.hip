@@ -198,20 +198,26 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
         cfg = -1;   // a forced id of the other operand width is ignored entirely
         splits = 0;
         if (e4m3) {
-            // measured on MI355X (SwiGLU, fused width 22016, K = 4096, weights cold
-            // in HBM): 256x256 tiles once there are >= 2 full rounds of them, and
-            // above 256 rows while they fill between half and all of one round
-            // (M = 384, 512: 57, 59 us against 62, 72 us for 128x128); above 128
-            // rows, 128x256 tiles while they fit one round (the weights stream from
-            // HBM once, with a 3-deep ring; M = 192: 39 us against 52 us for 32-row
-            // tiles), else 128x128; up to 128 rows, 32-row tiles (256 wide when
-            // that still gives half a round)
+            // measured on MI355X (weights cold in HBM; these shapes are bound by how
+            // fast each CU pulls its operand tiles, so more busy CUs and waves win):
+            // 256x256 tiles once there are >= 2 full rounds of them, and above 256 rows
+            // while they fill between half and all of one round (SwiGLU, fused width
+            // 22016, K = 4096, M = 384, 512: 57, 59 us against 62, 72 us for 128x128);
+            // 32-row tiles while two work-groups per CU hold them all (GEMM 256 x 4096
+            // x 4096: 14.3 us against 24.8 us for 128x256 with split-K); above 128
+            // rows, 8-wave 128x256 tiles while they fit one round (SwiGLU M = 192, 256:
+            // 34, 36 us against 40, 39 us with 4 waves and 52 us with 32-row tiles),
+            // else 128x128; up to 128 rows, 32-row tiles (256 wide when that still
+            // gives half a round)
             const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
             const int64_t mid = cdiv(q.M, 128) * cdiv(q.N, 256);
+            const int64_t thin = cdiv(q.M, 32) * cdiv(q.N, 128);
             if (big >= 2 * kNumCU || (q.M > 256 && big <= kNumCU && 2 * big > kNumCU))
                 cfg = 14;
+            else if (q.M > 128 && thin <= 2 * kNumCU)
+                cfg = 17;
             else if (q.M > 128)
-                cfg = mid <= kNumCU ? 33 : 15;
+                cfg = mid <= kNumCU ? 45 : 15;
             else
                 cfg = cdiv(q.N, 256) >= 128 ? 16 : 17;
         } else {
@@ -638,7 +644,7 @@ int choose_w12(const Problem16& q_out) {
         return w12_cfg_ok(kCfg16[cfg], q_out) ? cfg : -1;
     if (e4m3) {
         const int64_t big = cdiv(q2.M, 256) * cdiv(q2.N, 256);
-        cfg = big >= 2 * kNumCU ? 14 : (q_out.M >= 256 ? 33 : 16);
+        cfg = big >= 2 * kNumCU ? 14 : (q_out.M >= 256 ? 45 : 16);
         return w12_cfg_ok(kCfg16[cfg], q_out) ? cfg : -1;
     }
     cfg = -1;

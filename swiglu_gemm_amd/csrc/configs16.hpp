@@ -63,6 +63,7 @@ constexpr Cfg16 kCfg16[] = {
     // 64-row tiles: twice the work-groups of 128-row tiles for 65..128-row problems
     {0, 1, 64, 256, 64, 3, 1, 4, "dma 64x256x64 s3 1x4w"},
     {0, 1, 64, 128, 64, 4, 1, 4, "dma 64x128x64 s4 1x4w"},
+    {1, 1, 128, 256, 128, 3, 2, 4, "e4m3 dma 128x256x128 s3 2x4w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
@@ -152,6 +153,7 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(17, 1, 32, 128, 128, 4, 1, 4)    \
     X(21, 2, 256, 256, 128, 2, 4, 2)   \
     X(23, 2, 128, 256, 128, 2, 2, 4)   \
-    X(33, 1, 128, 256, 128, 3, 2, 2)
+    X(33, 1, 128, 256, 128, 3, 2, 2)   \
+    X(45, 1, 128, 256, 128, 3, 2, 4)
 
 }  // namespace sg

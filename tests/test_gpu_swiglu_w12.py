@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 W12_CFGS16 = [10, 8, 32, 6, 43]  # configurations that can take separate weights
-W12_CFGS8 = [14, 16, 33]
+W12_CFGS8 = [14, 16, 33, 45]
 
 
 @pytest.fixture(scope="module", autouse=True)
