@@ -261,6 +261,51 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
     }
 }
 
+// GEMM epilogue (beta = 0, full tile, C 16-byte aligned with ldc a multiple of 8) of the
+// direct-to-LDS kernels: one 32-row block of every wave at a time is rounded to the
+// output type and staged in LDS as rows of the tile (16 bytes of padding per row), then
+// every thread stores whole 16-byte row pieces, consecutive threads covering whole
+// lines, as non-temporal stores.  The block buffer is reused: the barrier before each
+// block's staging follows the previous block's LDS reads (its global stores may still
+// be in flight).  rb: first tile row of the calling wave; cb: its first tile column.
+template <int DT, int FM, int FN, int BM, int BN, int NT>
+__device__ __forceinline__ void epilogue_gemm_rows_lds(const Gemm16Params& p,
+                                                       f32x16 (&acc)[FN][FM], char* smem,
+                                                       int m0, int n0, int rb, int cb,
+                                                       int lane) {
+    constexpr int ROW = 2 * BN + 16;               // bytes per staged row
+    constexpr int CPR = BN / 8;                    // 16-byte pieces (8 outputs) per row
+    constexpr int WMS = BM / (32 * FM);            // wave rows of the tile
+    constexpr int PB = WMS * 32 * CPR;             // pieces per 32-row block
+    const int lm = lane & 31, lq = (lane >> 5) * 4;
+    const int wr = rb / (32 * FM);                 // the calling wave's row of waves
+    const float alpha = p.alpha;
+    uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
+#pragma unroll
+    for (int tm = 0; tm < FM; ++tm) {
+        __syncthreads();
+        char* row = smem + (wr * 32 + lm) * ROW;
+#pragma unroll
+        for (int tn = 0; tn < FN; ++tn)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = cb + tn * 32 + 8 * g + lq;
+                *reinterpret_cast<u32x2*>(row + 2 * c) =
+                    u32x2{pack2<DT>(alpha * acc[tn][tm][4 * g], alpha * acc[tn][tm][4 * g + 1]),
+                          pack2<DT>(alpha * acc[tn][tm][4 * g + 2],
+                                    alpha * acc[tn][tm][4 * g + 3])};
+            }
+        __syncthreads();
+        for (int i = threadIdx.x; i < PB; i += NT) {
+            const int rr = i / CPR, c = i - rr * CPR;
+            const int r = (rr >> 5) * (32 * FM) + tm * 32 + (rr & 31);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rr * ROW + c * 16);
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<u32x4*>(C + (int64_t)(m0 + r) * p.ldc + n0 + c * 8));
+        }
+    }
+}
+
 // SwiGLU epilogue of the direct-to-LDS kernels, staged through LDS so that the
 // global stores run along rows.  In the MFMA accumulator layout a wave holds 32
 // rows x a few columns, so storing from registers touches 32 rows (cache lines)
@@ -270,7 +315,10 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
 // This runs one 32-row block of every wave at a time (block tm: rows wm*TM + tm*32
 // + 0..31 of each wave row wm), so the stores of a block drain while the next
 // block's SiLU is computed; each block has its own rows of the staged tile, and
-// the barrier between blocks orders LDS only.
+// the barrier between blocks orders LDS only.  The 16-byte row pieces are non-temporal stores:
+// whole lines that need no write-combining in L2 (measured: bf16 SwiGLU M = 2048 / 8192
+// 36.5 -> 35.4 us / 140.3 -> 134.7 us; the same hint on the accumulator-layout stores
+// of the GEMM epilogue, 8-byte pieces of 32 rows, made those kernels far slower).
 // Called by every thread of the work-group after the main loop (LDS is free once
 // every wave passed the barrier at the top).  W12: the tile's B columns were BN/2
 // of W1 then BN/2 of W2, so gate and up of one output sit at the same register of
@@ -344,7 +392,9 @@ __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
             const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
             uint16_t* y = Y + (int64_t)m * p.ldc + o;
             if (v16 && o + 8 <= nout) {
-                *reinterpret_cast<u32x4*>(y) = u32x4{lo.x, lo.y, hi.x, hi.y};
+                // whole lines from consecutive threads: streamed past the cache
+                __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y},
+                                            reinterpret_cast<u32x4*>(y));
             } else {
                 const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll

@@ -42,15 +42,12 @@ def rne16(x, dtype):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("cfg", CFGS16)
-def test_output_rounding_bit_exact(cfg, dtype):
+def rounding_case(cfg, dtype, M, N, K):
     """A holds one nonzero per row, so every output is a single product that the fp32
     accumulator holds exactly: the stored code must be its round-to-nearest-even
     16-bit code, bit for bit -- ties (checked to occur), fp16 subnormals, signs.
     beta = 0 with NaN in C: the old C is not read."""
     import swiglu_gemm_amd as sg
-    M, N, K = 512, 256, 64
     gen = np.random.default_rng(900 + cfg)
     a = gen.standard_normal(M) * np.where(gen.random(M) < 0.25, 1e-3, 1.0)
     A = np.zeros((M, K))
@@ -65,7 +62,7 @@ def test_output_rounding_bit_exact(cfg, dtype):
     assert np.count_nonzero((up != down) & (ref != 0)) > 0, "no rounding ties in the case"
     C = to_dev(C_bits, dtype)
     forced(cfg, 1)
-    print("rounding cfg %d %s" % (cfg, dtype), flush=True)
+    print("rounding cfg %d %s M=%d N=%d" % (cfg, dtype, M, N), flush=True)
     try:
         sg.gemm(to_dev(A_bits, dtype), to_dev(B_bits, dtype), C, alpha=1.0, beta=0.0,
                 dtype={"f16": 1, "bf16": 2}[dtype])
@@ -76,6 +73,64 @@ def test_output_rounding_bit_exact(cfg, dtype):
     assert "cfg=%d " % cfg in desc, desc
     got = from_dev(C)
     want = rne16(ref, dtype)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "%s: %d codes differ, first at %s: got %#06x want %#06x (%r)" % (
+        desc, len(bad), bad[0], got[tuple(bad[0])], want[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("cfg", CFGS16)
+def test_output_rounding_bit_exact(cfg, dtype):
+    """A few tiles: the register epilogue."""
+    rounding_case(cfg, dtype, 512, 256, 64)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("cfg", [10, 24, 13, 30, 32, 43, 44, 5, 20])
+def test_output_rounding_bit_exact_many_tiles(cfg, dtype):
+    """More work-groups than one round of the CUs: the row-staged epilogue of the
+    direct-to-LDS kernels (full tiles) next to the register epilogue (edge tiles:
+    N = 4608 is not a multiple of every tile width)."""
+    rounding_case(cfg, dtype, 8192, 4608, 64)
+
+
+@pytest.mark.parametrize("cfg", [14, 15, 17, 33, 45])
+def test_e4m3_output_rounding_bit_exact_many_tiles(cfg):
+    """e4m3 operands, bf16 output: one product per output (A has one nonzero per row)
+    times alpha = 1.0625, exact in fp32 (at most 8 + 5 significant bits) and rounded once
+    to bf16 -- ties occur, where a bare e4m3 product (<= 8 bits) would always be exact --
+    on more work-groups than one round (row-staged epilogue on full tiles, register
+    epilogue on edge tiles)."""
+    import swiglu_gemm_amd as sg
+    M, N, K = 8192, 4608, 128
+    gen = np.random.default_rng(950 + cfg)
+    a = torch.from_numpy(gen.standard_normal(M).astype(np.float32) * 8).to(torch.float8_e4m3fn)
+    A = torch.zeros((M, K), dtype=torch.float8_e4m3fn)
+    A[np.arange(M), np.arange(M) % K] = a
+    B = torch.from_numpy(gen.standard_normal((K, N)).astype(np.float32) * 8).to(
+        torch.float8_e4m3fn)
+    A_bits, B_bits = A.view(torch.uint8).numpy(), B.view(torch.uint8).numpy()
+    C_bits = np.full((M, N), 0x7FC0, dtype=np.uint16)
+    alpha = 1.0625
+    ref = oracle.gemm("N", "N", M, N, K, alpha, A_bits, K, B_bits, N, 0.0, C_bits, N, "e4m3",
+                      c_dtype="bf16")
+    r32 = ref.astype(np.float32)                       # exact: alpha times one product
+    up = rne16(np.nextafter(r32, np.float32(np.inf)), "bf16")
+    down = rne16(np.nextafter(r32, np.float32(-np.inf)), "bf16")
+    assert np.count_nonzero((up != down) & (ref != 0)) > 0, "no rounding ties in the case"
+    C = to_dev(C_bits, "bf16")
+    forced(cfg, 1)
+    print("e4m3 rounding cfg %d" % cfg, flush=True)
+    try:
+        sg.gemm(to_dev(A_bits, "e4m3"), to_dev(B_bits, "e4m3"), C, alpha=alpha, beta=0.0,
+                dtype=3)
+        torch.cuda.synchronize()
+        desc = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+    assert "cfg=%d " % cfg in desc, desc
+    got = from_dev(C)
+    want = rne16(ref, "bf16")
     bad = np.argwhere(got != want)
     assert bad.size == 0, "%s: %d codes differ, first at %s: got %#06x want %#06x (%r)" % (
         desc, len(bad), bad[0], got[tuple(bad[0])], want[tuple(bad[0])], ref[tuple(bad[0])])
