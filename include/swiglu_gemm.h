@@ -231,9 +231,11 @@ const char* sg_status_string(int status);
 
 /*
  * Describes the kernel configuration chosen by the most recent successful
- * sg_gemm / sg_swiglu_gemm call on the calling thread (tile, split count) as a
- * NUL-terminated string copied into buf (at most len bytes).  Returns the full
- * length of the description.
+ * sg_gemm / sg_swiglu_gemm call on the calling thread (tile, split count; for a
+ * problem run as two launches over column ranges, "columns 0..n1" and the tail's
+ * configuration; for the decode kernels their grid and units) as a NUL-terminated
+ * string copied into buf (at most len bytes).  Returns the full length of the
+ * description.  Meant for logs and tests; the format is not a stable interface.
  */
 int sg_last_config(char* buf, int len);
 
