@@ -17,8 +17,8 @@ from helpers import assert_close, from_dev, gemm_oracle_rows, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-# (dtype, M, N, K): 256-row tiles leave a last round 1/16 (e4m3, 256 x 256 tiles:
-# 16 x 33 = 528) or 3/8 (bf16, 256 x 320 tiles: 32 x 27 = 864) full
+# (dtype, M, N, K): 256-row tiles fill the last pass over the CUs to 1/16 (e4m3, 256 x 256 tiles:
+# 16 x 33 = 528) or to 3/8 (bf16, 256 x 320 tiles: 32 x 27 = 864)
 SHAPES = {"bf16": (8192, 8448, 256), "e4m3": (4096, 8448, 256)}
 SEAM = {"bf16": 7680, "e4m3": 8192}     # first column of the tail launch
 
