@@ -661,14 +661,63 @@ int choose_w12(const Problem16& q_out) {
     return cfg;
 }
 
+// The column split of plan_col_split for the split-weight SwiGLU: a tile covers
+// BN/2 columns of W1 and the same of W2 (BN/2 outputs), so the seam n1 is in fused
+// columns and W1, W2 and Y continue at column n1 / 2 in the tail launch; the tail
+// takes the split-weight 128-row tile (measured: bf16 M = 2048, N = 4864, K = 896).
+ColSplit plan_w12_split(const Problem16& q_out, int cfg) {
+    ColSplit s;
+    int fc = -1, fs = 0;
+    if (forced_config(&fc, &fs)) return s;
+    const Cfg16& c = kCfg16[cfg];
+    if (c.BM < 256) return s;
+    const int64_t tm = cdiv(q_out.M, c.BM), tn = cdiv(2 * q_out.N, c.BN);
+    const int64_t rest = (tm * tn) % kNumCU;
+    if (tm * tn <= kNumCU || rest == 0 || 2 * rest > kNumCU) return s;
+    const int64_t strip = cdiv(rest, tm);
+    if (strip >= tn) return s;
+    const int tail = q_out.esz == 1 ? 45 : 6;
+    const Cfg16& t = kCfg16[tail];
+    Problem16 qt = q_out;
+    qt.N = q_out.N - (tn - strip) * c.BN / 2;
+    if (!w12_cfg_ok(t, qt)) return s;
+    if (cdiv(q_out.M, t.BM) * cdiv(2 * qt.N, t.BN) > 2 * kNumCU) return s;
+    s.n1 = (tn - strip) * c.BN;
+    s.cfg_tail = tail;
+    return s;
+}
+
 template <int DT>
-hipError_t run_w12(int cfg, Gemm16Params p, hipStream_t st) {
+hipError_t run_w12(int cfg, const Problem16& q_out, Gemm16Params p, hipStream_t st) {
     if (!p.A || !p.B || !p.B2 || !p.C) return hipErrorInvalidValue;   // never launch on NULL
     const Cfg16& c = kCfg16[cfg];
     p.tiles_m = (int)cdiv(p.M, c.BM);
     p.tiles_n = (int)cdiv(p.N, c.BN);
     p.group_m = group_m();
     p.k_per_split = (int)split_len(p.K, 1, c.BK);
+    const ColSplit cs = plan_w12_split(q_out, cfg);
+    if (cs.n1 > 0) {
+        const Cfg16& t = kCfg16[cs.cfg_tail];
+        Gemm16Params pt = p;
+        p.N = (int)cs.n1;
+        p.tiles_n = (int)cdiv(cs.n1, c.BN);
+        pt.N = (int)(2 * q_out.N - cs.n1);
+        pt.tiles_m = (int)cdiv(pt.M, t.BM);
+        pt.tiles_n = (int)cdiv(pt.N, t.BN);
+        pt.k_per_split = (int)split_len(pt.K, 1, t.BK);
+        const int64_t off = cs.n1 / 2;                // weight column = output column
+        pt.B = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(p.B) +
+                                                 off * q_out.esz);
+        pt.B2 = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(p.B2) +
+                                                  off * q_out.esz);
+        pt.C = static_cast<char*>(p.C) + off * 2;
+        std::snprintf(g_last_cfg, sizeof(g_last_cfg),
+                      "swiglu_w12 cfg=%d %s splits=1 columns 0..%lld, tail cfg=%d %s", cfg,
+                      c.name, (long long)cs.n1, cs.cfg_tail, t.name);
+        hipError_t e = launch16_dt<DT>(false, false, EPI_SWIGLU_W12, cfg, p, 1, st);
+        if (e != hipSuccess) return e;
+        return launch16_dt<DT>(false, false, EPI_SWIGLU_W12, cs.cfg_tail, pt, 1, st);
+    }
     std::snprintf(g_last_cfg, sizeof(g_last_cfg), "swiglu_w12 cfg=%d %s splits=1", cfg, c.name);
     return launch16_dt<DT>(false, false, EPI_SWIGLU_W12, cfg, p, 1, st);
 }
@@ -1000,9 +1049,9 @@ int sg_swiglu_gemm_w12(const void* A, const void* W1, const void* W2, void* Y, i
             p.vec_c = aligned(Y, 8) && (N % 4 == 0);
             p.epi_flags = aligned(Y, 16) && N % 8 == 0 ? EPI_Y16 : 0;
             hipError_t e;
-            if (dtype == SG_F8E4M3) e = run_w12<DT_E4M3>(cfg, p, st);
-            else if (dtype == SG_F16) e = run_w12<DT_F16>(cfg, p, st);
-            else e = run_w12<DT_BF16>(cfg, p, st);
+            if (dtype == SG_F8E4M3) e = run_w12<DT_E4M3>(cfg, q, p, st);
+            else if (dtype == SG_F16) e = run_w12<DT_F16>(cfg, q, p, st);
+            else e = run_w12<DT_BF16>(cfg, q, p, st);
             return status_of(e);
         }
     }

@@ -96,3 +96,26 @@ def test_swiglu_column_split(dtype):
     rows = sample_rows(M, 8)
     ref = oracle.swiglu(len(rows), N, K, pb["A"][rows, :], Wf, dtype, sa, sw)
     assert_close(got[rows, :], ref, dtype, K, desc)
+
+
+@pytest.mark.parametrize("dtype,M,N,K,seam,tail", [("bf16", 2048, 4864, 896, 8192, 6),
+                                                  ("e4m3", 4096, 11008, 4096, 20480, 45)])
+def test_swiglu_w12_column_split(dtype, M, N, K, seam, tail):
+    """Split-weight SwiGLU: the seam is a fused column, W1, W2 and Y continue at half of
+    it in the tail launch (bf16: 256 x 256 tiles, 8 x 38 = 304; e4m3: 16 x 86 = 1376)."""
+    import swiglu_gemm_amd as sg
+    pb = inputs.swiglu_problem(320, M, N, K, dtype)
+    sa, sw = pb.get("scale_a", 1.0), pb.get("scale_w", 1.0)
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    print("colsplit swiglu_w12 %s M=%d N=%d K=%d" % (dtype, M, N, K), flush=True)
+    sg.swiglu_gemm_w12(to_dev(pb["A"], dtype), to_dev(pb["W1"], dtype), to_dev(pb["W2"], dtype),
+                       Y, sa, sw)
+    torch.cuda.synchronize()
+    desc = sg.last_config()
+    assert ("tail cfg=%d " % tail) in desc and "columns 0..%d," % seam in desc, desc
+    got = oracle.decode(from_dev(Y), "bf16")
+    assert np.all(np.isfinite(got)), desc
+    rows = sample_rows(M, 9)
+    Wf = oracle.interleave(pb["W1"], pb["W2"])
+    ref = oracle.swiglu(len(rows), N, K, pb["A"][rows, :], Wf, dtype, sa, sw)
+    assert_close(got[rows, :], ref, dtype, K, desc)
