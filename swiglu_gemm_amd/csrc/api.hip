@@ -207,8 +207,9 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
             // x 4096: 14.3 us against 24.8 us for 128x256 with split-K); above 128
             // rows, 8-wave 128x256 tiles while they fit one round (SwiGLU M = 192, 256:
             // 34, 36 us against 40, 39 us with 4 waves and 52 us with 32-row tiles),
-            // else 128x128; up to 128 rows, 32-row tiles (256 wide when that still
-            // gives half a round)
+            // else 128x128; up to 128 rows, 32-row tiles: 128 wide while one work-group
+            // per CU holds them, else 256 wide if that is one round (SwiGLU M = 64: 27.6
+            // against 33.0 us with 344 work-groups of 32 x 128), else 128 wide
             const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
             const int64_t mid = cdiv(q.M, 128) * cdiv(q.N, 256);
             const int64_t thin = cdiv(q.M, 32) * cdiv(q.N, 128);
@@ -218,8 +219,10 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
                 cfg = 17;
             else if (q.M > 128)
                 cfg = mid <= kNumCU ? 45 : 15;
+            else if (cdiv(q.M, 32) * cdiv(q.N, 128) <= kNumCU)
+                cfg = 17;
             else
-                cfg = cdiv(q.N, 256) >= 128 ? 16 : 17;
+                cfg = cdiv(q.M, 32) * cdiv(q.N, 256) <= kNumCU ? 16 : 17;
         } else {
             double best = 0.0;
             for (const Cand16& cand : kCand16) {
@@ -252,7 +255,15 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
             if (cfg < 0) cfg = cdiv(q.M, 256) * cdiv(q.N, 256) >= kNumCU ? 0 : 2;
         }
     }
-    if (splits <= 0) splits = pick_splits(kCfg16[cfg], q);
+    if (splits <= 0) {
+        splits = pick_splits(kCfg16[cfg], q);
+        // e4m3 above the decode sizes: the reduction launch costs more than split-K
+        // returns unless the tiles fill under an eighth of the CUs (measured: 64 x 4096
+        // x 4096 NT with 32 x 128 tiles, 10.4 us unsplit against 12.7 us with 2 splits)
+        if (e4m3 && !forced && q.M > 32 && splits > 1 &&
+            cdiv(q.M, kCfg16[cfg].BM) * cdiv(q.N, kCfg16[cfg].BN) * 8 > kNumCU)
+            splits = 1;
+    }
     if (!dma_ok(kCfg16[cfg], q, split_len(q.K, splits, kCfg16[cfg].BK))) {
         if (kCfg16[cfg].dma && !e4m3 && !kCfg16[cfg].e4m3) {
             cfg = kCfg16[cfg].BM >= 256 ? 0 : 2;
