@@ -298,6 +298,43 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
     }
 }
 
+// Split-K partial sums of a full tile (N a multiple of 4): one 32-row block of every
+// wave at a time is staged in LDS as fp32 rows (16 bytes of padding per row), then every
+// thread stores whole 16-byte row pieces into this split's [M][N] slab (plain stores:
+// the reduction reads them back at once).  rb / cb: first tile row / column of the wave.
+template <int FM, int FN, int BM, int BN, int NT>
+__device__ __forceinline__ void epilogue_partial_rows_lds(const Gemm16Params& p,
+                                                          f32x16 (&acc)[FN][FM], char* smem,
+                                                          int m0, int n0, int rb, int cb,
+                                                          int lane) {
+    constexpr int ROW = 4 * BN + 16;               // bytes per staged row
+    constexpr int CPR = BN / 4;                    // 16-byte pieces (4 sums) per row
+    constexpr int WMS = BM / (32 * FM);            // wave rows of the tile
+    constexpr int PB = WMS * 32 * CPR;             // pieces per 32-row block
+    const int lm = lane & 31, lq = (lane >> 5) * 4;
+    const int wr = rb / (32 * FM);
+    float* W = reinterpret_cast<float*>(p.C) + (int64_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+    for (int tm = 0; tm < FM; ++tm) {
+        __syncthreads();
+        char* row = smem + (wr * 32 + lm) * ROW;
+#pragma unroll
+        for (int tn = 0; tn < FN; ++tn)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4*>(row + 4 * (cb + tn * 32 + 8 * g + lq)) =
+                    f32x4{acc[tn][tm][4 * g], acc[tn][tm][4 * g + 1], acc[tn][tm][4 * g + 2],
+                          acc[tn][tm][4 * g + 3]};
+        __syncthreads();
+        for (int i = threadIdx.x; i < PB; i += NT) {
+            const int rr = i / CPR, c = i - rr * CPR;
+            const int r = (rr >> 5) * (32 * FM) + tm * 32 + (rr & 31);
+            *reinterpret_cast<f32x4*>(W + (int64_t)(m0 + r) * p.N + n0 + c * 4) =
+                *reinterpret_cast<const f32x4*>(smem + rr * ROW + c * 16);
+        }
+    }
+}
+
 // GEMM epilogue (beta = 0, full tile, C 16-byte aligned with ldc a multiple of 8) of the
 // direct-to-LDS kernels: one 32-row block of every wave at a time is rounded to the
 // output type and staged in LDS as rows of the tile (16 bytes of padding per row), then

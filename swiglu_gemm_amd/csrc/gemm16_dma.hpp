@@ -360,6 +360,15 @@ __device__ __forceinline__ void dma_epilogue(
         }
         epilogue_gemm_ex_lds<DT_OUT, FM, FN>(p, acc, smem, m0 + wm * TM, n0 + wn * TN, wave, lane);
     } else {
+        if constexpr (EPI == EPI_PARTIAL && (BM / (32 * FM)) * 32 * (4 * BN + 16) <= D::LDS) {
+            // split-K partials of a full tile leave as whole lines (measured: see the
+            // design notes)
+            if (m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0) {
+                epilogue_partial_rows_lds<FM, FN, BM, BN, 64 * WM * WN>(p, acc, smem, m0, n0,
+                                                                        wm * TM, wn * TN, lane);
+                return;
+            }
+        }
         // Staged row stores where work-groups run in more than one round (measured:
         // fp16 / bf16 8192^3 3-4 % and the e4m3 4096 x 22016 x 4096 GEMM 9 % faster; a
         // single round, 2048 x 9728 x 896, 2.5 % slower); rings too small for a staged
