@@ -127,17 +127,18 @@ struct Batch {
     int64_t sA = 0, sB = 0, sC = 0;
 };
 
-// Whether a direct-to-LDS configuration can run the problem: no K tail, aligned
-// operands, DMA-compatible tiles, and a row-contiguous operand whose row length
-// is a whole number of 16-byte chunks (edge rows / chunks are clamped in-kernel).
+// Whether a direct-to-LDS configuration can run the problem: 16-byte aligned
+// operands and rows (base pointers and ld) and DMA-compatible tiles.  Edge rows and
+// chunks are clamped in-kernel; a row-contiguous operand's row (M or N elements)
+// may end inside a chunk.  A K tail (K not a multiple of BK) is loaded through
+// registers by the one-stream kernel; the ping-pong kernel needs whole K tiles.
 bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
     if (!c.dma || c.e4m3 != (q.esz == 1)) return false;
-    if (!q.vec_a || !q.vec_b || q.K % c.BK != 0 || kps % c.BK != 0) return false;
+    if (!q.vec_a || !q.vec_b || kps % c.BK != 0) return false;
+    if (c.dma == 2 && q.K % c.BK != 0) return false;
     const int nw = c.dma == 2 ? 4 : c.WM * c.WN;     // ping-pong: group 0 issues the DMA
     if (!dma_tile_ok(!q.ta, c.BM, c.BK, q.esz, nw) || !dma_tile_ok(q.tb, c.BN, c.BK, q.esz, nw))
         return false;
-    if (q.ta && (q.M * q.esz) % 16 != 0) return false;   // A rows hold M elements
-    if (!q.tb && (q.N * q.esz) % 16 != 0) return false;  // B rows hold N elements
     return true;
 }
 
@@ -642,7 +643,7 @@ bool w12_cfg_ok(const Cfg16& c, const Problem16& q_out) {
     if (c.dma != 1 || (c.BN / c.WN / 32) % 2 != 0 || c.BN % 64 != 0) return false;
     Cfg16 half = c;
     half.BN = c.BN / 2;
-    return dma_ok(half, q_out, q_out.K);
+    return dma_ok(half, q_out, split_len(q_out.K, 1, c.BK));
 }
 
 int choose_w12(const Problem16& q_out) {
@@ -1066,7 +1067,8 @@ int sg_swiglu_gemm_w12(const void* A, const void* W1, const void* W2, void* Y, i
             return status_of(e);
         }
     }
-    // shapes the split-weight kernel cannot take (K tail, unaligned rows, K == 0):
+    // shapes the split-weight kernel cannot take (rows that are not whole 16-byte
+    // chunks, K == 0):
     // build W_fused in library scratch and take the interleaved path
     float* ws = nullptr;
     hipError_t e = workspace((size_t)(K > 0 ? K : 1) * 2 * N * esz, &ws, 1);

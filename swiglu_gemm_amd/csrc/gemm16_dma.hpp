@@ -109,8 +109,11 @@ struct DmaStream {
                 const int r = min(r0 + row, rows - 1);
                 gp[i] = base + ((int64_t)r * ld + k0) * ESZ + c * 16;
             } else {
+                // past the row's end: the last 16-byte aligned chunk that starts in
+                // it (its bytes past the end reach only outputs that are never
+                // stored; it lies in one page, mapped since its first byte is data)
                 const int u = (slot >> 1) ^ T::swz(row);
-                const int cb = min(r0 * ESZ + u * 32 + (slot & 1) * 16, rows * ESZ - 16);
+                const int cb = min(r0 * ESZ + u * 32 + (slot & 1) * 16, (rows * ESZ - 1) & ~15);
                 gp[i] = base + (int64_t)(k0 + row) * ld * ESZ + cb;
             }
         }
@@ -129,6 +132,41 @@ struct DmaStream {
             const char* g = gp[i] + t * step;
             asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                          :: "s"(lds), "v"(g) : "memory", "m0");
+        }
+    }
+    // A trailing partial K tile (the stream initialised at its first k), of which
+    // only the first `kvalid` k belong to the problem: loaded through registers into
+    // the LDS positions issue() would fill, zero at k >= kvalid, so fragment reads
+    // and MFMAs are those of a full tile.  A chunk that holds the problem's last k
+    // is read whole: it is 16-byte aligned and its first byte is in the operand, so
+    // it lies in a page that is mapped; the bytes past K are then cleared.  Chunks
+    // wholly past K are not read.
+    __device__ __forceinline__ void load_tail(char* stage, int kvalid, int wave, int lane) const {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int b = wave + i * NWAVES;
+            const int chunk = b * 64 + lane;
+            const int row = chunk / T::SLOTS;
+            const int slot = chunk % T::SLOTS;
+            const char* g = gp[i];
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if constexpr (KC) {
+                constexpr int EPC = 16 / ESZ;                       // elements per chunk
+                const int n = kvalid - (slot ^ T::swz(row)) * EPC;  // of them in the problem
+                if (n > 0) {
+                    v = *reinterpret_cast<const u32x4*>(g);
+                    if (n < EPC) {
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const int nb = n * ESZ - 4 * d;         // valid bytes of dword d
+                            v[d] = nb >= 4 ? v[d] : nb <= 0 ? 0u : v[d] & ((1u << (8 * nb)) - 1u);
+                        }
+                    }
+                }
+            } else if (row < kvalid) {
+                v = *reinterpret_cast<const u32x4*>(g);
+            }
+            *reinterpret_cast<u32x4*>(stage + b * 1024 + lane * 16) = v;
         }
     }
 };
@@ -231,12 +269,13 @@ struct DmaShape {
 };
 
 // acc += op(A) * op(B) over K tiles [kbeg, kbeg + nkt*BK) of the output tile at
-// (m0, n0): the S-stage direct-to-LDS ring feeding the MFMAs.  Every thread of the
+// (m0, n0), plus a trailing partial tile of ktail (< BK) k when K is not a multiple
+// of BK: the S-stage direct-to-LDS ring feeding the MFMAs.  Every thread of the
 // work-group calls it; LDS is free on return only after a barrier (the last k-step
 // reads a stage without one).
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
 __device__ __forceinline__ void dma_mainloop(
-    const Gemm16Params& p, char* smem, int m0, int n0, int kbeg, int nkt,
+    const Gemm16Params& p, char* smem, int m0, int n0, int kbeg, int nkt, int ktail,
     typename DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>::Acc& acc, int wave, int lane) {
     using D = DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>;
     constexpr int ESZ = D::ESZ, FM = D::FM, FN = D::FN, KS = D::KS, TM = D::TM, TN = D::TN;
@@ -323,6 +362,37 @@ __device__ __forceinline__ void dma_mainloop(
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    if (ktail > 0) {
+        // every DMA has landed (the ring's last wait is for all of them); once every
+        // wave is past its reads, stage 0 takes the zero-filled tail tile.  The
+        // addresses are computed afresh (an opaque lane index keeps the compiler from
+        // carrying the main loop's through it).
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int kt = kbeg + nkt * BK;
+        __syncthreads();
+        {
+            DmaStream<KCA, BM, BK, ESZ, NW> ta;
+            ta.init(p.A, p.lda, m0, p.M, kt, wave, ln);
+            ta.load_tail(smem, ktail, wave, ln);
+        }
+        if constexpr (W12) {
+            DmaStream<KCB, BNS, BK, ESZ, NW> tb, tb2;
+            tb.init(p.B, p.ldb, n0 / 2, p.N / 2, kt, wave, ln);
+            tb.load_tail(smem + TA_::BYTES, ktail, wave, ln);
+            tb2.init(p.B2, p.ldb, n0 / 2, p.N / 2, kt, wave, ln);
+            tb2.load_tail(smem + TA_::BYTES + TB_::BYTES, ktail, wave, ln);
+        } else {
+            DmaStream<KCB, BNS, BK, ESZ, NW> tb;
+            tb.init(p.B, p.ldb, n0, p.N, kt, wave, ln);
+            tb.load_tail(smem + TA_::BYTES, ktail, wave, ln);
+        }
+        __syncthreads();
+        for (int s = 0; s < KS && s * D::KSTEP < ktail; ++s) {   // k-steps past K add 0
+            read_all(smem, s, fa[0], fb[0]);
+            mfma_all(fa[0], fb[0]);
+        }
+    }
 }
 
 // The epilogue of one finished output tile (every thread of the work-group).
@@ -400,7 +470,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
     const int m0 = tmi * BM, n0 = tni * BN;
     const int kbeg = blockIdx.y * p.k_per_split;
     const int kend = min(p.K, kbeg + p.k_per_split);
-    const int nkt = kend > kbeg ? (kend - kbeg) / BK : 0;
+    const int klen = kend > kbeg ? kend - kbeg : 0;
+    const int nkt = klen / BK, ktail = klen - nkt * BK;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 
     typename D::Acc acc;
@@ -410,8 +481,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
         for (int j = 0; j < D::FM; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    dma_mainloop<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, smem, m0, n0, kbeg, nkt, acc, wave,
-                                                         lane);
+    dma_mainloop<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, smem, m0, n0, kbeg, nkt, ktail, acc,
+                                                         wave, lane);
     dma_epilogue<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, acc, smem, m0, n0, wave, lane);
 }
 

@@ -47,7 +47,7 @@ struct DmaStreamS {
                 off[i] = (uint32_t)((int64_t)r * ld * ESZ + c * 16);
             } else {
                 const int u = (slot >> 1) ^ T::swz(row);
-                const int cb = min(r0 * ESZ + u * 32 + (slot & 1) * 16, rows * ESZ - 16) - r0 * ESZ;
+                const int cb = min(r0 * ESZ + u * 32 + (slot & 1) * 16, (rows * ESZ - 1) & ~15) - r0 * ESZ;
                 off[i] = (uint32_t)((int64_t)row * ld * ESZ + cb);
             }
         }

@@ -131,9 +131,10 @@ def test_epilogue_e4m3_output(dtype, act):
 
 @pytest.mark.parametrize("act", ["gelu", "silu"])
 def test_epilogue_other_paths(act):
-    """Register-staged kernel (K tail), split-K + reduction, decode path, generic
-    e4m3 kernel (K tail), each with bias and activation, 16-bit and e4m3 outputs."""
-    check_ex("bf16", "T", "N", 200, 300, 250, 420, act, "f32", expect=" reg ")
+    """Register-staged kernel (a leading dimension that is not a 16-byte multiple),
+    split-K + reduction, decode path, generic e4m3 kernel (K tail, odd rows), each
+    with bias and activation, 16-bit and e4m3 outputs."""
+    check_ex("bf16", "T", "N", 201, 300, 250, 420, act, "f32", expect=" reg ", ld_mode="tight")
     d = check_ex("f16", "N", "N", 64, 384, 8192, 421, act, "f16")
     assert split_count(d) > 1, d
     check_ex("bf16", "N", "T", 4, 1024, 2048, 422, act, "bf16", expect="decode")
