@@ -210,10 +210,10 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
                     if (full_c) {
                         if (beta != 0.0f) {
                             const u32x2 old = *reinterpret_cast<const u32x2*>(c);
-                            v[0] += beta * to_f32<DT>((uint16_t)(old.x & 0xffff));
-                            v[1] += beta * to_f32<DT>((uint16_t)(old.x >> 16));
-                            v[2] += beta * to_f32<DT>((uint16_t)(old.y & 0xffff));
-                            v[3] += beta * to_f32<DT>((uint16_t)(old.y >> 16));
+                            v[0] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(old.x & 0xffff)), v[0]);
+                            v[1] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(old.x >> 16)), v[1]);
+                            v[2] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(old.y & 0xffff)), v[2]);
+                            v[3] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(old.y >> 16)), v[3]);
                         }
                         u32x2 o;
                         o.x = pack2<DT>(v[0], v[1]);
@@ -224,7 +224,7 @@ __device__ __forceinline__ void epilogue16(const Gemm16Params& p, f32x16 (&acc)[
                         for (int e = 0; e < 4; ++e) {
                             if (n + e < p.N) {
                                 float x = v[e];
-                                if (beta != 0.0f) x += beta * to_f32<DT>(c[e]);
+                                if (beta != 0.0f) x = __builtin_fmaf(beta, to_f32<DT>(c[e]), x);
                                 c[e] = from_f32<DT>(x);
                             }
                         }
@@ -376,6 +376,77 @@ __device__ __forceinline__ void epilogue_gemm_rows_lds(const Gemm16Params& p,
             const u32x4 v = *reinterpret_cast<const u32x4*>(smem + rr * ROW + c * 16);
             __builtin_nontemporal_store(
                 v, reinterpret_cast<u32x4*>(C + (int64_t)(m0 + r) * p.ldc + n0 + c * 8));
+        }
+    }
+}
+
+// The GEMM epilogue with beta != 0, staged so that C_old is read and C written as
+// whole 16-byte row pieces.  One 32-row block (tm) of every wave row and one wave
+// column (h, TN = BN / WN columns) at a time, the waves of that column write alpha *
+// acc in fp32 into LDS rows; all threads then read 8 values of C_old, form alpha *
+// acc + beta * C_old in fp32 (one fma) and store the 8 values rounded once.  Pieces
+// past M are skipped and the piece that N cuts goes element by element, so edge
+// tiles take this path too (C must be 16-byte aligned with ldc a multiple of 8).
+// Same arithmetic as the register epilogue, so the outputs are bit-identical.
+// Called by every thread after the main loop.
+template <int DT, int FM, int FN, int BM, int BN, int WN, int NT>
+__device__ __forceinline__ void epilogue_gemm_rows_beta_lds(const Gemm16Params& p,
+                                                            f32x16 (&acc)[FN][FM], char* smem,
+                                                            int m0, int n0, int rb, int wn,
+                                                            int lane) {
+    constexpr int TN = BN / WN;                    // columns of one wave column
+    constexpr int ROW = 4 * TN + 16;               // bytes per staged row (fp32)
+    constexpr int CPR = TN / 8;                    // 16-byte pieces (8 outputs) of C per row
+    constexpr int WMS = BM / (32 * FM);            // wave rows of the tile
+    constexpr int PB = WMS * 32 * CPR;             // pieces per pass
+    static_assert(FN * 32 == TN, "one wave column holds FN fragments");
+    const int lm = lane & 31, lq = (lane >> 5) * 4;
+    const int wr = rb / (32 * FM);                 // the calling wave's row of waves
+    const float alpha = p.alpha, beta = p.beta;
+    uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
+#pragma unroll
+    for (int tm = 0; tm < FM; ++tm) {
+#pragma unroll
+        for (int h = 0; h < WN; ++h) {
+            __syncthreads();
+            if (wn == h) {
+                char* row = smem + (wr * 32 + lm) * ROW;
+#pragma unroll
+                for (int tn = 0; tn < FN; ++tn)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<f32x4*>(row + 4 * (tn * 32 + 8 * g + lq)) =
+                            f32x4{alpha * acc[tn][tm][4 * g], alpha * acc[tn][tm][4 * g + 1],
+                                  alpha * acc[tn][tm][4 * g + 2], alpha * acc[tn][tm][4 * g + 3]};
+            }
+            __syncthreads();
+            for (int i = threadIdx.x; i < PB; i += NT) {
+                const int rr = i / CPR, c = i - rr * CPR;
+                const int m = m0 + (rr >> 5) * (32 * FM) + tm * 32 + (rr & 31);
+                const int n = n0 + h * TN + c * 8;
+                if (m >= p.M || n >= p.N) continue;
+                const char* src = smem + rr * ROW + c * 32;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+                const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                uint16_t* cp = C + (int64_t)m * p.ldc + n;
+                if (n + 8 <= p.N) {
+                    const u32x4 old = *reinterpret_cast<const u32x4*>(cp);
+                    const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        o[j] = pack2<DT>(
+                            __builtin_fmaf(beta, to_f32<DT>((uint16_t)(ow[j] & 0xffff)), v[2 * j]),
+                            __builtin_fmaf(beta, to_f32<DT>((uint16_t)(ow[j] >> 16)), v[2 * j + 1]));
+                    *reinterpret_cast<u32x4*>(cp) = u32x4{o[0], o[1], o[2], o[3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < p.N)
+                            cp[e] = from_f32<DT>(__builtin_fmaf(beta, to_f32<DT>(cp[e]), v[e]));
+                }
+            }
         }
     }
 }
