@@ -64,6 +64,8 @@ constexpr Cfg16 kCfg16[] = {
     {0, 1, 64, 256, 64, 3, 1, 4, "dma 64x256x64 s3 1x4w"},
     {0, 1, 64, 128, 64, 4, 1, 4, "dma 64x128x64 s4 1x4w"},
     {1, 1, 128, 256, 128, 3, 2, 4, "e4m3 dma 128x256x128 s3 2x4w"},
+    // 192-column tiles: one full round where 256 columns leave CUs idle (N = 3072)
+    {0, 1, 256, 192, 64, 2, 4, 2, "dma 256x192x64 s2 4x2w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
@@ -112,7 +114,8 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(31, 1, 128, 128, 32, 8, 2, 2)    \
     X(32, 1, 128, 256, 64, 3, 2, 4)    \
     X(43, 1, 64, 256, 64, 3, 1, 4)     \
-    X(44, 1, 64, 128, 64, 4, 1, 4)
+    X(44, 1, 64, 128, 64, 4, 1, 4)     \
+    X(46, 1, 256, 192, 64, 2, 4, 2)
 
 // the pipeline-depth study rows, instantiated for fp16 NN EPI_GEMM only
 #define SG_CONFIGS_SWEEP(X)            \
