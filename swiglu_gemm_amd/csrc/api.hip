@@ -223,7 +223,13 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
             else if (q.M > 128 && thin <= 2 * kNumCU)
                 cfg = 17;
             else if (q.M > 128)
-                cfg = mid <= kNumCU ? 45 : 15;
+                // ... and 128 x 192 where 128 x 256 leaves over a quarter of the CUs
+                // idle and the narrower tiles still fit one round (GEMM 256 x 11008 x
+                // 4096 NT: 24.4 against 29.1 us; SwiGLU M = 160, 256: 34.3, 35.6
+                // against 36.2, 36.7 us)
+                cfg = mid > kNumCU ? 15
+                      : (4 * mid <= 3 * kNumCU && cdiv(q.M, 128) * cdiv(q.N, 192) <= kNumCU) ? 47
+                                                                                          : 45;
             else if (cdiv(q.M, 32) * cdiv(q.N, 128) <= kNumCU)
                 cfg = 17;
             else

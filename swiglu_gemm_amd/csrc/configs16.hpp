@@ -66,6 +66,7 @@ constexpr Cfg16 kCfg16[] = {
     {1, 1, 128, 256, 128, 3, 2, 4, "e4m3 dma 128x256x128 s3 2x4w"},
     // 192-column tiles: one full round where 256 columns leave CUs idle (N = 3072)
     {0, 1, 256, 192, 64, 2, 4, 2, "dma 256x192x64 s2 4x2w"},
+    {1, 1, 128, 192, 128, 3, 4, 2, "e4m3 dma 128x192x128 s3 4x2w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
@@ -157,6 +158,7 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(21, 2, 256, 256, 128, 2, 4, 2)   \
     X(23, 2, 128, 256, 128, 2, 2, 4)   \
     X(33, 1, 128, 256, 128, 3, 2, 2)   \
-    X(45, 1, 128, 256, 128, 3, 2, 4)
+    X(45, 1, 128, 256, 128, 3, 2, 4)   \
+    X(47, 1, 128, 192, 128, 3, 4, 2)
 
 }  // namespace sg

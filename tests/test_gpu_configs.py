@@ -94,7 +94,7 @@ def test_output_rounding_bit_exact_many_tiles(cfg, dtype):
     rounding_case(cfg, dtype, 8192, 4608, 64)
 
 
-@pytest.mark.parametrize("cfg", [14, 15, 17, 33, 45])
+@pytest.mark.parametrize("cfg", [14, 15, 17, 33, 45, 47])
 def test_e4m3_output_rounding_bit_exact_many_tiles(cfg):
     """e4m3 operands, bf16 output: one product per output (A has one nonzero per row)
     times alpha = 1.0625, exact in fp32 (at most 8 + 5 significant bits) and rounded once

@@ -119,7 +119,7 @@ def test_ktail_every_16bit_config(cfg, K):
 
 
 @pytest.mark.parametrize("K,lda", [(48, None), (1040, None), (1000, 1008), (4100, 4112)])
-@pytest.mark.parametrize("cfg", [14, 15, 16, 17, 33, 45])
+@pytest.mark.parametrize("cfg", [14, 15, 16, 17, 33, 45, 47])
 def test_ktail_every_e4m3_config(cfg, K, lda):
     """Forced e4m3 configurations with a K tail; K = 1000 and 4100 leave 8 and 4
     valid bytes in the last chunk of each row (rows padded to 1008 / 4112 bytes)."""
