@@ -114,14 +114,14 @@ __device__ __forceinline__ void epilogue_gemm_ex_lds(const Gemm16Params& p, f32x
                     const uint16_t* c = reinterpret_cast<const uint16_t*>(p.C) + idx;
                     if (vec) {
                         const u32x2 old = *reinterpret_cast<const u32x2*>(c);
-                        v[0] += beta * to_f32<DT>((uint16_t)(old.x & 0xffff));
-                        v[1] += beta * to_f32<DT>((uint16_t)(old.x >> 16));
-                        v[2] += beta * to_f32<DT>((uint16_t)(old.y & 0xffff));
-                        v[3] += beta * to_f32<DT>((uint16_t)(old.y >> 16));
+                        v[0] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(old.x & 0xffff)), v[0]);
+                        v[1] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(old.x >> 16)), v[1]);
+                        v[2] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(old.y & 0xffff)), v[2]);
+                        v[3] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(old.y >> 16)), v[3]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (e < valid) v[e] += beta * to_f32<DT>(c[e]);
+                            if (e < valid) v[e] = __builtin_fmaf(beta, to_f32<DT>(c[e]), v[e]);
                     }
                 }
                 f32x4 y;
@@ -380,23 +380,39 @@ __device__ __forceinline__ void epilogue_gemm_rows_lds(const Gemm16Params& p,
     }
 }
 
+// Wave columns of a tile staged per pass by the fp32 row epilogues below: all WN if
+// the fp32 rows of one 32-row block of every wave row fit in LDSB bytes (EXTRA more
+// bytes beside them), else the largest power-of-two divisor of WN that fits; 0 if
+// not even one wave column fits.
+template <int BM, int BN, int FM, int WN, int LDSB, int EXTRA>
+constexpr int staged_wave_cols() {
+    const int wms = BM / (32 * FM);
+    for (int cw = WN; cw >= 1; cw /= 2)
+        if (WN % cw == 0 && wms * 32 * (4 * (BN / WN) * cw + 16) + EXTRA <= LDSB) return cw;
+    return 0;
+}
+
 // The GEMM epilogue with beta != 0, staged so that C_old is read and C written as
-// whole 16-byte row pieces.  One 32-row block (tm) of every wave row and one wave
-// column (h, TN = BN / WN columns) at a time, the waves of that column write alpha *
-// acc in fp32 into LDS rows; all threads then read 8 values of C_old, form alpha *
+// whole 16-byte row pieces.  One 32-row block (tm) of every wave row and CW wave
+// columns (pass h; CW from staged_wave_cols) at a time, the waves of those columns
+// write alpha * acc in fp32 into LDS rows; all threads then read 8 values of C_old,
+// form alpha *
 // acc + beta * C_old in fp32 (one fma) and store the 8 values rounded once.  Pieces
 // past M are skipped and the piece that N cuts goes element by element, so edge
 // tiles take this path too (C must be 16-byte aligned with ldc a multiple of 8).
 // Same arithmetic as the register epilogue, so the outputs are bit-identical.
 // Called by every thread after the main loop.
-template <int DT, int FM, int FN, int BM, int BN, int WN, int NT>
+template <int DT, int FM, int FN, int BM, int BN, int WN, int NT, int LDSB>
 __device__ __forceinline__ void epilogue_gemm_rows_beta_lds(const Gemm16Params& p,
                                                             f32x16 (&acc)[FN][FM], char* smem,
                                                             int m0, int n0, int rb, int wn,
                                                             int lane) {
     constexpr int TN = BN / WN;                    // columns of one wave column
-    constexpr int ROW = 4 * TN + 16;               // bytes per staged row (fp32)
-    constexpr int CPR = TN / 8;                    // 16-byte pieces (8 outputs) of C per row
+    constexpr int CW = staged_wave_cols<BM, BN, FM, WN, LDSB, 0>();
+    static_assert(CW > 0, "one wave column of fp32 rows fits the LDS ring");
+    constexpr int TS = CW * TN;                    // columns staged per pass
+    constexpr int ROW = 4 * TS + 16;               // bytes per staged row (fp32)
+    constexpr int CPR = TS / 8;                    // 16-byte pieces (8 outputs) of C per row
     constexpr int WMS = BM / (32 * FM);            // wave rows of the tile
     constexpr int PB = WMS * 32 * CPR;             // pieces per pass
     static_assert(FN * 32 == TN, "one wave column holds FN fragments");
@@ -407,10 +423,10 @@ __device__ __forceinline__ void epilogue_gemm_rows_beta_lds(const Gemm16Params& 
 #pragma unroll
     for (int tm = 0; tm < FM; ++tm) {
 #pragma unroll
-        for (int h = 0; h < WN; ++h) {
+        for (int h = 0; h < WN / CW; ++h) {
             __syncthreads();
-            if (wn == h) {
-                char* row = smem + (wr * 32 + lm) * ROW;
+            if (wn / CW == h) {
+                char* row = smem + (wr * 32 + lm) * ROW + 4 * (wn % CW) * TN;
 #pragma unroll
                 for (int tn = 0; tn < FN; ++tn)
 #pragma unroll
@@ -423,7 +439,7 @@ __device__ __forceinline__ void epilogue_gemm_rows_beta_lds(const Gemm16Params& 
             for (int i = threadIdx.x; i < PB; i += NT) {
                 const int rr = i / CPR, c = i - rr * CPR;
                 const int m = m0 + (rr >> 5) * (32 * FM) + tm * 32 + (rr & 31);
-                const int n = n0 + h * TN + c * 8;
+                const int n = n0 + h * TS + c * 8;
                 if (m >= p.M || n >= p.N) continue;
                 const char* src = smem + rr * ROW + c * 32;
                 const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
@@ -445,6 +461,119 @@ __device__ __forceinline__ void epilogue_gemm_rows_beta_lds(const Gemm16Params& 
                     for (int e = 0; e < 8; ++e)
                         if (n + e < p.N)
                             cp[e] = from_f32<DT>(__builtin_fmaf(beta, to_f32<DT>(cp[e]), v[e]));
+                }
+            }
+        }
+    }
+}
+
+// EPI_GEMM_EX staged the same way: alpha * acc in fp32, CW wave columns and one
+// 32-row block at a time; every thread then finishes 8 consecutive outputs of a row (beta *
+// C_old with one fma, bias, activation, one rounding or the e4m3 code of y *
+// inv_scale) and stores them as one 16-byte piece (8 bytes of e4m3 codes),
+// non-temporally (whole lines).  Rows past M are skipped and the piece that N cuts
+// goes element by element, so edge tiles take this path too (C 16-byte aligned,
+// ldc a multiple of 8).  The steps never index the accumulator, so the activation
+// code is emitted once, in the rolled piece loop.
+template <int DT, int FM, int FN, int BM, int BN, int WN, int NT, int LDSB>
+__device__ __forceinline__ void epilogue_gemm_ex_rows_lds(const Gemm16Params& p,
+                                                          f32x16 (&acc)[FN][FM], char* smem,
+                                                          int m0, int n0, int rb, int wn,
+                                                          int lane) {
+    constexpr int TN = BN / WN;                    // columns of one wave column
+    constexpr int CW = staged_wave_cols<BM, BN, FM, WN, LDSB, 4 * BN>();
+    static_assert(CW > 0, "one wave column of fp32 rows and the bias fit the LDS ring");
+    constexpr int TS = CW * TN;                    // columns staged per pass
+    constexpr int ROW = 4 * TS + 16;               // bytes per staged row (fp32)
+    constexpr int CPR = TS / 8;                    // pieces of 8 outputs per row
+    constexpr int WMS = BM / (32 * FM);            // wave rows of the tile
+    constexpr int PB = WMS * 32 * CPR;             // pieces per pass
+    static_assert(FN * 32 == TN, "one wave column holds FN fragments");
+    const int lm = lane & 31, lq = (lane >> 5) * 4;
+    const int wr = rb / (32 * FM);
+    const EpiEx& ex = p.ex;
+    const float alpha = p.alpha, beta = ex.out_fp8 ? 0.0f : p.beta;
+    // the tile's bias values, once, behind the staging rows (read after the barrier)
+    float* sbias = reinterpret_cast<float*>(smem + WMS * 32 * ROW);
+    for (int j = threadIdx.x; j < BN; j += NT) sbias[j] = n0 + j < p.N ? ex_bias(ex, n0 + j) : 0.0f;
+#pragma unroll
+    for (int tm = 0; tm < FM; ++tm) {
+#pragma unroll
+        for (int h = 0; h < WN / CW; ++h) {
+            __syncthreads();
+            if (wn / CW == h) {
+                char* row = smem + (wr * 32 + lm) * ROW + 4 * (wn % CW) * TN;
+#pragma unroll
+                for (int tn = 0; tn < FN; ++tn)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<f32x4*>(row + 4 * (tn * 32 + 8 * g + lq)) =
+                            f32x4{alpha * acc[tn][tm][4 * g], alpha * acc[tn][tm][4 * g + 1],
+                                  alpha * acc[tn][tm][4 * g + 2], alpha * acc[tn][tm][4 * g + 3]};
+            }
+            __syncthreads();
+#pragma unroll 2
+            for (int i = threadIdx.x; i < PB; i += NT) {
+                const int rr = i / CPR, c = i - rr * CPR;
+                const int m = m0 + (rr >> 5) * (32 * FM) + tm * 32 + (rr & 31);
+                const int n = n0 + h * TS + c * 8;
+                if (m >= p.M || n >= p.N) continue;
+                const int nv = p.N - n < 8 ? p.N - n : 8;
+                const char* src = smem + rr * ROW + c * 32;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+                float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                const int64_t idx = (int64_t)m * p.ldc + n;
+                if (beta != 0.0f) {
+                    const uint16_t* cp = reinterpret_cast<const uint16_t*>(p.C) + idx;
+                    if (nv == 8) {
+                        const u32x4 old = *reinterpret_cast<const u32x4*>(cp);
+                        const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            v[2 * j] = __builtin_fmaf(beta, to_f32<DT>((uint16_t)(ow[j] & 0xffff)),
+                                                      v[2 * j]);
+                            v[2 * j + 1] =
+                                __builtin_fmaf(beta, to_f32<DT>((uint16_t)(ow[j] >> 16)), v[2 * j + 1]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (e < nv) v[e] = __builtin_fmaf(beta, to_f32<DT>(cp[e]), v[e]);
+                    }
+                }
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(sbias + h * TS + c * 8);
+                const f32x4 b1 = *reinterpret_cast<const f32x4*>(sbias + h * TS + c * 8 + 4);
+                const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = ex_act(ex.act, v[e] + b[e]);
+                if (ex.out_fp8) {
+                    const float q0[4] = {y[0] * ex.inv_scale, y[1] * ex.inv_scale,
+                                         y[2] * ex.inv_scale, y[3] * ex.inv_scale};
+                    const float q1[4] = {y[4] * ex.inv_scale, y[5] * ex.inv_scale,
+                                         y[6] * ex.inv_scale, y[7] * ex.inv_scale};
+                    const uint32_t w0 = e4m3_code4(q0), w1 = e4m3_code4(q1);
+                    uint8_t* c8 = reinterpret_cast<uint8_t*>(p.C) + idx;
+                    if (nv == 8) {
+                        __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(c8));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (e < nv) c8[e] = (uint8_t)((e < 4 ? w0 : w1) >> (8 * (e & 3)));
+                    }
+                } else {
+                    uint16_t* cp = reinterpret_cast<uint16_t*>(p.C) + idx;
+                    if (nv == 8) {
+                        __builtin_nontemporal_store(
+                            u32x4{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3]),
+                                  pack2<DT>(y[4], y[5]), pack2<DT>(y[6], y[7])},
+                            reinterpret_cast<u32x4*>(cp));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (e < nv) cp[e] = from_f32<DT>(y[e]);
+                    }
                 }
             }
         }

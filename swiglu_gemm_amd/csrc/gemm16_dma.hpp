@@ -410,6 +410,14 @@ __device__ __forceinline__ void dma_epilogue(
             p, acc, smem, m0, n0, wm * TM, W12 ? wn * (TN / 2) : wn * TN, lane);
     } else if constexpr (EPI == EPI_GEMM_EX) {
         static_assert(D::LDS >= D::NW * 32 * 36 * 4, "EX staging fits the LDS ring");
+        // finished as whole row pieces from fp32 staging (measured: see the design notes)
+        if constexpr (staged_wave_cols<BM, BN, FM, WN, D::LDS, 4 * BN>() > 0) {
+            if ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc & 7) == 0) {
+                epilogue_gemm_ex_rows_lds<DT_OUT, FM, FN, BM, BN, WN, 64 * WM * WN, D::LDS>(
+                    p, acc, smem, m0, n0, wm * TM, wn, lane);
+                return;
+            }
+        }
         __syncthreads();
         // full tiles: the finished values leave through a row buffer as whole lines
         constexpr int FRAG = D::NW * 32 * 36 * 4, WMS = BM / (32 * FM), NT = 64 * WM * WN;
@@ -445,10 +453,10 @@ __device__ __forceinline__ void dma_epilogue(
         // 32-row block keep the register epilogue.
         // beta != 0: C_old read and C written as whole lines (measured: see the design
         // notes)
-        if constexpr (EPI == EPI_GEMM && (BM / (32 * FM)) * 32 * (4 * TN + 16) <= D::LDS) {
+        if constexpr (EPI == EPI_GEMM && staged_wave_cols<BM, BN, FM, WN, D::LDS, 0>() > 0) {
             if (p.beta != 0.0f && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 &&
                 (p.ldc & 7) == 0) {
-                epilogue_gemm_rows_beta_lds<DT_OUT, FM, FN, BM, BN, WN, 64 * WM * WN>(
+                epilogue_gemm_rows_beta_lds<DT_OUT, FM, FN, BM, BN, WN, 64 * WM * WN, D::LDS>(
                     p, acc, smem, m0, n0, wm * TM, wn, lane);
                 return;
             }
