@@ -38,7 +38,9 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 // EPI_GEMM_EX: y = act(alpha*acc + beta*C_old + bias[n]), stored in DT or, for an
-// e4m3 output, as the e4m3fn code of y * inv_scale.  Each wave stages one 32 x 32
+// e4m3 output, as the e4m3fn code of y * inv_scale.  This form serves the register-
+// staged and ping-pong kernels, and the direct-to-LDS kernel when C is not 16-byte
+// aligned or ldc is not a multiple of 8 (else epilogue_gemm_ex_rows_lds).  Each wave stages one 32 x 32
 // fp32 fragment at a time in a region of the (by now idle) LDS ring of its own, and
 // a rolled loop then finishes four consecutive columns per lane (row-contiguous
 // stores).  The accumulator is only ever indexed by constants: with the
@@ -55,24 +57,12 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// ROWS_OSZ = 0: each finished quad is stored to C directly.  ROWS_OSZ = 1 / 2 (full
-// tile, C 16-byte aligned, ldc * OSZ a multiple of 16; BM, BN, NT the tile and
-// work-group size, m0 / n0 the tile origin): the finished output values (e4m3 codes /
-// 16-bit) go into a row buffer in LDS behind the fragment regions instead, one 32-row
-// block of every wave at a time, and every thread then stores whole 16-byte row pieces
-// non-temporally (whole lines; measured against the direct quad stores: see the design
-// notes).
-template <int DT, int FM, int FN, int ROWS_OSZ = 0, int BM = 0, int BN = 0, int NT = 0>
+template <int DT, int FM, int FN>
 __device__ __forceinline__ void epilogue_gemm_ex_lds(const Gemm16Params& p, f32x16 (&acc)[FN][FM],
                                                      char* smem, int mb, int nb, int wave,
-                                                     int lane, int m0 = 0, int n0 = 0) {
+                                                     int lane) {
     constexpr int LD = 36;                                 // floats per staged row (+4 pad)
     float* frag = reinterpret_cast<float*>(smem) + wave * (32 * LD);
-    constexpr int ROW = ROWS_OSZ * BN + 16;                // row buffer: bytes per row
-    constexpr int CPR = ROWS_OSZ * BN / 16;                // 16-byte pieces per row
-    constexpr int WMS = ROWS_OSZ ? BM / (32 * FM) : 1;     // wave rows of the tile
-    char* rows = smem + (NT / 64) * 32 * LD * 4;           // behind the fragment regions
-    const int wr = ROWS_OSZ ? (mb - m0) / (32 * FM) : 0;   // the wave's row of waves
     const EpiEx& ex = p.ex;
     const float alpha = p.alpha, beta = ex.out_fp8 ? 0.0f : p.beta;
     const int lm = lane & 31, lq = (lane >> 5) * 4;
@@ -104,10 +94,10 @@ __device__ __forceinline__ void epilogue_gemm_ex_lds(const Gemm16Params& p, f32x
             for (int j = 0; j < 4; ++j) {   // two independent quads per pass overlap
                 const int r = (lane >> 3) + 8 * j;         // quad q = lane + 64j: row q/8
                 const int m = mb + tm * 32 + r;
-                if (!ROWS_OSZ && (m >= p.M || valid <= 0)) continue;
+                if (m >= p.M || valid <= 0) continue;
                 const int64_t idx = (int64_t)m * p.ldc + n;
                 f32x4 v = *reinterpret_cast<const f32x4*>(frag + r * LD + c4);
-                const bool vec = ROWS_OSZ || (p.vec_c && valid == 4);
+                const bool vec = p.vec_c && valid == 4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] *= alpha;
                 if (beta != 0.0f) {
@@ -127,18 +117,7 @@ __device__ __forceinline__ void epilogue_gemm_ex_lds(const Gemm16Params& p, f32x
                 f32x4 y;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) y[e] = ex_act(ex.act, v[e] + bq[tn][e]);
-                if constexpr (ROWS_OSZ != 0) {
-                    // tile row wr*TM + tm*32 + r is row wr*32 + r of the block buffer
-                    char* dst = rows + (wr * 32 + r) * ROW + (nb - n0 + tn * 32 + c4) * ROWS_OSZ;
-                    if constexpr (ROWS_OSZ == 1) {
-                        const float ys[4] = {y[0] * ex.inv_scale, y[1] * ex.inv_scale,
-                                             y[2] * ex.inv_scale, y[3] * ex.inv_scale};
-                        *reinterpret_cast<uint32_t*>(dst) = e4m3_code4(ys);
-                    } else {
-                        *reinterpret_cast<u32x2*>(dst) =
-                            u32x2{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
-                    }
-                } else if (ex.out_fp8) {
+                if (ex.out_fp8) {
                     uint8_t* c8 = reinterpret_cast<uint8_t*>(p.C) + idx;
                     const float ys[4] = {y[0] * ex.inv_scale, y[1] * ex.inv_scale,
                                          y[2] * ex.inv_scale, y[3] * ex.inv_scale};
@@ -165,20 +144,6 @@ __device__ __forceinline__ void epilogue_gemm_ex_lds(const Gemm16Params& p, f32x
                 }
             }
             __builtin_amdgcn_wave_barrier();
-        }
-        if constexpr (ROWS_OSZ != 0 && tn == FN - 1) {
-            // block tm of every wave is in the row buffer: store it, then free it
-            __syncthreads();
-            char* C = reinterpret_cast<char*>(p.C);
-            for (int i = threadIdx.x; i < WMS * 32 * CPR; i += NT) {
-                const int rr = i / CPR, cc = i - rr * CPR;
-                const int row = (rr >> 5) * (32 * FM) + tm * 32 + (rr & 31);
-                const u32x4 v = *reinterpret_cast<const u32x4*>(rows + rr * ROW + cc * 16);
-                __builtin_nontemporal_store(
-                    v, reinterpret_cast<u32x4*>(C + ((int64_t)(m0 + row) * p.ldc + n0) * ROWS_OSZ +
-                                                cc * 16));
-            }
-            __syncthreads();
         }
     });
 }
@@ -493,8 +458,10 @@ __device__ __forceinline__ void epilogue_gemm_ex_rows_lds(const Gemm16Params& p,
     const int wr = rb / (32 * FM);
     const EpiEx& ex = p.ex;
     const float alpha = p.alpha, beta = ex.out_fp8 ? 0.0f : p.beta;
-    // the tile's bias values, once, behind the staging rows (read after the barrier)
+    // the tile's bias values, once, behind the staging rows; written only after every
+    // wave is past its last fragment reads of the ring (read after the next barrier)
     float* sbias = reinterpret_cast<float*>(smem + WMS * 32 * ROW);
+    __syncthreads();
     for (int j = threadIdx.x; j < BN; j += NT) sbias[j] = n0 + j < p.N ? ex_bias(ex, n0 + j) : 0.0f;
 #pragma unroll
     for (int tm = 0; tm < FM; ++tm) {

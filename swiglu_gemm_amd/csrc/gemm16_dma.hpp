@@ -418,24 +418,9 @@ __device__ __forceinline__ void dma_epilogue(
                 return;
             }
         }
+        // C not 16-byte aligned or ldc not a multiple of 8: quads stored from the
+        // fragment staging
         __syncthreads();
-        // full tiles: the finished values leave through a row buffer as whole lines
-        constexpr int FRAG = D::NW * 32 * 36 * 4, WMS = BM / (32 * FM), NT = 64 * WM * WN;
-        const int osz = p.ex.out_fp8 ? 1 : 2;
-        if (m0 + BM <= p.M && n0 + BN <= p.N && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 &&
-            ((p.ldc * osz) & 15) == 0) {
-            if (p.ex.out_fp8) {
-                if constexpr (FRAG + WMS * 32 * (BN + 16) <= D::LDS) {
-                    epilogue_gemm_ex_lds<DT_OUT, FM, FN, 1, BM, BN, NT>(
-                        p, acc, smem, m0 + wm * TM, n0 + wn * TN, wave, lane, m0, n0);
-                    return;
-                }
-            } else if constexpr (FRAG + WMS * 32 * (2 * BN + 16) <= D::LDS) {
-                epilogue_gemm_ex_lds<DT_OUT, FM, FN, 2, BM, BN, NT>(
-                    p, acc, smem, m0 + wm * TM, n0 + wn * TN, wave, lane, m0, n0);
-                return;
-            }
-        }
         epilogue_gemm_ex_lds<DT_OUT, FM, FN>(p, acc, smem, m0 + wm * TM, n0 + wn * TN, wave, lane);
     } else {
         if constexpr (EPI == EPI_PARTIAL && (BM / (32 * FM)) * 32 * (4 * BN + 16) <= D::LDS) {

@@ -118,9 +118,11 @@ def check_ex(dtype, ta, tb, M, N, K, seed, act, bdt, beta=0.3, out8=False, ld_mo
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32", "e4m3"])
 def test_epilogue_tile_kernels(dtype, act):
     """Multi-tile ragged shapes on the large-tile kernels (direct-to-LDS for the
-    aligned 16-bit / e4m3 rows), bias in fp32 and in bf16."""
+    aligned 16-bit / e4m3 rows), bias in fp32 and in bf16; C rows of 522 elements
+    (ldc not a multiple of 8) take the quad-store form of the epilogue."""
     check_ex(dtype, "N", "N", 300, 520, 256, 400, act, "f32")
     check_ex(dtype, "N", "T", 257, 384, 512, 401, act, "bf16")
+    check_ex(dtype, "N", "T", 300, 522, 256, 402, act, "f32", ld_mode="tight")
 
 
 @pytest.mark.parametrize("act", ACTS)
