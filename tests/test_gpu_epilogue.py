@@ -245,3 +245,29 @@ def test_fused_qkv_projection_is_one_gemm():
     ref = oracle.gemm("N", "N", M, 3 * d, d, 1.0, X, d, Wqkv, 3 * d, 0.0,
                       np.zeros((M, 3 * d), np.uint16), 3 * d, "bf16")
     assert_close(oracle.decode(fused, "bf16"), ref, "bf16", d, "qkv")
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 2048, 4864, 896), ("e4m3", 2048, 2048, 2048)])
+def test_epilogue_repeatable(dtype, M, N, K):
+    """Repeated calls give identical bits (a wave writing LDS before every wave has
+    left the ring would show here): beta + bias + GELU, and the e4m3 output."""
+    import swiglu_gemm_amd as sg
+    p, scale = case(dtype, "N", "N", M, N, K, 460, ld_mode="tight")
+    A, B = to_dev(p["A"], dtype), to_dev(p["B"], dtype)
+    bias = to_dev(bias_vec(N, "f32", 461), "f32")
+    od = out_dtype(dtype)
+    print("repeatable gemm_ex %s %dx%dx%d" % (dtype, M, N, K), flush=True)
+    outs = []
+    for _ in range(5):
+        C = to_dev(p["C"], od)
+        C8 = torch.zeros((M, N), dtype=torch.uint8, device="cuda:0")
+        sg.gemm_ex(A, B, C, alpha=0.7 * scale, beta=0.5, bias=bias, activation="gelu",
+                   dtype=DT_CODE[dtype])
+        sg.gemm_ex(A, B, C8, alpha=0.7 * scale, bias=bias, activation="silu", out_scale=0.125,
+                   dtype=DT_CODE[dtype])
+        torch.cuda.synchronize()
+        outs.append((from_dev(C), from_dev(C8)))
+    desc = sg.last_config()
+    assert "dma" in desc, desc
+    for o in outs[1:]:
+        assert bits_equal(o[0], outs[0][0]) and bits_equal(o[1], outs[0][1]), desc
