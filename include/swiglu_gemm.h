@@ -192,8 +192,8 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y,
  *  5 M, 6 N, 7 K   >= 0.
  *  8 dtype   as sg_swiglu_gemm.   9 scale_a, 10 scale_w   as sg_swiglu_gemm.
  *  11 stream hipStream_t (void*).
- * Shapes the direct kernel cannot take (K not a multiple of the K tile, rows not
- * 16-byte multiples, unaligned pointers) are run by interleaving W1, W2 into a
+ * Shapes the direct kernel cannot take (rows of A, W1 or W2 that are not 16-byte
+ * multiples, unaligned pointers) are run by interleaving W1, W2 into a
  * library-owned buffer (grown on demand, freed by sg_release) and calling
  * sg_swiglu_gemm; calls on several streams of one device must not overlap then.
  * Quick returns: M == 0 or N == 0 does nothing; K == 0 writes Y = 0.
