@@ -357,8 +357,8 @@ constexpr int staged_wave_cols() {
     return 0;
 }
 
-// The GEMM epilogue with beta != 0, staged so that C_old is read and C written as
-// whole 16-byte row pieces.  One 32-row block (tm) of every wave row and CW wave
+// The GEMM epilogue with beta != 0 (and with beta = 0 on edge tiles), staged so that
+// C_old is read (never at beta = 0) and C written as whole 16-byte row pieces.  One 32-row block (tm) of every wave row and CW wave
 // columns (pass h; CW from staged_wave_cols) at a time, the waves of those columns
 // write alpha * acc in fp32 into LDS rows; all threads then read 8 values of C_old,
 // form alpha *
@@ -412,20 +412,26 @@ __device__ __forceinline__ void epilogue_gemm_rows_beta_lds(const Gemm16Params& 
                 const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
                 uint16_t* cp = C + (int64_t)m * p.ldc + n;
                 if (n + 8 <= p.N) {
-                    const u32x4 old = *reinterpret_cast<const u32x4*>(cp);
-                    const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
                     uint32_t o[4];
+                    if (beta != 0.0f) {
+                        const u32x4 old = *reinterpret_cast<const u32x4*>(cp);
+                        const uint32_t ow[4] = {old.x, old.y, old.z, old.w};
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        o[j] = pack2<DT>(
-                            __builtin_fmaf(beta, to_f32<DT>((uint16_t)(ow[j] & 0xffff)), v[2 * j]),
-                            __builtin_fmaf(beta, to_f32<DT>((uint16_t)(ow[j] >> 16)), v[2 * j + 1]));
+                        for (int j = 0; j < 4; ++j)
+                            o[j] = pack2<DT>(
+                                __builtin_fmaf(beta, to_f32<DT>((uint16_t)(ow[j] & 0xffff)), v[2 * j]),
+                                __builtin_fmaf(beta, to_f32<DT>((uint16_t)(ow[j] >> 16)), v[2 * j + 1]));
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) o[j] = pack2<DT>(v[2 * j], v[2 * j + 1]);
+                    }
                     *reinterpret_cast<u32x4*>(cp) = u32x4{o[0], o[1], o[2], o[3]};
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         if (n + e < p.N)
-                            cp[e] = from_f32<DT>(__builtin_fmaf(beta, to_f32<DT>(cp[e]), v[e]));
+                            cp[e] = from_f32<DT>(
+                                beta != 0.0f ? __builtin_fmaf(beta, to_f32<DT>(cp[e]), v[e]) : v[e]);
                 }
             }
         }

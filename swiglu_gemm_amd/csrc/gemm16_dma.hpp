@@ -436,10 +436,11 @@ __device__ __forceinline__ void dma_epilogue(
         // fp16 / bf16 8192^3 3-4 % and the e4m3 4096 x 22016 x 4096 GEMM 9 % faster; a
         // single round, 2048 x 9728 x 896, 2.5 % slower); rings too small for a staged
         // 32-row block keep the register epilogue.
-        // beta != 0: C_old read and C written as whole lines (measured: see the design
-        // notes)
+        // beta != 0, and edge tiles at beta = 0: C_old read and C written as whole lines
+        // (measured: see the design notes)
         if constexpr (EPI == EPI_GEMM && staged_wave_cols<BM, BN, FM, WN, D::LDS, 0>() > 0) {
-            if (p.beta != 0.0f && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 &&
+            const bool edge = m0 + BM > p.M || n0 + BN > p.N;
+            if ((p.beta != 0.0f || edge) && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 &&
                 (p.ldc & 7) == 0) {
                 epilogue_gemm_rows_beta_lds<DT_OUT, FM, FN, BM, BN, WN, 64 * WM * WN, D::LDS>(
                     p, acc, smem, m0, n0, wm * TM, wn, lane);
