@@ -458,7 +458,7 @@ def pmc_swiglu_summarize(fetch_csv, write_csv, sq_csv):
         copy = [d[counter] for d in ds if "copybuffer" in d["name"].lower()]
         scale[counter] = COPY_BYTES / (max(copy) * 1024.0)
     lines = ["# Counters of the fused SwiGLU kernels (HBM bytes, MFMA busy, LDS), one MI355X", "",
-             "Commands (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`),",
+             "Commands (repository root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`),",
              "one counter set per run:", "", "```",
              "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/f -o f -- "
              "python <repo>/bench.py --pmc-probe-swiglu",
@@ -601,7 +601,7 @@ def stage_sweep_summarize(trace_csv, sweep_jsonl):
         r = least_squares(lambda x: (model(x, occ) - T) / T, x0, bounds=(lb, np.inf))
         fits[occ] = r.x
     lines = ["# Pipeline depth and tile study: fp16 8192^3 NN GEMM on one MI355X", "",
-             "Commands (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "Commands (repository root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`):", "",
              "```", "rocprofv3 --kernel-trace --output-format csv -d <out> -o sw -- "
              "python <repo>/bench.py --stage-sweep > sweep.jsonl",
              "python bench.py --stage-sweep-summarize <out>/sw_kernel_trace.csv sweep.jsonl", "```", "",
@@ -746,7 +746,7 @@ def decode_summarize(trace_csv, jsonl):
     cases = [json.loads(l) for l in open(jsonl) if l.startswith('{"decode_case"')]
     assert len(segs) == len(cases), (len(segs), len(cases))
     lines = ["# Decode-shaped GEMM / SwiGLU (1..32 rows), weights cold in HBM, one MI355X", "",
-             "Commands (repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "Commands (repository root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`):", "",
              "```", "rocprofv3 --kernel-trace --output-format csv -d <out> -o dec -- "
              "python <repo>/bench.py --decode > decode.jsonl",
              "python bench.py --decode-summarize <out>/dec_kernel_trace.csv decode.jsonl", "```", "",
