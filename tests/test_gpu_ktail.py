@@ -180,3 +180,12 @@ def test_ktail_swiglu(dtype, M, N, K):
     desc = sg.last_config()
     assert desc.startswith("swiglu_w12") and "via W_fused" not in desc, desc
     assert_close(oracle.decode(from_dev(Y), "bf16"), ref, dtype, K, desc)
+
+
+@pytest.mark.parametrize("dtype,M,N,K,lda", [("bf16", 16, 4096, 1000, None), ("f16", 1, 3000, 2049, None),
+                                             ("e4m3", 8, 2048, 1040, None), ("e4m3", 32, 1024, 1000, 1008)])
+def test_ktail_decode_sizes(dtype, M, N, K, lda):
+    """1..32 token rows with a K tail: the decode kernels need whole 128-byte K tiles,
+    so these run on the tile kernels with the tail (weights stored N x K)."""
+    desc = check_full(dtype, "N", "T", M, N, K, 680 + M, lda=lda, ldb=lda)
+    assert "dma" in desc and not desc.startswith("decode"), desc
