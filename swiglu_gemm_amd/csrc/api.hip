@@ -170,13 +170,14 @@ int pick_splits(const Cfg16& c, const Problem16& q) {
 // rate from bf16 512 x 4096 x 4096 NT, one round of 256 tiles in 30.6 us; 256 x
 // 192: fp16 4096 x {3072, 6144} x 4096 and 8192 x 3072 x 4096, one and two full
 // rounds, 101.7, 186.1 and 184.5 us against 119.8, 210.8 and 209.8 us for the
-// previous choice.)
+// previous choice; 128 x 192: bf16 SwiGLU M = 512, fused width 9728, one round of
+// 204 tiles, 15.7-16.0 us against 17.6 us for 152 tiles of 128 x 256.)
 struct Cand16 {
     int id;
     double tf_per_cu;
 };
 constexpr Cand16 kCand16[] = {{10, 4.7}, {24, 5.0}, {46, 4.6}, {13, 3.6},
-                               {32, 3.6}, {6, 3.4},  {44, 2.43}};
+                               {32, 3.6}, {48, 3.0}, {6, 3.4}, {44, 2.43}};
 constexpr double kTileOverheadUs = 3.0;   // pipeline fill + epilogue per tile
 constexpr double kSplitBytesPerUs = 4e6;  // fp32 partials: written, then read back
 constexpr double kSplitLaunchUs = 5.0;    // the reduction kernel

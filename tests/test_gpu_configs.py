@@ -14,7 +14,7 @@ from helpers import assert_close, bits_equal, from_dev, split_count, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-CFGS16 = list(range(14)) + [18, 19, 20, 22] + list(range(24, 33)) + [43, 44, 46]   # every 16-bit id
+CFGS16 = list(range(14)) + [18, 19, 20, 22] + list(range(24, 33)) + [43, 44, 46, 48]   # every 16-bit id
 WIDE = [24, 25, 26]                # 320-column tiles (640-byte LDS rows)
 TRANS = ["NN", "NT", "TN", "TT"]
 
@@ -86,7 +86,7 @@ def test_output_rounding_bit_exact(cfg, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("cfg", [10, 24, 46, 13, 30, 32, 43, 44, 5, 20])
+@pytest.mark.parametrize("cfg", [10, 24, 46, 48, 13, 30, 32, 43, 44, 5, 20])
 def test_output_rounding_bit_exact_many_tiles(cfg, dtype):
     """More work-groups than one round of the CUs: the row-staged epilogue of the
     direct-to-LDS kernels (full tiles) next to the register epilogue (edge tiles:

@@ -103,7 +103,7 @@ def test_partial_chunks_4097x3001x2049(tr):
     assert_close(got[rows, :N], ref, "bf16", K, desc)
 
 
-CFG16 = [10, 24, 46, 13, 32, 6, 44, 30, 5, 3, 11, 12, 27]
+CFG16 = [10, 24, 46, 48, 13, 32, 6, 44, 30, 5, 3, 11, 12, 27]
 
 
 @pytest.mark.parametrize("K", [40, 1000, 2049])
