@@ -358,15 +358,15 @@ constexpr int staged_wave_cols() {
 }
 
 // The GEMM epilogue with beta != 0 (and with beta = 0 on edge tiles), staged so that
-// C_old is read (never at beta = 0) and C written as whole 16-byte row pieces.  One 32-row block (tm) of every wave row and CW wave
-// columns (pass h; CW from staged_wave_cols) at a time, the waves of those columns
-// write alpha * acc in fp32 into LDS rows; all threads then read 8 values of C_old,
-// form alpha *
-// acc + beta * C_old in fp32 (one fma) and store the 8 values rounded once.  Pieces
-// past M are skipped and the piece that N cuts goes element by element, so edge
-// tiles take this path too (C must be 16-byte aligned with ldc a multiple of 8).
-// Same arithmetic as the register epilogue, so the outputs are bit-identical.
-// Called by every thread after the main loop.
+// C_old is read (never at beta = 0) and C written as whole 16-byte row pieces.  For
+// one 32-row block (tm) of every wave row and CW wave columns (pass h; CW from
+// staged_wave_cols) at a time, the waves of those columns write alpha * acc in fp32
+// into LDS rows; all threads then read 8 values of C_old, form alpha * acc + beta *
+// C_old in fp32 (one fma) and store the 8 values rounded once.  Pieces past M are
+// skipped and the piece that N cuts goes element by element, so edge tiles take this
+// path too (C must be 16-byte aligned with ldc a multiple of 8).  Same arithmetic as
+// the register epilogue, so the outputs are bit-identical.  Called by every thread
+// after the main loop.
 template <int DT, int FM, int FN, int BM, int BN, int WN, int NT, int LDSB>
 __device__ __forceinline__ void epilogue_gemm_rows_beta_lds(const Gemm16Params& p,
                                                             f32x16 (&acc)[FN][FM], char* smem,
