@@ -68,10 +68,10 @@ typedef enum {
  * Quick returns: M == 0 or N == 0 does nothing; K == 0 or alpha == 0 computes
  * C = beta * C_old without reading A or B.
  * Alignment: any element-aligned pointers and leading dimensions are accepted.
- * The direct-to-LDS kernels run when A and B are 16-byte aligned and lda, ldb
- * times the element size are multiples of 16 (any M, N, K); other fp16 / bf16
- * problems run on a register-staged kernel, other e4m3 problems on a kernel with
- * one thread per output.
+ * For fp16, bf16 and e4m3 the direct-to-LDS kernels run when A and B are 16-byte
+ * aligned and lda, ldb times the element size are multiples of 16 (any M, N, K);
+ * other fp16 / bf16 problems run on a register-staged kernel, other e4m3 problems
+ * on a kernel with one thread per output.
  * Invalid: trans flag (-1/-2), negative size (-3/-4/-5), NULL A/B when they are
  * read (-7/-9), ld too small (-8/-10/-13), NULL C (-12), unknown dtype (-14).
  */
