@@ -26,6 +26,7 @@ Prints ONE JSON line.
 
 Counter helpers (used to produce the committed HBM-traffic figure):
     python bench.py --pmc-probe            # copy of a known size, then 3 GEMM launches
+    python bench.py --pmc-probe-nt         # bf16 GEMM, B stored N x K, beside hipBLASLt
     python bench.py --pmc-summarize FETCH.csv WRITE.csv   # -> profiles/traffic_*.json
 
 Power-limited MFMA ceiling (context for roofline.frac, a separate run):
@@ -350,6 +351,30 @@ def pmc_probe():
         sg.gemm(A, B, C)
     torch.cuda.synchronize()
     print("pmc probe done: %s" % sg.last_config(), flush=True)
+
+
+def pmc_probe_nt():
+    """Run under rocprofv3 --pmc: the bf16 8192 x 4096 x 4096 GEMM with B stored N x K
+    (both operands k-contiguous), three launches of hipBLASLt (torch.mm) before and
+    after three of this library, on the same seeded tensors."""
+    import torch
+    import swiglu_gemm_amd as sg
+    from swiglu_gemm_amd import inputs
+    sg.lib()
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    A = torch.randn(8192, 4096, generator=gen).bfloat16().to("cuda:0")
+    B = torch.randn(4096, 4096, generator=gen).bfloat16().to("cuda:0")   # N x K
+    C = torch.empty(8192, 4096, dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(3):
+        torch.mm(A, B.t())
+    torch.cuda.synchronize()
+    for _ in range(3):
+        sg.gemm(A, B, C, transB="T")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mm(A, B.t())
+    torch.cuda.synchronize()
+    print("pmc probe nt done: %s" % sg.last_config(), flush=True)
 
 
 def pmc_summarize(fetch_csv, write_csv):
@@ -842,6 +867,8 @@ def main():
     ap.add_argument("--pmc-probe", action="store_true")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--pmc-probe-swiglu", action="store_true")
+    ap.add_argument("--pmc-probe-nt", action="store_true",
+                    help="bf16 GEMM with B stored N x K: this library beside hipBLASLt")
     ap.add_argument("--pmc-swiglu-summarize", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "SQ_CSV"))
     ap.add_argument("--mfma-ceiling", action="store_true")
     ap.add_argument("--stage-sweep", action="store_true")
@@ -871,6 +898,9 @@ def main():
         return
     if args.pmc_probe_swiglu:
         pmc_probe_swiglu()
+        return
+    if args.pmc_probe_nt:
+        pmc_probe_nt()
         return
     if args.pmc_swiglu_summarize:
         pmc_swiglu_summarize(*args.pmc_swiglu_summarize)
