@@ -107,6 +107,11 @@ def _check(status: int, what: str) -> None:
 
 
 # ---------------------------------------------------------------- torch glue
+# Every wrapper checks, before the library is called, that the tensors it passes
+# hold what the C ABI will read and write (shapes, dtypes, row strides, storage
+# extent): the library sees bare pointers, so a short or mistyped tensor would
+# otherwise send the kernels past its allocation.  The device is checked last,
+# so that every other check can be exercised without a GPU.
 def _dtype_code(t) -> int:
     import torch
     m = {torch.float32: SG_F32, torch.float16: SG_F16, torch.bfloat16: SG_BF16,
@@ -114,6 +119,17 @@ def _dtype_code(t) -> int:
     if t.dtype not in m:
         raise TypeError("unsupported dtype %s" % t.dtype)
     return m[t.dtype]
+
+
+# bytes per element of the operands and of the output, per dtype code
+_IN_SIZE = {SG_F32: 4, SG_F16: 2, SG_BF16: 2, SG_F8E4M3: 1}
+
+
+def _out_dtypes(code: int):
+    """torch dtypes accepted for C / Y when the operands have dtype code `code`."""
+    import torch
+    return {SG_F32: (torch.float32,), SG_F16: (torch.float16,), SG_BF16: (torch.bfloat16,),
+            SG_F8E4M3: (torch.bfloat16,)}[code]
 
 
 def _stream(t):
@@ -129,6 +145,82 @@ def _ld(t) -> int:
     return max(int(t.stride(0)), 1) if t.size(0) > 1 else max(int(t.size(1)), 1)
 
 
+def _span(rows: int, cols: int, ld: int) -> int:
+    """Elements from the first to one past the last of a rows x cols row-major view
+    with row stride ld (0 for an empty view)."""
+    return 0 if rows <= 0 or cols <= 0 else (rows - 1) * ld + cols
+
+
+def _avail(t) -> int:
+    """Elements of t's storage from t's first element to the end of the storage."""
+    return t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+
+
+def _need(t, name: str, elems: int) -> None:
+    if elems > _avail(t):
+        raise ValueError("%s holds %d elements from its first one, the call needs %d"
+                         % (name, _avail(t), elems))
+
+
+def _same_size(t, name: str, code: int, what: str) -> None:
+    if t.element_size() != _IN_SIZE[code]:
+        raise TypeError("%s has %d-byte elements, %s needs %d" % (name, t.element_size(), what,
+                                                                   _IN_SIZE[code]))
+
+
+def _on_gpu(*ts) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("every tensor must be on the GPU")
+
+
+def _contig(t, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc, c_dtypes, batch=1,
+               strides=(0, 0, 0)):
+    """Sizes and leading dimensions of a GEMM call, checked against the tensors."""
+    if ta not in ("N", "T") or tb not in ("N", "T"):
+        raise ValueError("transA and transB must be 'N' or 'T'")
+    if M is None:
+        if A.dim() < 2 or B.dim() < 2:
+            raise ValueError("A and B must have at least 2 dimensions")
+        M = A.size(-1) if ta == "T" else A.size(-2)
+        K = A.size(-2) if ta == "T" else A.size(-1)
+        N = B.size(-2) if tb == "T" else B.size(-1)
+        kb = B.size(-1) if tb == "T" else B.size(-2)
+        if kb != K:
+            raise ValueError("op(A) is %d x %d but op(B) has %d rows" % (M, K, kb))
+    elif N is None or K is None:
+        raise ValueError("give M, N and K together")
+    M, N, K = int(M), int(N), int(K)
+    if M < 0 or N < 0 or K < 0:
+        raise ValueError("M, N and K must be >= 0")
+    lda = (_ld(A) if A.dim() == 2 else int(A.stride(-2))) if lda is None else int(lda)
+    ldb = (_ld(B) if B.dim() == 2 else int(B.stride(-2))) if ldb is None else int(ldb)
+    ldc = (_ld(C) if C.dim() == 2 else int(C.stride(-2))) if ldc is None else int(ldc)
+    _same_size(A, "A", code, "the operand dtype")
+    _same_size(B, "B", code, "the operand dtype")
+    if C.dtype not in c_dtypes:
+        raise TypeError("C has dtype %s, expected one of %s" % (C.dtype, c_dtypes))
+    for t, name in ((A, "A"), (B, "B"), (C, "C")):
+        if t.dim() >= 2 and t.size(-1) > 1 and t.stride(-1) != 1:
+            raise ValueError("%s: the last dimension must be contiguous (stride 1)" % name)
+    sA, sB, sC = strides
+    last = max(int(batch) - 1, 0)
+    if M and K:
+        _need(A, "A", last * sA + (_span(K, M, lda) if ta == "T" else _span(M, K, lda)))
+    if N and K:
+        _need(B, "B", last * sB + (_span(N, K, ldb) if tb == "T" else _span(K, N, ldb)))
+    if M and N:
+        _need(C, "C", last * sC + _span(M, N, ldc))
+    return M, N, K, lda, ldb, ldc
+
+
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N", transB: str = "N",
          dtype: int | None = None, M=None, N=None, K=None, lda=None, ldb=None, ldc=None):
     """C = alpha * op(A) @ op(B) + beta * C, in place on C (2-D row-major tensors on the
@@ -136,17 +228,12 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N", tran
     bf16 and alpha should carry the product of the two per-tensor scales."""
     code = _dtype_code(A) if dtype is None else dtype
     ta, tb = transA.upper(), transB.upper()
-    if M is None:
-        M = A.size(1) if ta == "T" else A.size(0)
-        K = A.size(0) if ta == "T" else A.size(1)
-        N = B.size(0) if tb == "T" else B.size(1)
-    lda = _ld(A) if lda is None else lda
-    ldb = _ld(B) if ldb is None else ldb
-    ldc = _ld(C) if ldc is None else ldc
-    st = lib().sg_gemm(ta.encode(), tb.encode(), int(M), int(N), int(K), float(alpha),
-                       ctypes.c_void_p(A.data_ptr()), int(lda), ctypes.c_void_p(B.data_ptr()),
-                       int(ldb), float(beta), ctypes.c_void_p(C.data_ptr()), int(ldc), code,
-                       _stream(C))
+    M, N, K, lda, ldb, ldc = _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc,
+                                        _out_dtypes(code))
+    _on_gpu(A, B, C)
+    st = lib().sg_gemm(ta.encode(), tb.encode(), M, N, K, float(alpha),
+                       ctypes.c_void_p(A.data_ptr()), lda, ctypes.c_void_p(B.data_ptr()),
+                       ldb, float(beta), ctypes.c_void_p(C.data_ptr()), ldc, code, _stream(C))
     _check(st, "sg_gemm")
     return C
 
@@ -159,24 +246,26 @@ def gemm_ex(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N",
     'none', 'relu', 'gelu', 'gelu_tanh' or 'silu'.  out_scale: None (C has gemm's
     output type) or the per-tensor scale of an e4m3 output (C an e4m3 / uint8
     tensor holding the codes of y / out_scale; beta must be 0)."""
+    import torch
     code = _dtype_code(A) if dtype is None else dtype
     ta, tb = transA.upper(), transB.upper()
-    if M is None:
-        M = A.size(1) if ta == "T" else A.size(0)
-        K = A.size(0) if ta == "T" else A.size(1)
-        N = B.size(0) if tb == "T" else B.size(1)
-    lda = _ld(A) if lda is None else lda
-    ldb = _ld(B) if ldb is None else ldb
-    ldc = _ld(C) if ldc is None else ldc
+    c_dtypes = (torch.float8_e4m3fn, torch.uint8) if out_scale is not None else _out_dtypes(code)
+    M, N, K, lda, ldb, ldc = _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc, c_dtypes)
     if activation not in ACTIVATIONS:
         raise ValueError("unknown activation %r" % activation)
+    if bias is not None:
+        if bias.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+            raise TypeError("bias must be fp32, fp16 or bf16")
+        if bias.dim() != 1 or not bias.is_contiguous() or bias.numel() < N:
+            raise ValueError("bias must be a contiguous vector of at least N = %d values" % N)
+    _on_gpu(A, B, C, bias)
     epi = Epilogue(ctypes.c_void_p(bias.data_ptr()) if bias is not None else None,
                    _dtype_code(bias) if bias is not None else SG_F32, ACTIVATIONS[activation],
                    SG_F8E4M3 if out_scale is not None else -1,
                    float(out_scale) if out_scale is not None else 1.0)
-    st = lib().sg_gemm_ex(ta.encode(), tb.encode(), int(M), int(N), int(K), float(alpha),
-                          ctypes.c_void_p(A.data_ptr()), int(lda), ctypes.c_void_p(B.data_ptr()),
-                          int(ldb), float(beta), ctypes.c_void_p(C.data_ptr()), int(ldc), code,
+    st = lib().sg_gemm_ex(ta.encode(), tb.encode(), M, N, K, float(alpha),
+                          ctypes.c_void_p(A.data_ptr()), lda, ctypes.c_void_p(B.data_ptr()),
+                          ldb, float(beta), ctypes.c_void_p(C.data_ptr()), ldc, code,
                           ctypes.byref(epi), _stream(C))
     _check(st, "sg_gemm_ex")
     return C
@@ -188,33 +277,57 @@ def gemm_strided_batched(A, B, C, batch, strideA, strideB, strideC, alpha: float
                          ldc=None):
     """C_b = alpha * op(A_b) @ op(B_b) + beta * C_b for b < batch, X_b = X + b*strideX
     elements (A, B, C: device tensors whose storage holds every problem; sizes and
-    leading dimensions default to those of the 2-D views given)."""
+    leading dimensions default to those of the last two dimensions given)."""
     code = _dtype_code(A) if dtype is None else dtype
     ta, tb = transA.upper(), transB.upper()
-    if M is None:
-        M = A.size(-1) if ta == "T" else A.size(-2)
-        K = A.size(-2) if ta == "T" else A.size(-1)
-        N = B.size(-2) if tb == "T" else B.size(-1)
-    lda = A.stride(-2) if lda is None else lda
-    ldb = B.stride(-2) if ldb is None else ldb
-    ldc = C.stride(-2) if ldc is None else ldc
-    st = lib().sg_gemm_strided_batched(ta.encode(), tb.encode(), int(M), int(N), int(K),
-                                       float(alpha), ctypes.c_void_p(A.data_ptr()), int(lda),
-                                       int(strideA), ctypes.c_void_p(B.data_ptr()), int(ldb),
+    if int(batch) < 0 or min(int(strideA), int(strideB), int(strideC)) < 0:
+        raise ValueError("batch and strides must be >= 0")
+    M, N, K, lda, ldb, ldc = _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc,
+                                        _out_dtypes(code), batch=int(batch),
+                                        strides=(int(strideA), int(strideB), int(strideC)))
+    _on_gpu(A, B, C)
+    st = lib().sg_gemm_strided_batched(ta.encode(), tb.encode(), M, N, K,
+                                       float(alpha), ctypes.c_void_p(A.data_ptr()), lda,
+                                       int(strideA), ctypes.c_void_p(B.data_ptr()), ldb,
                                        int(strideB), float(beta), ctypes.c_void_p(C.data_ptr()),
-                                       int(ldc), int(strideC), int(batch), code, _stream(C))
+                                       ldc, int(strideC), int(batch), code, _stream(C))
     _check(st, "sg_gemm_strided_batched")
     return C
+
+
+def _swiglu_args(A, W_list, Y, two_n: bool):
+    """M, N, K of a SwiGLU call, with A [M, K], each weight [K, 2N] (two_n) or [K, N]
+    and Y [M, N] contiguous; operands of one dtype, Y bf16 (fp16 for fp16 inputs)."""
+    import torch
+    if A.dim() != 2 or any(w.dim() != 2 for w in W_list):
+        raise ValueError("A and the weights must be 2-D")
+    M, K = int(A.shape[0]), int(A.shape[1])
+    W0 = W_list[0]
+    if two_n and W0.shape[1] % 2:
+        raise ValueError("Wfused must have an even number of columns (gate, up pairs)")
+    N = int(W0.shape[1]) // 2 if two_n else int(W0.shape[1])
+    code = _dtype_code(A)
+    if code == SG_F32:
+        raise TypeError("SwiGLU takes bf16, fp16 or e4m3 operands")
+    _contig(A, "A", (M, K))
+    for i, w in enumerate(W_list):
+        _contig(w, "weight %d" % i, (K, 2 * N if two_n else N))
+        if _dtype_code(w) != code or w.element_size() != A.element_size():
+            raise TypeError("the weights must have A's dtype")
+    if Y.dtype not in _out_dtypes(code):
+        raise TypeError("Y has dtype %s, expected %s" % (Y.dtype, _out_dtypes(code)[0]))
+    _contig(Y, "Y", (M, N))
+    return M, N, K, code
 
 
 def swiglu_gemm(A, Wfused, Y, scale_a: float = 1.0, scale_w: float = 1.0):
     """Y = SiLU(s*A@W1) * (s*A@W2) from the column-interleaved Wfused [K, 2N]
     (s = scale_a*scale_w); A [M, K], Y [M, N], all contiguous."""
-    M, K = A.shape
-    N = Wfused.shape[1] // 2
+    M, N, K, code = _swiglu_args(A, [Wfused], Y, True)
+    _on_gpu(A, Wfused, Y)
     st = lib().sg_swiglu_gemm(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(Wfused.data_ptr()),
-                              ctypes.c_void_p(Y.data_ptr()), int(M), int(N), int(K),
-                              _dtype_code(A), float(scale_a), float(scale_w), _stream(Y))
+                              ctypes.c_void_p(Y.data_ptr()), M, N, K, code, float(scale_a),
+                              float(scale_w), _stream(Y))
     _check(st, "sg_swiglu_gemm")
     return Y
 
@@ -222,12 +335,11 @@ def swiglu_gemm(A, Wfused, Y, scale_a: float = 1.0, scale_w: float = 1.0):
 def swiglu_gemm_w12(A, W1, W2, Y, scale_a: float = 1.0, scale_w: float = 1.0):
     """Y = SiLU(s*A@W1) * (s*A@W2) from separate W1, W2 [K, N] (s = scale_a*scale_w);
     A [M, K], Y [M, N], all contiguous."""
-    M, K = A.shape
-    N = W1.shape[1]
+    M, N, K, code = _swiglu_args(A, [W1, W2], Y, False)
+    _on_gpu(A, W1, W2, Y)
     st = lib().sg_swiglu_gemm_w12(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(W1.data_ptr()),
                                   ctypes.c_void_p(W2.data_ptr()), ctypes.c_void_p(Y.data_ptr()),
-                                  int(M), int(N), int(K), _dtype_code(A), float(scale_a),
-                                  float(scale_w), _stream(Y))
+                                  M, N, K, code, float(scale_a), float(scale_w), _stream(Y))
     _check(st, "sg_swiglu_gemm_w12")
     return Y
 
@@ -235,11 +347,21 @@ def swiglu_gemm_w12(A, W1, W2, Y, scale_a: float = 1.0, scale_w: float = 1.0):
 def interleave_gate_up(W1, W2, out=None):
     """Wfused[:, 0::2] = W1, Wfused[:, 1::2] = W2 (bit-exact), on the GPU."""
     import torch
-    K, N = W1.shape
+    if W1.dim() != 2:
+        raise ValueError("W1 must be 2-D")
+    K, N = int(W1.shape[0]), int(W1.shape[1])
+    _contig(W1, "W1", (K, N))
+    _contig(W2, "W2", (K, N))
+    if W2.dtype != W1.dtype:
+        raise TypeError("W1 and W2 must have one dtype")
     if out is None:
         out = torch.empty((K, 2 * N), dtype=W1.dtype, device=W1.device)
+    _contig(out, "out", (K, 2 * N))
+    if out.element_size() != W1.element_size():
+        raise TypeError("out must have W1's element size")
+    _on_gpu(W1, W2, out)
     st = lib().sg_interleave_gate_up(ctypes.c_void_p(W1.data_ptr()), ctypes.c_void_p(W2.data_ptr()),
-                                     ctypes.c_void_p(out.data_ptr()), int(K), int(N),
+                                     ctypes.c_void_p(out.data_ptr()), K, N,
                                      _dtype_code(W1), _stream(out))
     _check(st, "sg_interleave_gate_up")
     return out
@@ -247,9 +369,18 @@ def interleave_gate_up(W1, W2, out=None):
 
 def silu_mul(G, U, Y):
     """Y = SiLU(G) * U elementwise (contiguous, bf16 or fp16)."""
-    M, N = G.shape
+    import torch
+    if G.dim() != 2:
+        raise ValueError("G must be 2-D")
+    M, N = int(G.shape[0]), int(G.shape[1])
+    if G.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("silu_mul takes bf16 or fp16")
+    for t, name in ((G, "G"), (U, "U"), (Y, "Y")):
+        _contig(t, name, (M, N))
+        if t.dtype != G.dtype:
+            raise TypeError("G, U and Y must have one dtype")
+    _on_gpu(G, U, Y)
     st = lib().sg_silu_mul(ctypes.c_void_p(G.data_ptr()), ctypes.c_void_p(U.data_ptr()),
-                           ctypes.c_void_p(Y.data_ptr()), int(M), int(N), _dtype_code(G),
-                           _stream(Y))
+                           ctypes.c_void_p(Y.data_ptr()), M, N, _dtype_code(G), _stream(Y))
     _check(st, "sg_silu_mul")
     return Y
