@@ -19,9 +19,12 @@
  *   bias 7, largest magnitude 448, no infinities).  Every product is accumulated
  *   in fp32 and rounded to the output type (nearest-even) once, at the end.
  * - Split-K workspace (fp32 partial sums) is owned by the library: one buffer per
- *   device, grown on first need, released by sg_release().  Calls that need it and
- *   run concurrently on different streams of one device are serialised by the
- *   caller (the library does not order streams).
+ *   device, grown on first need (to a power of two, at least 1 MiB), released by
+ *   sg_release().  A call fetches it once and passes that address to each of its
+ *   kernels.  Growth never synchronises the device: the smaller buffer, which work
+ *   enqueued earlier may still read, is kept until sg_release().  Calls that need
+ *   the workspace and run concurrently on different streams of one device are
+ *   serialised by the caller (the library does not order streams).
  * - Problems with 1..32 rows of A ('N') may run on the decode kernels: a persistent
  *   stream-K pass over the weight and, when a column tile is shared by several
  *   work-groups, a second fix-up launch that adds their partial sums (a fixed
@@ -244,8 +247,8 @@ const char* sg_status_string(int status);
  */
 int sg_last_config(char* buf, int len);
 
-/* Frees the library-owned split-K workspace on every device.  Must not be called
- * while enqueued work that uses it is still running. */
+/* Frees the library-owned workspace buffers (current and outgrown) on every device,
+ * after synchronising each device that holds one. */
 void sg_release(void);
 
 #ifdef __cplusplus

@@ -11,6 +11,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "aux_kernels.hpp"
 #include "configs16.hpp"
@@ -54,6 +55,12 @@ bool aligned(const void* p, int bytes) { return ((uintptr_t)p % bytes) == 0; }
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
 
 // ---------------------------------------------------------------- workspace
+// Library-owned device buffers, one per (kind, device), grown on demand.  A call
+// fetches its buffer once and hands that pointer to every kernel it enqueues.
+// Growth never synchronises: the old buffer may still be read by work enqueued
+// earlier (on any stream), so it is retired, not freed, and sg_release() frees the
+// retired buffers with the current ones.  Sizes are rounded up to powers of two
+// (at least 1 MiB), so a buffer is retired at most a few dozen times.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
@@ -63,30 +70,30 @@ std::mutex g_ws_mu;
 // split-weight SwiGLU's fallback for shapes its own kernel cannot take); slot 2:
 // partial sums of the decode path's split column tiles
 constexpr int kSlots = 3;
-Workspace g_ws[kSlots][64];
+constexpr int kMaxDevices = 64;
+Workspace g_ws[kSlots][kMaxDevices];
+std::vector<void*> g_retired[kMaxDevices];
+
+size_t ws_round(size_t bytes) {
+    size_t want = (size_t)1 << 20;
+    while (want < bytes) want <<= 1;
+    return want;
+}
 
 hipError_t workspace(size_t bytes, float** out, int slot = 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lk(g_ws_mu);
     Workspace& w = g_ws[slot][dev];
     if (w.bytes < bytes) {
-        if (w.ptr) {
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return e;
-            e = hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-            if (e != hipSuccess) return e;
-        }
-        size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
-        e = hipMalloc(&w.ptr, want);
-        if (e != hipSuccess) {
-            w.ptr = nullptr;
-            return e;
-        }
+        const size_t want = ws_round(bytes);
+        void* fresh = nullptr;
+        e = hipMalloc(&fresh, want);
+        if (e != hipSuccess) return e;
+        if (w.ptr) g_retired[dev].push_back(w.ptr);
+        w.ptr = fresh;
         w.bytes = want;
     }
     *out = reinterpret_cast<float*>(w.ptr);
@@ -355,9 +362,13 @@ ColSplit plan_col_split(const Problem16& q, int cfg, int splits, int epi) {
     return s;
 }
 
+// Runs one 16-bit / e4m3 problem on the tile kernels.  With split-K the partial
+// sums go to the workspace, whose address is returned in *ws_used for the
+// reduction the caller enqueues next (the same buffer: it is fetched once).
 template <int DT>
 hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* out,
-                 bool out_vec, const char* what, hipStream_t st, int* splits_used) {
+                 bool out_vec, const char* what, hipStream_t st, int* splits_used,
+                 float** ws_used) {
     if (!p.A || !p.B || !out) return hipErrorInvalidValue;           // never launch on NULL
     int cfg = 0, splits = 1;
     choose16(q, &cfg, &splits);
@@ -406,6 +417,7 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
     float* ws = nullptr;
     hipError_t e = workspace((size_t)splits * q.M * q.N * sizeof(float), &ws);
     if (e != hipSuccess) return e;
+    *ws_used = ws;
     p.C = ws;
     p.vec_c = 1;
     set_last(what, cfg, splits);
@@ -546,12 +558,10 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
     p.vec_b = aligned(B, 16) && (ldb % 8 == 0) && (bt.sB % 16 == 0);
     Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 2, bt.n};
     int splits = 1;
-    hipError_t e = run16<DT>(ta, tb, ex.on ? EPI_GEMM_EX : EPI_GEMM, q, p, C,
-                             c_vec_ok(C, ldc, bt.sC, ex), "gemm16", st, &splits);
-    if (e != hipSuccess || splits <= 1) return e;
     float* ws = nullptr;
-    e = workspace((size_t)splits * M * N * sizeof(float), &ws);
-    if (e != hipSuccess) return e;
+    hipError_t e = run16<DT>(ta, tb, ex.on ? EPI_GEMM_EX : EPI_GEMM, q, p, C,
+                             c_vec_ok(C, ldc, bt.sC, ex), "gemm16", st, &splits, &ws);
+    if (e != hipSuccess || splits <= 1) return e;
     hipLaunchKernelGGL(reduce_gemm_kernel<DT>, dim3(grid_1d(M * N)), dim3(256), 0, st, ws, splits,
                        (int)M, (int)N, C, ldc, alpha, beta, ex);
     return hipGetLastError();
@@ -586,8 +596,9 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
     p.vec_b = aligned(B, 16) && (ldb % 16 == 0) && (bt.sB % 16 == 0);
     Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1, bt.n};
     int splits = 1;
+    float* ws = nullptr;
     hipError_t e = run16<DT_E4M3>(ta, tb, ex.on ? EPI_GEMM_EX : EPI_GEMM, q, p, C,
-                                  c_vec_ok(C, ldc, bt.sC, ex), "gemm8", st, &splits);
+                                  c_vec_ok(C, ldc, bt.sC, ex), "gemm8", st, &splits, &ws);
     if (e == hipErrorNotSupported) {
         std::snprintf(g_last_cfg, sizeof(g_last_cfg), "gemm8 generic splits=1");
         for (int64_t z = 0; z < bt.n; ++z) {   // rare path (K tails, odd alignment)
@@ -599,9 +610,6 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
         return hipGetLastError();
     }
     if (e != hipSuccess || splits <= 1) return e;
-    float* ws = nullptr;
-    e = workspace((size_t)splits * M * N * sizeof(float), &ws);
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_gemm_kernel<DT_BF16>, dim3(grid_1d(M * N)), dim3(256), 0, st, ws,
                        splits, (int)M, (int)N, C, ldc, alpha, beta, ex);
     return hipGetLastError();
@@ -989,9 +997,10 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
         if (d != hipErrorNotSupported) return status_of(d);
     }
     int splits = 1;
+    float* ws = nullptr;
     hipError_t e;
     if (dtype == SG_F8E4M3) {
-        e = run16<DT_E4M3>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu8", st, &splits);
+        e = run16<DT_E4M3>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu8", st, &splits, &ws);
         if (e == hipErrorNotSupported) {
             std::snprintf(g_last_cfg, sizeof(g_last_cfg), "swiglu8 generic splits=1");
             hipLaunchKernelGGL(swiglu_e4m3_generic, dim3(grid_1d(M * N)), dim3(256), 0, st,
@@ -1000,14 +1009,11 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
             return status_of(hipGetLastError());
         }
     } else if (out_dt == SG_F16) {
-        e = run16<DT_F16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits);
+        e = run16<DT_F16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits, &ws);
     } else {
-        e = run16<DT_BF16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits);
+        e = run16<DT_BF16>(false, false, EPI_SWIGLU, q, p, Y, yvec, "swiglu16", st, &splits, &ws);
     }
     if (e != hipSuccess || splits <= 1) return status_of(e);
-    float* ws = nullptr;
-    e = workspace((size_t)splits * M * N2 * sizeof(float), &ws);
-    if (e != hipSuccess) return status_of(e);
     const unsigned g = grid_1d(M * N);
     if (out_dt == SG_F16)
         hipLaunchKernelGGL(reduce_swiglu_kernel<DT_F16>, dim3(g), dim3(256), 0, st, ws, splits,
@@ -1175,18 +1181,18 @@ void sg_release(void) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) cur = -1;
-    for (int slot = 0; slot < kSlots; ++slot) {
-        for (int d = 0; d < 64; ++d) {
-            Workspace& w = g_ws[slot][d];
-            if (w.ptr) {
-                if (hipSetDevice(d) == hipSuccess) {
-                    (void)hipDeviceSynchronize();
-                    (void)hipFree(w.ptr);
-                }
-                w.ptr = nullptr;
-                w.bytes = 0;
-            }
+    for (int d = 0; d < kMaxDevices; ++d) {
+        bool any = !g_retired[d].empty();
+        for (int slot = 0; slot < kSlots; ++slot) any = any || g_ws[slot][d].ptr;
+        if (!any) continue;
+        if (hipSetDevice(d) == hipSuccess) {
+            (void)hipDeviceSynchronize();
+            for (int slot = 0; slot < kSlots; ++slot)
+                if (g_ws[slot][d].ptr) (void)hipFree(g_ws[slot][d].ptr);
+            for (void* r : g_retired[d]) (void)hipFree(r);
         }
+        for (int slot = 0; slot < kSlots; ++slot) g_ws[slot][d] = Workspace{};
+        g_retired[d].clear();
     }
     if (cur >= 0) (void)hipSetDevice(cur);
 }
