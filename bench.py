@@ -113,36 +113,82 @@ def to_dev(bits, dtype, torch):
     return t.to("cuda:0")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(p, M, N, K, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of the same GEMM: R full rows of C (all
-    N columns, full K), R chosen to take about budget_s seconds."""
+    """The fp64 oracle on a bounded sample of the same GEMM: R full rows of C (all N
+    columns, full K) on every host core, R chosen to take about budget_s seconds.  The
+    operands are decoded to fp64 once, before the clock starts, so only the oracle's
+    i-p-j loop is timed.  Returns the record and the computed rows (for the error
+    report beside it)."""
     import oracle
     threads = oracle.max_threads()
-    rows_per_batch = threads
-    done = 0
-    t_total = 0.0
+    B = oracle.decode(p["B"], "f16").ravel()
+    batch = 2 * threads
+    done, t_total = 0, 0.0
+    rows_out = []
     while t_total < budget_s and done < M:
-        rows = np.arange(done, min(done + rows_per_batch, M))
-        sub = dict(A=np.ascontiguousarray(p["A"][rows, :]), C=np.ascontiguousarray(p["C"][rows, :]))
+        r1 = min(done + batch, M)
+        a = oracle.decode(np.ascontiguousarray(p["A"][done:r1, :]), "f16").ravel()
+        c = np.zeros((r1 - done) * N)
         t0 = time.perf_counter()
-        oracle.gemm("N", "N", len(rows), N, K, 1.0, sub["A"], p["lda"], p["B"], p["ldb"], 0.0,
-                    sub["C"], p["ldc"], "f16", nthreads=threads)
+        oracle.gemm_f64("N", "N", r1 - done, N, K, 1.0, a, p["lda"], B, p["ldb"], 0.0, c, N,
+                        nthreads=threads)
         t_total += time.perf_counter() - t0
-        done += len(rows)
+        rows_out.append(c.reshape(r1 - done, N))
+        done = r1
     flops = 2.0 * done * N * K
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d rows of the fp16 %dx%dx%d GEMM (full N and K), fp64 i-p-j "
-                      "oracle incl. decode, %.1f s" % (done, M, M, N, K, t_total)}
+    rec = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": "rows 0..%d of the %d-row fp16 %dx%dx%d GEMM (full N and K): the fp64 "
+                     "i-p-j oracle loop on %d threads, operands decoded before timing, %.1f s"
+                     % (done - 1, M, M, N, K, threads, t_total)}
+    return rec, np.concatenate(rows_out, axis=0)
+
+
+def error_report(y, yhat, atol, rtol):
+    """Error of GPU values y against oracle values yhat: largest absolute and relative
+    error, the largest error over max|yhat|, the share of elements more than 1 % off,
+    and the worst error as a fraction of the tolerance atol + rtol*|yhat|."""
+    d = np.abs(y - yhat)
+    a = np.abs(yhat)
+    nz = a > 0
+    return {"elements": int(d.size), "max_abs": float(d.max()),
+            "max_rel": float((d[nz] / a[nz]).max()) if nz.any() else 0.0,
+            "max_abs_over_max_ref": float(d.max() / a.max()) if a.max() > 0 else 0.0,
+            "share_rel_gt_1pct": float(np.count_nonzero(d > 0.01 * a)) / d.size,
+            "worst_over_tolerance": float(np.max(d / (atol + rtol * a)))}
+
+
+def f16_bits_to_f64(bits):
+    return bits.view(np.float16).astype(np.float64)
+
+
+def bf16_bits_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 COLD_BYTES = 512 * 1024 * 1024     # rotate operand copies past the 256 MB last-level cache
 
 
-def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True):
+def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True, keep=None):
     """Fused vs this library's unfused path (vs torch eager) for one SwiGLU size.
     Cold: the weights rotate through enough device copies (> 512 MB in all) that
     W_fused comes from HBM each step; hot: two copies, which the last-level cache
-    keeps.  Two seeded problems; the further copies are device clones."""
+    keeps.  Two seeded problems; the further copies are device clones.  With a dict
+    `keep`, the first problem's inputs and its fused and unfused outputs are stored
+    there (host copies) for the error report."""
     workload = 4 if dtype == "bf16" else 5
     base = []
     for r in range(2):
@@ -184,6 +230,13 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True):
     t_w12 = time_steps(w12, steps, warmup, torch)
     cfg_w12 = sg.last_config()
     t_unfused = time_steps(unfused, steps, warmup, torch)
+    if keep is not None:
+        A, W1, W2, Wf, sa, sw = base[0]
+        sg.swiglu_gemm(A, Wf, Y, sa, sw)
+        keep["fused"] = Y.view(torch.int16).cpu().numpy().view(np.uint16)
+        unfused(0)
+        keep["unfused"] = Y.view(torch.int16).cpu().numpy().view(np.uint16)
+        keep["problem"] = inputs.swiglu_problem(workload, M, N, K, dtype)
     flops = 4.0 * M * N * K
     nbytes = M * K * esz + K * 2 * N * esz + M * N * 2
     tf = flops / (t_fused * 1e-3) / 1e12
@@ -309,11 +362,69 @@ def bench_epilogue(torch, sg, steps, warmup):
 def env_info(torch):
     props = torch.cuda.get_device_properties(0)
     info = {"device": props.name, "compute_units": props.multi_processor_count,
-            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
     for key in ("gcnArchName", "clock_rate"):
         if hasattr(props, key):
             info[key] = getattr(props, key)
+    try:
+        import subprocess
+        r = subprocess.run(["hipcc", "--version"], capture_output=True, text=True, timeout=20)
+        info["hipcc"] = " ".join(r.stdout.split()[:6])
+    except Exception:
+        pass
     return info
+
+
+def sclk_mhz():
+    """The GPU's current shader clock in MHz (rocm-smi), or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                           timeout=20)
+    except Exception:
+        return None
+    for line in r.stdout.splitlines():
+        if "sclk" in line.lower():
+            m = re.search(r"(\d+)\s*Mhz", line, re.I)
+            if m:
+                return int(m.group(1))
+    return None
+
+
+def sclk_under_load(fn, torch, launches=1500):
+    """Shader clock sampled while `launches` queued steps keep the GPU busy (the
+    samples are taken after the queue is filled, before it drains)."""
+    for i in range(launches):
+        fn(i)
+    samples = [sclk_mhz() for _ in range(3)]
+    torch.cuda.synchronize()
+    samples = [x for x in samples if x is not None]
+    return samples or None
+
+
+def copy_bandwidth(torch, nbytes=COPY_BYTES, reps=20):
+    """Streaming rate of a plain device-to-device copy (read + write bytes per
+    second) over two buffer pairs, 2 GiB in all, so the last-level cache holds
+    neither: the practical HBM ceiling on this board."""
+    bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1.0)
+    for i in range(4):
+        bufs[2 * (i % 2) + 1].copy_(bufs[2 * (i % 2)])
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(reps):
+        bufs[2 * (i % 2) + 1].copy_(bufs[2 * (i % 2)])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return round(2.0 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
 def gemm_inputs(inputs, torch, M, N, K, nsets):
@@ -927,12 +1038,18 @@ def main():
         sg.gemm(A, B, C, alpha=1.0, beta=0.0)
 
     print("bench: timing fp16 8192^3 GEMM", file=sys.stderr, flush=True)
+    sclk_before = sclk_mhz()
     ms = time_steps(step, args.steps, args.warmup, torch)
+    sclk_after = sclk_mhz()
     cfg = sg.last_config()
     stats = step_stats(step, args.steps, torch)
+    sclk_load = sclk_under_load(step, torch)
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic()
+    step(0)                                  # set 0 holds the seeded problem of the oracle
+    torch.cuda.synchronize()
+    c_gpu = sets[0][2].view(torch.int16).cpu().numpy().view(np.uint16)
     del sets
     torch.cuda.empty_cache()
     out = {
@@ -950,6 +1067,10 @@ def main():
         "step_stats": stats,
         "env": env_info(torch),
     }
+    out["env"].update({"sclk_mhz_before": sclk_before, "sclk_mhz_after": sclk_after,
+                       "sclk_mhz_under_load": sclk_load})
+    print("bench: device copy bandwidth", file=sys.stderr, flush=True)
+    out["env"]["copy_gbs"] = copy_bandwidth(torch)
     if not args.quick:
         print("bench: bf16 8192^3 GEMM and the ragged bf16 GEMMs", file=sys.stderr, flush=True)
         out["gemm_bf16_8192"] = bench_gemm_bf16_8192(torch, sg, max(10, args.steps // 2),
@@ -965,18 +1086,42 @@ def main():
         sizes = [("bf16", m, 4864, 896) for m in (128, 512, 2048, 8192)] + \
                 [("e4m3", m, 11008, 4096) for m in (1, 16, 256, 4096)]
     sw = []
+    kept = {}
     for dt, m, n, k in sizes:
         print("bench: SwiGLU %s M=%d" % (dt, m), file=sys.stderr, flush=True)
         sw.append(bench_swiglu(torch, sg, inputs, dt, m, n, k, max(10, args.steps // 2),
-                               args.warmup))
+                               args.warmup, keep=kept if (dt, m) == ("bf16", 2048) else None))
         torch.cuda.empty_cache()
     out["swiglu_m2048"] = [s for s in sw if s["dtype"] == "bf16" and s["M"] == 2048][0]
     if len(sw) > 1:
         out["swiglu_all"] = sw
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(host, M, N, K, args.cpu_budget)
+        out["cpu_baseline"], ref_rows = cpu_baseline(host, M, N, K, args.cpu_budget)
+        out["numerics"] = oracle_checks(c_gpu, ref_rows, kept)
     print(json.dumps(out), flush=True)
+
+
+def oracle_checks(c_gpu, ref_rows, kept, swiglu_rows=256):
+    """The error report of the CPU-baseline leg: the headline GEMM's output on the rows
+    the oracle just computed, and the bf16 SwiGLU at M = 2048 (fused kernel and the
+    unfused two-GEMM path) on its first swiglu_rows rows against the fp64 oracle."""
+    import oracle
+    R = ref_rows.shape[0]
+    out = {"gemm_f16_8192": dict(error_report(f16_bits_to_f64(c_gpu[:R]), ref_rows, 1e-3, 1e-2),
+                                 rows="0..%d" % (R - 1))}
+    if kept:
+        pb = kept["problem"]
+        M, K = pb["A"].shape
+        N = pb["W1"].shape[1]
+        R2 = min(swiglu_rows, M)
+        Wf = oracle.interleave(pb["W1"], pb["W2"])
+        ref = oracle.swiglu(R2, N, K, pb["A"][:R2], Wf, "bf16")
+        out["swiglu_bf16_m2048"] = {
+            "rows": "0..%d" % (R2 - 1),
+            "fused": error_report(bf16_bits_to_f64(kept["fused"][:R2]), ref, 1e-2, 2e-2),
+            "unfused": error_report(bf16_bits_to_f64(kept["unfused"][:R2]), ref, 1e-2, 2e-2)}
+    return out
 
 
 if __name__ == "__main__":

@@ -1,6 +1,8 @@
 """Shared helpers for the GPU parity tests: device transfer of raw storage and the
 comparison rule |y - yhat| <= atol + rtol*|yhat| (the tolerance form of
 "为什么 GEMM 是 CUDA 的必修课", 精度不是数据类型名称这么简单)."""
+import json
+import os
 import re
 
 import numpy as np
@@ -41,11 +43,49 @@ def from_dev(t):
     return t.cpu().numpy()
 
 
-def assert_close(y, yhat, dtype, K, what=""):
-    """y: fp64 values decoded from the GPU output; yhat: fp64 oracle values."""
+def error_stats(y, yhat, dtype, K):
+    """Error of the GPU values y against the oracle's yhat, beside the pass/fail rule:
+    largest absolute and relative error, the largest error over max|yhat|, the share of
+    elements more than 1 % off (the mismatch measure of "Resumo Técnico: Sobreposição
+    de Ativação em Nível de Tile ...", Resultados), and the worst |y - yhat| as a
+    fraction of the tolerance atol + rtol*|yhat| (pass iff <= 1)."""
+    atol, rtol = TOL[dtype](K)
+    d = np.abs(y - yhat)
+    a = np.abs(yhat)
+    n = int(d.size)
+    if n == 0:
+        return dict(n=0)
+    nz = a > 0
+    rel = d[nz] / a[nz]
+    amax = float(a.max())
+    return dict(n=n, K=int(K), dtype=dtype,
+                max_abs=float(d.max()),
+                max_rel=float(rel.max()) if rel.size else 0.0,
+                max_abs_over_max_ref=float(d.max() / amax) if amax > 0 else 0.0,
+                share_rel_gt_1pct=float(np.count_nonzero(d > 0.01 * a)) / n,
+                worst_over_tol=float(np.max(d / (atol + rtol * a))))
+
+
+def record(what, stats):
+    """Append one comparison's statistics to the JSON-lines file named by
+    SG_NUMERICS_REPORT (no-op when unset)."""
+    path = os.environ.get("SG_NUMERICS_REPORT")
+    if not path:
+        return
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "a") as f:
+        f.write(json.dumps(dict(case=what, **stats)) + "\n")
+
+
+def assert_close(y, yhat, dtype, K, what="", report=False):
+    """y: fp64 values decoded from the GPU output; yhat: fp64 oracle values.  Every
+    element must satisfy |y - yhat| <= atol + rtol*|yhat|; with report=True the error
+    statistics of the comparison are also recorded."""
     atol, rtol = TOL[dtype](K)
     assert y.shape == yhat.shape
     assert np.all(np.isfinite(y)), "%s: non-finite output" % what
+    if report:
+        record(what, error_stats(y, yhat, dtype, K))
     excess = np.abs(y - yhat) - (atol + rtol * np.abs(yhat))
     if np.any(excess > 0):
         i = np.unravel_index(np.argmax(excess), excess.shape)
@@ -56,24 +96,6 @@ def assert_close(y, yhat, dtype, K, what=""):
 
 def bits_equal(a, b):
     return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
-
-
-def gemm_oracle_rows(rows, p, transA, transB, M, N, K, alpha, beta, dtype):
-    """Oracle for a subset of rows of C: returns fp64 [len(rows), N]."""
-    rows = np.asarray(rows)
-    A = oracle.decode(p["A"], dtype)
-    B = oracle.decode(p["B"], dtype).ravel()
-    C = oracle.decode(p["C"], out_dtype(dtype))
-    if transA in "Tt":     # A stored K x M: take columns
-        Asub = np.ascontiguousarray(A[:, rows])
-        lda = len(rows)
-    else:
-        Asub = np.ascontiguousarray(A[rows, :])
-        lda = p["lda"]
-    Csub = np.ascontiguousarray(C[rows, :]).ravel()
-    oracle.gemm_f64(transA, transB, len(rows), N, K, oracle.as_f32(alpha), Asub.ravel(), lda, B,
-                    p["ldb"], oracle.as_f32(beta), Csub, p["ldc"])
-    return Csub.reshape(len(rows), p["ldc"])[:, :N]
 
 
 def split_count(cfg: str) -> int:

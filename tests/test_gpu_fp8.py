@@ -49,29 +49,18 @@ def weights():
     return pb, oracle.interleave(pb["W1"], pb["W2"])
 
 
-@pytest.mark.parametrize("M", [1, 16])
-def test_swiglu_e4m3_skinny_full(M, weights):
+@pytest.mark.parametrize("M", [1, 16, 256, 4096])
+def test_swiglu_e4m3_full(M, weights):
+    """Every output of the e4m3 SwiGLU workload (K = 4096, N = 11008, per-tensor
+    scales) at each of its token counts, in the default launch configuration."""
     N, K = 11008, 4096
     wb, Wf = weights
     pb = inputs.swiglu_problem(5, M, N, K, "e4m3")
     assert pb["scale_w"] == wb["scale_w"]
     y, cfg = run_swiglu8(pb, Wf, M, N, K)
     ref = oracle.swiglu(M, N, K, pb["A"], Wf, "e4m3", pb["scale_a"], pb["scale_w"])
-    assert_close(oracle.decode(y, "bf16"), ref, "e4m3", K, "swiglu e4m3 M=%d %s" % (M, cfg))
-
-
-@pytest.mark.parametrize("M", [256, 4096])
-def test_swiglu_e4m3_sampled_rows(M, weights):
-    N, K = 11008, 4096
-    _, Wf = weights
-    pb = inputs.swiglu_problem(5, M, N, K, "e4m3")
-    y, cfg = run_swiglu8(pb, Wf, M, N, K)
-    got = oracle.decode(y, "bf16")
-    assert np.all(np.isfinite(got))
-    gen = np.random.default_rng(M)
-    rows = sorted(set([0, 1, 31, 32, 127, 128, M // 2, M - 1] + list(gen.integers(0, M, size=8))))
-    ref = oracle.swiglu(len(rows), N, K, pb["A"][rows, :], Wf, "e4m3", pb["scale_a"], pb["scale_w"])
-    assert_close(got[rows, :], ref, "e4m3", K, "swiglu e4m3 M=%d %s" % (M, cfg))
+    assert_close(oracle.decode(y, "bf16"), ref, "e4m3", K, "swiglu e4m3 M=%d %s" % (M, cfg),
+                 report=True)
 
 
 @pytest.mark.parametrize("splits", [1, 2])

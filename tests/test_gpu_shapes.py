@@ -2,7 +2,7 @@
 the C ABI: multi-round grids with ragged edges (row-staged stores on full tiles,
 register stores on edge tiles), beta != 0, every transpose pair, the 16-bit cost model
 (64-row tiles, split-K) and the e4m3 rules (32-row, 8-wave 128 x 256 and 256 x 256
-tiles, the column split).  Large outputs are checked on sampled rows, every column."""
+tiles, the column split).  Every output is compared."""
 import os
 
 import numpy as np
@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from swiglu_gemm_amd import inputs
-from helpers import assert_close, from_dev, gemm_oracle_rows, to_dev
+from helpers import assert_close, from_dev, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -61,14 +61,6 @@ def test_default_path_shape(case):
     torch.cuda.synchronize()
     desc = sg.last_config()
     got = oracle.decode(from_dev(C), od)
-    if M * N <= 4 * 1024 * 1024:
-        ref = oracle.gemm(ta, tb, M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], beta,
-                          p["C"], p["ldc"], dtype, c_dtype=od)
-        assert_close(got, ref, dtype, K, desc)
-    else:
-        gen = np.random.default_rng(seed)
-        rows = sorted(set(r for r in [0, 1, 31, 32, 255, 256, M // 2, M - 2, M - 1] +
-                          list(gen.integers(0, M, size=12)) if r < M))
-        ref = gemm_oracle_rows(rows, p, ta, tb, M, N, K, alpha, beta, dtype)
-        assert_close(got[rows, :], ref, dtype, K, desc)
-        assert np.all(np.isfinite(got)), desc
+    ref = oracle.gemm(ta, tb, M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], beta,
+                      p["C"], p["ldc"], dtype, c_dtype=od)
+    assert_close(got, ref, dtype, K, desc)

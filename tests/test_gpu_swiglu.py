@@ -60,28 +60,17 @@ def test_interleave_bit_exact(dtype, K, N):
     assert bits_equal(a, W1) and bits_equal(b, W2)
 
 
-@pytest.mark.parametrize("M", [128, 512])
+@pytest.mark.parametrize("M", [128, 512, 2048, 8192])
 def test_swiglu_bf16_full(M):
+    """Every output of the bf16 SwiGLU workload (K = 896, N = 4864) at each of its
+    token counts, in the default launch configuration."""
     N, K = 4864, 896
     pb = inputs.swiglu_problem(4, M, N, K, "bf16")
     Wf = interleave_on_gpu(pb["W1"], pb["W2"], "bf16")
     y, cfg = run_swiglu(pb["A"], Wf, M, N, K, "bf16")
     ref = oracle.swiglu(M, N, K, pb["A"], Wf, "bf16")
-    assert_close(oracle.decode(y, "bf16"), ref, "bf16", K, "swiglu M=%d %s" % (M, cfg))
-
-
-@pytest.mark.parametrize("M", [2048, 8192])
-def test_swiglu_bf16_sampled_rows(M):
-    N, K = 4864, 896
-    pb = inputs.swiglu_problem(4, M, N, K, "bf16")
-    Wf = interleave_on_gpu(pb["W1"], pb["W2"], "bf16")
-    y, cfg = run_swiglu(pb["A"], Wf, M, N, K, "bf16")
-    got = oracle.decode(y, "bf16")
-    assert np.all(np.isfinite(got))
-    gen = np.random.default_rng(M)
-    rows = sorted(set([0, 1, 255, 256, M // 2, M - 2, M - 1] + list(gen.integers(0, M, size=25))))
-    ref = oracle.swiglu(len(rows), N, K, pb["A"][rows, :], Wf, "bf16")
-    assert_close(got[rows, :], ref, "bf16", K, "swiglu M=%d %s" % (M, cfg))
+    assert_close(oracle.decode(y, "bf16"), ref, "bf16", K, "swiglu bf16 M=%d %s" % (M, cfg),
+                 report=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
