@@ -229,6 +229,16 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True, k
     t_hot = time_steps(fused_over(base), steps, warmup, torch)
     t_w12 = time_steps(w12, steps, warmup, torch)
     cfg_w12 = sg.last_config()
+    # Gate then Up (Kernel-1 of the SwiGLU page) on the same split weights, its tile
+    # chosen as the library does (256-row tiles once they fill the CUs)
+    big = -(-M // 256) * -(-2 * N // 256) >= 256
+    seq_cfg = (51 if big else 52) if dtype == "e4m3" else (49 if big else 50)
+    os.environ["SG_FORCE_CONFIG"] = "%d,1" % seq_cfg
+    try:
+        t_seq = time_steps(w12, steps, warmup, torch)
+        cfg_seq = sg.last_config()
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
     t_unfused = time_steps(unfused, steps, warmup, torch)
     if keep is not None:
         A, W1, W2, Wf, sa, sw = base[0]
@@ -248,7 +258,8 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True, k
            "ms_hot": round(t_hot, 5),
            "unfused_ms": round(t_unfused, 5), "speedup_vs_unfused": round(t_unfused / t_fused, 3),
            "kernel_config": cfg,
-           "w12_ms": round(t_w12, 5), "w12_kernel_config": cfg_w12}
+           "w12_ms": round(t_w12, 5), "w12_kernel_config": cfg_w12,
+           "seq_ms": round(t_seq, 5), "seq_kernel_config": cfg_seq}
     if eager and dtype == "bf16":
         def eager_fn(i):
             A, W1, W2, _, _, _ = sets[i % ncold]

@@ -140,7 +140,7 @@ struct Batch {
 // may end inside a chunk.  A K tail (K not a multiple of BK) is loaded through
 // registers by the one-stream kernel; the ping-pong kernel needs whole K tiles.
 bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
-    if (!c.dma || c.e4m3 != (q.esz == 1)) return false;
+    if (!c.dma || c.dma == 3 || c.e4m3 != (q.esz == 1)) return false;
     if (!q.vec_a || !q.vec_b || kps % c.BK != 0) return false;
     if (c.dma == 2 && q.K % c.BK != 0) return false;
     const int nw = c.dma == 2 ? 4 : c.WM * c.WN;     // ping-pong: group 0 issues the DMA
@@ -656,6 +656,8 @@ hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alp
 // Configurations that can run it (see w12_ok in launch16.hpp): 16-bit candidates
 // weighed with the same cost model as the interleaved kernel; e4m3 by rows.
 constexpr Cand16 kCandW12[] = {{10, 4.7}, {8, 4.7}, {32, 3.6}, {6, 3.4}};
+// rows from which the split-weight SwiGLU runs Gate then Up (Kernel-1)
+constexpr int64_t kSeqMinRows = (int64_t)1 << 40;
 
 bool w12_cfg_ok(const Cfg16& c, const Problem16& q_out) {
     // c runs on [M, 2N, K]; each weight is a K x N row-contiguous operand of BN/2 columns
@@ -716,6 +718,44 @@ ColSplit plan_w12_split(const Problem16& q_out, int cfg) {
     s.n1 = (tn - strip) * c.BN;
     s.cfg_tail = tail;
     return s;
+}
+
+// ------------------------------------- split-weight SwiGLU, Gate then Up (Kernel-1)
+// Whether configuration c (dma kind 3) can run the Gate-then-Up kernel on q_out
+// (M rows, N outputs, K): whole K tiles, 16-byte aligned rows, DMA-compatible A
+// and half tiles, and gate / up fragments in pairs.
+bool seq_cfg_ok(const Cfg16& c, const Problem16& q_out) {
+    if (c.dma != 3 || (c.e4m3 != 0) != (q_out.esz == 1)) return false;
+    if (!q_out.vec_a || !q_out.vec_b || q_out.K % c.BK != 0) return false;
+    if ((c.BN / c.WN / 32) % 2 != 0 || c.BN % 64 != 0) return false;
+    const int nw = c.WM * c.WN;
+    return dma_tile_ok(true, c.BM, c.BK, q_out.esz, nw) &&
+           dma_tile_ok(false, c.BN / 2, c.BK, q_out.esz, nw);
+}
+
+// The Gate-then-Up configuration for q_out, or -1: 256-row tiles once they fill the
+// CUs, else 128-row tiles (twice the work-groups).
+int choose_seq(const Problem16& q_out) {
+    const bool e4m3 = q_out.esz == 1;
+    int cfg = -1, splits = 0;
+    if (forced_config(&cfg, &splits) && cfg >= 0 && cfg < kNumCfg16)
+        return seq_cfg_ok(kCfg16[cfg], q_out) ? cfg : -1;
+    const int big = e4m3 ? 51 : 49, small = e4m3 ? 52 : 50;
+    const int64_t tiles = cdiv(q_out.M, 256) * cdiv(2 * q_out.N, 256);
+    const int c = tiles >= kNumCU ? big : small;
+    return seq_cfg_ok(kCfg16[c], q_out) ? c : -1;
+}
+
+template <int DT>
+hipError_t run_seq(int cfg, Gemm16Params p, hipStream_t st) {
+    if (!p.A || !p.B || !p.B2 || !p.C) return hipErrorInvalidValue;   // never launch on NULL
+    const Cfg16& c = kCfg16[cfg];
+    p.tiles_m = (int)cdiv(p.M, c.BM);
+    p.tiles_n = (int)cdiv(p.N, c.BN);
+    p.group_m = group_m();
+    p.k_per_split = p.K;
+    std::snprintf(g_last_cfg, sizeof(g_last_cfg), "swiglu_seq cfg=%d %s splits=1", cfg, c.name);
+    return launch16_dt<DT>(false, false, EPI_SWIGLU_SEQ, cfg, p, 1, st);
 }
 
 template <int DT>
@@ -1059,7 +1099,13 @@ int sg_swiglu_gemm_w12(const void* A, const void* W1, const void* W2, void* Y, i
     if (K > 0) {
         Problem16 q{M, N, K, aligned(A, 16) && (K * esz) % 16 == 0,
                     aligned(W1, 16) && aligned(W2, 16) && (N * esz) % 16 == 0, false, false, esz};
-        const int cfg = choose_w12(q);
+        // the pages' dual-kernel choice: Gate then Up (Kernel-1) from kSeqMinRows rows,
+        // Gate and Up side by side in one K loop below that (a forced configuration
+        // of either kind selects its kernel)
+        int fc = -1, fs = 0;
+        const bool forced = forced_config(&fc, &fs) && fc >= 0 && fc < kNumCfg16;
+        const int seq = (forced ? kCfg16[fc].dma == 3 : M >= kSeqMinRows) ? choose_seq(q) : -1;
+        const int cfg = seq >= 0 ? seq : choose_w12(q);
         if (cfg >= 0) {
             Gemm16Params p{};
             p.A = reinterpret_cast<const uint16_t*>(A);
@@ -1078,9 +1124,17 @@ int sg_swiglu_gemm_w12(const void* A, const void* W1, const void* W2, void* Y, i
             p.vec_c = aligned(Y, 8) && (N % 4 == 0);
             p.epi_flags = aligned(Y, 16) && N % 8 == 0 ? EPI_Y16 : 0;
             hipError_t e;
-            if (dtype == SG_F8E4M3) e = run_w12<DT_E4M3>(cfg, q, p, st);
-            else if (dtype == SG_F16) e = run_w12<DT_F16>(cfg, q, p, st);
-            else e = run_w12<DT_BF16>(cfg, q, p, st);
+            if (seq >= 0) {
+                if (dtype == SG_F8E4M3) e = run_seq<DT_E4M3>(cfg, p, st);
+                else if (dtype == SG_F16) e = run_seq<DT_F16>(cfg, p, st);
+                else e = run_seq<DT_BF16>(cfg, p, st);
+            } else if (dtype == SG_F8E4M3) {
+                e = run_w12<DT_E4M3>(cfg, q, p, st);
+            } else if (dtype == SG_F16) {
+                e = run_w12<DT_F16>(cfg, q, p, st);
+            } else {
+                e = run_w12<DT_BF16>(cfg, q, p, st);
+            }
             return status_of(e);
         }
     }

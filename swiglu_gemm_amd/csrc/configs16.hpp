@@ -7,7 +7,8 @@ struct Cfg16 {
     int e4m3;           // 1: e4m3 operands (BK in bytes), 0: fp16 / bf16 operands
     int dma;            // 0: register-staged (gemm16.hpp), 1: direct global->LDS ring
                         // (gemm16_dma.hpp), 2: the same ring with the 8-wave ping-pong
-                        // schedule (gemm_pingpong.hpp)
+                        // schedule (gemm_pingpong.hpp), 3: the direct ring for the
+                        // split-weight SwiGLU with Gate then Up (EPI_SWIGLU_SEQ only)
     int BM, BN, BK, S;  // tile and LDS stages
     int WM, WN;         // waves along M and N
     const char* name;
@@ -68,6 +69,11 @@ constexpr Cfg16 kCfg16[] = {
     {0, 1, 256, 192, 64, 2, 4, 2, "dma 256x192x64 s2 4x2w"},
     {1, 1, 128, 192, 128, 3, 4, 2, "e4m3 dma 128x192x128 s3 4x2w"},
     {0, 1, 128, 192, 64, 3, 4, 2, "dma 128x192x64 s3 4x2w"},
+    // split-weight SwiGLU, Gate then Up (BN: the fused width, BN/2 outputs)
+    {0, 3, 256, 256, 64, 3, 4, 2, "seq 256x256x64 s3 4x2w"},
+    {0, 3, 128, 256, 64, 4, 2, 2, "seq 128x256x64 s4 2x2w"},
+    {1, 3, 256, 256, 128, 3, 4, 2, "e4m3 seq 256x256x128 s3 4x2w"},
+    {1, 3, 128, 256, 128, 4, 2, 2, "e4m3 seq 128x256x128 s4 2x2w"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
@@ -150,6 +156,15 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(16, 1, 32, 256, 128, 4, 1, 4)    \
     X(17, 1, 32, 128, 128, 4, 1, 4)    \
     X(33, 1, 128, 256, 128, 3, 2, 2)
+
+// the split-weight SwiGLU with Gate then Up (EPI_SWIGLU_SEQ, NN only)
+#define SG_CONFIGS_SEQ(X)              \
+    X(49, 1, 256, 256, 64, 3, 4, 2)    \
+    X(50, 1, 128, 256, 64, 4, 2, 2)
+
+#define SG_CONFIGS_E4M3_SEQ(X)         \
+    X(51, 1, 256, 256, 128, 3, 4, 2)   \
+    X(52, 1, 128, 256, 128, 4, 2, 2)
 
 // the same for every e4m3 row (all direct-to-LDS)
 #define SG_CONFIGS_E4M3(X)             \

@@ -573,12 +573,14 @@ __device__ __forceinline__ void epilogue_gemm_ex_rows_lds(const Gemm16Params& p,
 // otherwise cb is its first fused column (outputs at half of it).  SCALED: the
 // inputs were e4m3 and gate and up are multiplied by s = sA*sW first; 16-bit
 // inputs always have s = 1 (the C ABI rejects other scales for them).
-template <bool SCALED>
+// PRE: the gate accumulator already holds SiLU(s*g) (applied during the main loop).
+template <bool SCALED, bool PRE = false>
 __device__ __forceinline__ float swiglu_pair(float g, float u, float s) {
+    if constexpr (PRE) return SCALED ? g * (s * u) : g * u;
     return SCALED ? silu(s * g) * (s * u) : silu(g) * u;
 }
 
-template <int DT, int FM, int FN, int BM, int BN, int NT, bool W12, bool SCALED>
+template <int DT, int FM, int FN, int BM, int BN, int NT, bool W12, bool SCALED, bool PRE = false>
 __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
                                                     f32x16 (&acc)[FN][FM], char* smem, int m0,
                                                     int n0, int rb, int cb, int lane) {
@@ -606,8 +608,8 @@ __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
                     float y[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        y[e] = swiglu_pair<SCALED>(acc[tn][tm][4 * g + e],
-                                                   acc[tn + FN / 2][tm][4 * g + e], s);
+                        y[e] = swiglu_pair<SCALED, PRE>(acc[tn][tm][4 * g + e],
+                                                        acc[tn + FN / 2][tm][4 * g + e], s);
                     *reinterpret_cast<u32x2*>(row + 2 * c) =
                         u32x2{pack2<DT>(y[0], y[1]), pack2<DT>(y[2], y[3])};
                 }

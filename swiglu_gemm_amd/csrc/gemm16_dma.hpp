@@ -34,6 +34,8 @@
 // generic e4m3 kernel.
 #pragma once
 
+#include <type_traits>
+
 #include "epilogue16.hpp"
 #include "sg_device.hpp"
 
@@ -252,11 +254,15 @@ struct DmaShape {
     static_assert(BK % KSTEP == 0 && KS % 2 == 0, "k-steps per tile must be even");
     static constexpr bool KCA = !TA, KCB = TB;          // k-contiguous operands
     // EPI_SWIGLU_W12: the B tile is BN/2 columns of W1 followed by the same BN/2
-    // columns of W2; a wave's fragments tn < FN/2 are gate, tn + FN/2 the matching up
+    // columns of W2; a wave's fragments tn < FN/2 are gate, tn + FN/2 the matching up.
+    // EPI_SWIGLU_SEQ: the same output columns and fragment roles, but each stage holds
+    // one B tile of BN/2 columns: W1's for the first K/BK tiles, then W2's.
     static constexpr bool W12 = EPI == EPI_SWIGLU_W12;
-    static_assert(!W12 || (!TA && !TB && FN % 2 == 0 && BN % 64 == 0), "split-weight SwiGLU tile");
-    static constexpr int BNS = W12 ? BN / 2 : BN;       // columns per B source
-    static constexpr int NBS = W12 ? 2 : 1;             // B sources
+    static constexpr bool SEQ = EPI == EPI_SWIGLU_SEQ;
+    static_assert(!(W12 || SEQ) || (!TA && !TB && FN % 2 == 0 && BN % 64 == 0),
+                  "split-weight SwiGLU tile");
+    static constexpr int BNS = (W12 || SEQ) ? BN / 2 : BN;   // columns per B source
+    static constexpr int NBS = W12 ? 2 : 1;                   // B tiles per stage
     using TA_ = DmaTile<KCA, BM, BK, ESZ>;
     using TB_ = DmaTile<KCB, BNS, BK, ESZ>;
     static constexpr int STAGE = TA_::BYTES + NBS * TB_::BYTES;
@@ -395,6 +401,111 @@ __device__ __forceinline__ void dma_mainloop(
     }
 }
 
+// Split-weight SwiGLU with Gate and Up one after the other ("Resumo Técnico:
+// Sobreposição de Ativação em Nível de Tile ...", Metodologia / Kernel-1): the
+// work-group's output tile is BM rows x BN/2 columns of Y.  One S-stage ring runs
+// over 2*nkt K tiles -- (A, W1) for tiles 0..nkt-1 into the gate accumulators
+// (fragments tn < FN/2), then (A, W2) into the up accumulators (tn + FN/2).  The
+// ring issues S-1 tiles ahead, so when the last Gate tile is consumed the first Up
+// tiles are already in flight: SiLU(s * gate) is evaluated in registers while they
+// land (the page's overlap of the Swish with the Up-tile loads), and the epilogue
+// multiplies by s * up and stores.  K must be a multiple of BK (the chooser checks).
+template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
+__device__ __forceinline__ void dma_mainloop_seq(
+    const Gemm16Params& p, char* smem, int m0, int n0, int nkt,
+    typename DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>::Acc& acc, int wave, int lane) {
+    using D = DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>;
+    static_assert(D::SEQ, "sequential SwiGLU only");
+    constexpr int ESZ = D::ESZ, FM = D::FM, FN = D::FN, KS = D::KS, TM = D::TM, TN = D::TN;
+    constexpr int BNS = D::BNS, NW = D::NW, STAGE = D::STAGE, NL = D::NL, FH = FN / 2;
+    using TA_ = typename D::TA_;
+    using Frag = typename D::Frag;
+    const int wm = wave % WM, wn = wave / WM;
+
+    DmaStream<true, BM, BK, ESZ, NW> da;
+    DmaStream<false, BNS, BK, ESZ, NW> d1, d2;
+    da.init(p.A, p.lda, m0, p.M, 0, wave, lane);
+    d1.init(p.B, p.ldb, n0 / 2, p.N / 2, 0, wave, lane);
+    d2.init(p.B2, p.ldb, n0 / 2, p.N / 2, 0, wave, lane);
+    const int T = 2 * nkt;
+
+    Frag fa[2][FM], fb[2][FH];
+    auto read_all = [&](const char* st, int s, Frag (&af)[FM], Frag (&bf)[FH]) {
+#pragma unroll
+        for (int tm = 0; tm < FM; ++tm)
+            af[tm] = read_frag<true, BM, BK, ESZ>(st, wm * TM + tm * 32, s, lane);
+#pragma unroll
+        for (int tn = 0; tn < FH; ++tn)
+            bf[tn] = read_frag<false, BNS, BK, ESZ>(st + TA_::BYTES, wn * (TN / 2) + tn * 32, s,
+                                                   lane);
+    };
+    auto issue = [&](int t) {
+        char* st = smem + (t % S) * STAGE;
+        if (t < nkt) {
+            da.issue(st, t, wave);
+            d1.issue(st + TA_::BYTES, t, wave);
+        } else {
+            da.issue(st, t - nkt, wave);
+            d2.issue(st + TA_::BYTES, t - nkt, wave);
+        }
+    };
+    constexpr int NMF = FM * FH;
+    constexpr int RD_RC = ESZ == 2 ? 2 : 4, RD_KC = ESZ == 2 ? 1 : 2;
+    constexpr int NRD = RD_KC * FM + RD_RC * FH;
+    // tiles [t0, t1) into the accumulator fragments OFF .. OFF + FH - 1
+    auto phase = [&](auto off, int t0, int t1) __attribute__((always_inline)) {
+        constexpr int OFF = decltype(off)::value;
+        auto mfma_all = [&](const Frag (&af)[FM], const Frag (&bf)[FH]) {
+#pragma unroll
+            for (int tn = 0; tn < FH; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < FM; ++tm)
+                    acc[OFF + tn][tm] = mfma_op<DT>(bf[tn], af[tm], acc[OFF + tn][tm]);
+        };
+        for (int t = t0; t < t1; ++t) {
+            const char* cur = smem + (t % S) * STAGE;
+            const bool ahead = t + S - 1 < T;
+            if (ahead) issue(t + S - 1);
+#pragma unroll
+            for (int s = 0; s + 1 < KS; ++s) {
+                read_all(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+                mfma_all(fa[s & 1], fb[s & 1]);
+                sched_interleave<NMF, NRD, 0, 0>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (ahead) wait_vmcnt<(S - 2) * NL>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // the next tile's first fragments (on the last tile: a stale stage, unused)
+            read_all(smem + ((t + 1) % S) * STAGE, 0, fa[0], fb[0]);
+            mfma_all(fa[1], fb[1]);
+            sched_interleave<NMF, NRD, 0, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (nkt <= 0) return;
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+        if (i < T) issue(i);
+    if (T >= S - 1) wait_vmcnt<(S - 2) * NL>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_all(smem, 0, fa[0], fb[0]);
+    phase(std::integral_constant<int, 0>{}, 0, nkt);
+    // SiLU(s * gate) while the first Up tiles land
+    const float sc = DT == DT_E4M3 ? p.alpha : 1.0f;
+#pragma unroll
+    for (int tn = 0; tn < FH; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < FM; ++tm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[tn][tm][e] = silu(sc * acc[tn][tm][e]);
+    __builtin_amdgcn_sched_barrier(0);
+    phase(std::integral_constant<int, FH>{}, nkt, T);
+}
+
 // The epilogue of one finished output tile (every thread of the work-group).
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
 __device__ __forceinline__ void dma_epilogue(
@@ -402,11 +513,11 @@ __device__ __forceinline__ void dma_epilogue(
     char* smem, int m0, int n0, int wave, int lane) {
     using D = DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>;
     constexpr int DT_OUT = D::DT_OUT, FM = D::FM, FN = D::FN, TM = D::TM, TN = D::TN;
-    constexpr bool W12 = D::W12;
+    constexpr bool W12 = D::W12 || D::SEQ;
     const int wm = wave % WM, wn = wave / WM;
     if constexpr (EPI == EPI_SWIGLU || W12) {
         static_assert(BM * (BN + 8) <= D::LDS, "staged SwiGLU tile fits the LDS ring");
-        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN, W12, DT == DT_E4M3>(
+        epilogue_swiglu_lds<DT_OUT, FM, FN, BM, BN, 64 * WM * WN, W12, DT == DT_E4M3, D::SEQ>(
             p, acc, smem, m0, n0, wm * TM, W12 ? wn * (TN / 2) : wn * TN, lane);
     } else if constexpr (EPI == EPI_GEMM_EX) {
         static_assert(D::LDS >= D::NW * 32 * 36 * 4, "EX staging fits the LDS ring");
@@ -488,8 +599,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
         for (int j = 0; j < D::FM; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    dma_mainloop<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, smem, m0, n0, kbeg, nkt, ktail, acc,
-                                                         wave, lane);
+    if constexpr (D::SEQ)
+        dma_mainloop_seq<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, smem, m0, n0, nkt, acc, wave,
+                                                                 lane);
+    else
+        dma_mainloop<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, smem, m0, n0, kbeg, nkt, ktail,
+                                                             acc, wave, lane);
     dma_epilogue<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, acc, smem, m0, n0, wave, lane);
 }
 

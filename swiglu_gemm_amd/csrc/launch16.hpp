@@ -35,7 +35,7 @@ constexpr bool w12_ok() {
 template <int DT, bool TA, bool TB, int EPI, int DMA, int BM, int BN, int BK, int S, int WM, int WN>
 inline hipError_t launch_one(const Gemm16Params& p, int splits, hipStream_t st) {
     constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
-    if constexpr (EPI == EPI_SWIGLU_W12) {
+    if constexpr (EPI == EPI_SWIGLU_W12 || EPI == EPI_SWIGLU_SEQ) {
         if constexpr (w12_ok<DT, TA, TB, DMA, BM, BN, BK, WM, WN>())
             return launch_grid(gemm_dma_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
                                64 * WM * WN, st);
@@ -62,7 +62,19 @@ template <int DT, bool TA, bool TB, int EPI>
 hipError_t launch16_cfg(int cfg, const Gemm16Params& p, int splits, hipStream_t st) {
 #define SG_CASE(ID, DMA, BM, BN, BK, S, WM, WN) \
     case ID: return launch_one<DT, TA, TB, EPI, DMA, BM, BN, BK, S, WM, WN>(p, splits, st);
-    if constexpr (EPI == EPI_GEMM_EX) {
+    if constexpr (EPI == EPI_SWIGLU_SEQ) {
+        if constexpr (DT == DT_E4M3) {
+            switch (cfg) {
+                SG_CONFIGS_E4M3_SEQ(SG_CASE)
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (cfg) {
+                SG_CONFIGS_SEQ(SG_CASE)
+                default: return hipErrorInvalidValue;
+            }
+        }
+    } else if constexpr (EPI == EPI_GEMM_EX) {
         if constexpr (DT == DT_E4M3) {
             switch (cfg) {
                 SG_CONFIGS_E4M3_EX(SG_CASE)
@@ -95,14 +107,16 @@ hipError_t launch16_cfg(int cfg, const Gemm16Params& p, int splits, hipStream_t 
 #undef SG_CASE
 }
 
-// epi: EPI_GEMM / EPI_GEMM_EX / EPI_PARTIAL for any transpose pair; EPI_SWIGLU(_W12)
-// for NN only.
+// epi: EPI_GEMM / EPI_GEMM_EX / EPI_PARTIAL for any transpose pair; EPI_SWIGLU,
+// EPI_SWIGLU_W12 and EPI_SWIGLU_SEQ for NN only.
 template <int DT, bool TA, bool TB>
 hipError_t launch16_tr(int epi, int cfg, const Gemm16Params& p, int splits, hipStream_t st) {
     if constexpr (!TA && !TB) {
         if (epi == EPI_SWIGLU) return launch16_cfg<DT, TA, TB, EPI_SWIGLU>(cfg, p, splits, st);
         if (epi == EPI_SWIGLU_W12)
             return launch16_cfg<DT, TA, TB, EPI_SWIGLU_W12>(cfg, p, splits, st);
+        if (epi == EPI_SWIGLU_SEQ)
+            return launch16_cfg<DT, TA, TB, EPI_SWIGLU_SEQ>(cfg, p, splits, st);
     }
     if (epi == EPI_GEMM) return launch16_cfg<DT, TA, TB, EPI_GEMM>(cfg, p, splits, st);
     if (epi == EPI_GEMM_EX) return launch16_cfg<DT, TA, TB, EPI_GEMM_EX>(cfg, p, splits, st);

@@ -16,8 +16,16 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3 };
 // EPI_GEMM_EX: EPI_GEMM plus the EpiEx steps (compiled for the configurations the
-// library chooses, see SG_CONFIGS_EX / SG_CONFIGS_E4M3_EX)
-enum : int { EPI_GEMM = 0, EPI_SWIGLU = 1, EPI_PARTIAL = 2, EPI_SWIGLU_W12 = 3, EPI_GEMM_EX = 4 };
+// library chooses, see SG_CONFIGS_EX / SG_CONFIGS_E4M3_EX).  EPI_SWIGLU_SEQ: the
+// split-weight SwiGLU with Gate and Up computed one after the other (SG_CONFIGS_SEQ).
+enum : int {
+    EPI_GEMM = 0,
+    EPI_SWIGLU = 1,
+    EPI_PARTIAL = 2,
+    EPI_SWIGLU_W12 = 3,
+    EPI_GEMM_EX = 4,
+    EPI_SWIGLU_SEQ = 5
+};
 
 // ---------------------------------------------------------------------------
 // 16-bit storage <-> fp32

@@ -127,3 +127,93 @@ def test_w12_one_hot_bit_exact(dtype):
               W2=inputs.to_storage(W2, dtype), scale_a=1.0, scale_w=1.0)
     y, cfg = run_w12(pb, M, N, K, dtype)
     assert np.array_equal(oracle.decode(y, "bf16"), A[:, pi1] * A[:, pi2]), cfg
+
+
+# --------------------------------------------------------------------------
+# Gate then Up (Kernel-1 of the SwiGLU page): SiLU(Gate) computed between the two
+# K loops while the first Up tiles load
+# --------------------------------------------------------------------------
+SEQ_CFGS16 = [49, 50]
+SEQ_CFGS8 = [51, 52]
+
+
+def run_forced(pb, M, N, K, dtype, cfg):
+    os.environ["SG_FORCE_CONFIG"] = "%d,1" % cfg
+    try:
+        return run_w12(pb, M, N, K, dtype)
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+
+
+@pytest.mark.parametrize("cfg", SEQ_CFGS16)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_seq_16bit_bit_equal_to_side_by_side(cfg, dtype):
+    """Gate and Up accumulate the same products in the same K order as the kernel
+    that computes them side by side, and SiLU(s*g)*(s*u) is evaluated with the same
+    operations: identical bits.  Ragged M and N, several work-group rows."""
+    M, N, K = 300, 1000, 640
+    pb = inputs.swiglu_problem(170 + cfg, M, N, K, dtype)
+    y, desc = run_forced(pb, M, N, K, dtype, cfg)
+    assert "swiglu_seq cfg=%d " % cfg in desc, desc
+    y2, desc2 = run_forced(pb, M, N, K, dtype, 10)
+    assert "swiglu_w12 cfg=10 " in desc2, desc2
+    assert bits_equal(y, y2), (desc, desc2)
+    out = "f16" if dtype == "f16" else "bf16"
+    assert_close(oracle.decode(y, out), reference(pb, M, N, K, dtype), dtype, K, desc)
+
+
+@pytest.mark.parametrize("cfg", SEQ_CFGS8)
+@pytest.mark.parametrize("M", [16, 300])
+def test_seq_e4m3(cfg, M):
+    N, K = 1536, 1024
+    pb = inputs.swiglu_problem(180 + cfg, M, N, K, "e4m3")
+    y, desc = run_forced(pb, M, N, K, "e4m3", cfg)
+    assert "swiglu_seq cfg=%d " % cfg in desc, desc
+    y2, desc2 = run_forced(pb, M, N, K, "e4m3", 14)
+    assert bits_equal(y, y2), (desc, desc2)
+    assert_close(oracle.decode(y, "bf16"), reference(pb, M, N, K, "e4m3"), "e4m3", K, desc)
+
+
+@pytest.mark.parametrize("dtype,cfg", [("bf16", 49), ("e4m3", 51)])
+def test_seq_one_hot_bit_exact(dtype, cfg):
+    M, N, K = 256, 512, 1024
+    gen = np.random.default_rng(8)
+    half = K // 2
+    A = np.zeros((M, K))
+    A[:, :half] = 2.0 ** gen.integers(5, 9, size=(M, half))
+    A[:, half:] = gen.integers(-3, 4, size=(M, K - half))
+    pi1 = gen.integers(0, half, size=N)
+    pi2 = half + gen.integers(0, K - half, size=N)
+    W1 = np.zeros((K, N))
+    W2 = np.zeros((K, N))
+    W1[pi1, np.arange(N)] = 1.0
+    W2[pi2, np.arange(N)] = 1.0
+    pb = dict(A=inputs.to_storage(A, dtype), W1=inputs.to_storage(W1, dtype),
+              W2=inputs.to_storage(W2, dtype), scale_a=1.0, scale_w=1.0)
+    y, desc = run_forced(pb, M, N, K, dtype, cfg)
+    assert "swiglu_seq cfg=%d " % cfg in desc, desc
+    assert np.array_equal(oracle.decode(y, "bf16"), A[:, pi1] * A[:, pi2]), desc
+
+
+@pytest.mark.parametrize("dtype,M", [("bf16", 128), ("bf16", 512), ("bf16", 2048), ("bf16", 8192),
+                                     ("e4m3", 1), ("e4m3", 16), ("e4m3", 256), ("e4m3", 4096)])
+def test_split_weight_default_path_full(dtype, M):
+    """The split-weight entry point at the SwiGLU workloads' full sizes, in its
+    default choice between the two schedules: every output against the oracle."""
+    N, K = (4864, 896) if dtype == "bf16" else (11008, 4096)
+    pb = inputs.swiglu_problem(4 if dtype == "bf16" else 5, M, N, K, dtype)
+    y, desc = run_w12(pb, M, N, K, dtype)
+    assert_close(oracle.decode(y, "bf16"), reference(pb, M, N, K, dtype), dtype, K,
+                 "split-weight %s M=%d %s" % (dtype, M, desc), report=True)
+
+
+@pytest.mark.parametrize("dtype,M,cfg", [("bf16", 2048, 49), ("bf16", 8192, 49),
+                                         ("e4m3", 4096, 51), ("e4m3", 256, 52)])
+def test_seq_workload_sizes_full(dtype, M, cfg):
+    """Gate then Up forced at the SwiGLU workloads' full sizes: every output."""
+    N, K = (4864, 896) if dtype == "bf16" else (11008, 4096)
+    pb = inputs.swiglu_problem(4 if dtype == "bf16" else 5, M, N, K, dtype)
+    y, desc = run_forced(pb, M, N, K, dtype, cfg)
+    assert "swiglu_seq cfg=%d " % cfg in desc, desc
+    assert_close(oracle.decode(y, "bf16"), reference(pb, M, N, K, dtype), dtype, K,
+                 "seq %s M=%d %s" % (dtype, M, desc), report=True)
