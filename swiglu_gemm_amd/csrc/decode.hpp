@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(const DecodeParams p) {
             const uint32_t lds = (uint32_t)(uintptr_t)(
                 (__attribute__((address_space(3))) char*)(st + (wave + j * NW) * 1024));
             const char* g = ga[j] + kb * (BK * ESZ);
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                          :: "s"(lds), "v"(g) : "memory", "m0");
         }
 #pragma unroll
@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(const DecodeParams p) {
                     const int cb = min(t * (BNS * ESZ) + bcol[j], nb_src * ESZ - 16);
                     g = base + (int64_t)kb * BK * p.ldb * ESZ + boff[j] + cb;
                 }
-                asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                              :: "s"(lds), "v"(g) : "memory", "m0");
             }
         }

@@ -125,6 +125,9 @@ struct DmaStream {
     // Written as inline asm so the compiler does not model the asynchronous LDS
     // write (it would otherwise drain every outstanding load before each LDS
     // read); completion is enforced by wait_vmcnt + s_barrier in the main loop.
+    // The LDS-DMA reads M0 as its LDS address; a scalar write of M0 needs one wait
+    // state before that read on this GPU family (the s_nop the compiler's hazard
+    // recognizer would insert, which it cannot do inside an asm statement).
     __device__ __forceinline__ void issue(char* stage, int t, int wave) const {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -132,7 +135,7 @@ struct DmaStream {
             const uint32_t lds = (uint32_t)(uintptr_t)(
                 (__attribute__((address_space(3))) char*)(stage + b * 1024));
             const char* g = gp[i] + t * step;
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                          :: "s"(lds), "v"(g) : "memory", "m0");
         }
     }

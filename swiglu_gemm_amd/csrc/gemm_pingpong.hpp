@@ -60,7 +60,7 @@ struct DmaStreamS {
             const int b = widx + i * NWD;
             const uint32_t lds = (uint32_t)(uintptr_t)(
                 (__attribute__((address_space(3))) char*)(stage + b * 1024));
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                          :: "s"(lds), "v"(off[i]), "s"(bt) : "memory", "m0");
         }
     }
