@@ -656,7 +656,11 @@ hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alp
 // Configurations that can run it (see w12_ok in launch16.hpp): 16-bit candidates
 // weighed with the same cost model as the interleaved kernel; e4m3 by rows.
 constexpr Cand16 kCandW12[] = {{10, 4.7}, {8, 4.7}, {32, 3.6}, {6, 3.4}};
-// rows from which the split-weight SwiGLU runs Gate then Up (Kernel-1)
+// Rows from which the split-weight SwiGLU runs Gate then Up (Kernel-1).  Measured
+// on MI355X with the weights cold (bf16 K = 896, N = 4864, M = 128..8192; e4m3 K =
+// 4096, N = 11008, M = 1..4096) it was 1.15-1.9x slower than Gate and Up side by
+// side at every size: it reads A twice and each phase feeds only half of the
+// accumulators per fragment read.  So the side-by-side kernel takes every size.
 constexpr int64_t kSeqMinRows = (int64_t)1 << 40;
 
 bool w12_cfg_ok(const Cfg16& c, const Problem16& q_out) {
