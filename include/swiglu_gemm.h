@@ -102,6 +102,30 @@ typedef struct {
 } sg_epilogue;
 
 /*
+ * sg_gemm_noalloc: sg_gemm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, semantics, kernels and results are those of sg_gemm (bit-identical
+ * output for the same problem).  The split-K partial sums and the decode path's
+ * partial sums, which sg_gemm keeps in library-allocated workspace, live here in a
+ * fixed device array of SG_NOALLOC_SCRATCH_BYTES built into the library: every GPU
+ * the library runs on holds one copy until the process ends.  No call allocates or
+ * frees device memory (its device address is looked up once per device, on the
+ * first call there).
+ * - A problem whose chosen kernels need more scratch than that returns
+ *   SG_STATUS_SCRATCH_LIMIT before enqueuing anything (C is untouched).
+ * - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents; nothing in it needs to start at zero (each partial sum is written
+ *   before it is read).  Calls that overlap in time on one GPU (different streams,
+ *   or host threads enqueuing concurrently) race on it: order them.
+ */
+#define SG_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define SG_STATUS_SCRATCH_LIMIT (-100)
+int sg_gemm_noalloc(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
+                    const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                    int64_t ldc, int dtype, void* stream);
+
+/*
  * sg_gemm_ex: sg_gemm with the steps a fused GEMM epilogue folds in before the
  * accumulator is stored ("GEMM o Coração Matemático" §1, closing paragraph, and
  * §13.3, closing paragraph: bias and activations in the epilogue; "为什么 GEMM 是

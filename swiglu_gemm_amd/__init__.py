@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.sg_gemm.argtypes = [c, c, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
                               ctypes.c_int, vp]
         L.sg_gemm.restype = ctypes.c_int
+        L.sg_gemm_noalloc.argtypes = L.sg_gemm.argtypes
+        L.sg_gemm_noalloc.restype = ctypes.c_int
         L.sg_gemm_ex.argtypes = [c, c, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
                                  ctypes.c_int, ctypes.POINTER(Epilogue), vp]
         L.sg_gemm_ex.restype = ctypes.c_int

@@ -41,6 +41,12 @@ hipError_t launch16_dt(bool ta, bool tb, int epi, int cfg, const Gemm16Params& p
 }
 }  // namespace sg
 
+// sg_gemm_noalloc's scratch: a device array in this library's code object, so it
+// is never allocated by a call (every GPU the library runs on holds its own copy
+// until the process ends).  In host code its name is only a stand-in for the
+// device address, which is looked up once per device (scratch_address below).
+static __device__ __align__(256) char scratch[SG_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kNumCU = 256;               // MI355X: 256 compute units in 8 XCDs
@@ -80,7 +86,26 @@ size_t ws_round(size_t bytes) {
     return want;
 }
 
+// While sg_gemm_noalloc runs on a thread, its fixed scratch stands in for the
+// library-owned buffers: workspace() hands out the fixed buffer (or reports that
+// the problem needs more) and never allocates.  One call uses one buffer kind.
+struct FixedScratch {
+    char* base;
+    size_t cap;
+    bool overflow;
+};
+thread_local FixedScratch* g_fixed = nullptr;
+
 hipError_t workspace(size_t bytes, float** out, int slot = 0) {
+    if (g_fixed) {
+        (void)slot;
+        if (bytes > g_fixed->cap) {
+            g_fixed->overflow = true;
+            return hipErrorOutOfMemory;
+        }
+        *out = reinterpret_cast<float*>(g_fixed->base);
+        return hipSuccess;
+    }
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -97,6 +122,27 @@ hipError_t workspace(size_t bytes, float** out, int slot = 0) {
         w.bytes = want;
     }
     *out = reinterpret_cast<float*>(w.ptr);
+    return hipSuccess;
+}
+
+// Device address of `scratch` on the current device: hipGetSymbolAddress once per
+// device (with that device current), then the kept pointer.
+char* g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(char** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<char*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
     return hipSuccess;
 }
 
@@ -855,13 +901,10 @@ int gemm_run(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha, con
     return status_of(e);
 }
 
-}  // namespace
-
-extern "C" {
-
-int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
-            const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
-            int64_t ldc, int dtype, void* stream) {
+// The argument checks of sg_gemm (BLAS info style: -i for invalid argument i).
+int check_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
+               const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
+               int64_t ldc, int dtype) {
     if (!trans_ok(transA)) return -1;
     if (!trans_ok(transB)) return -2;
     if (M < 0 || M > kMaxDim) return -3;
@@ -883,9 +926,36 @@ int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alp
     if (ldc < (N > 1 ? N : 1)) return -13;
     if (dtype < SG_F32 || dtype > SG_F8E4M3) return -14;
     if ((int64_t)M * N > ((int64_t)1 << 40)) return -3;
-    if (M == 0 || N == 0) return 0;
-    return gemm_run(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, dtype, Batch{},
-                    reinterpret_cast<hipStream_t>(stream));
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sg_gemm(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
+            const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+            int64_t ldc, int dtype, void* stream) {
+    const int v = check_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype);
+    if (v != 0 || M == 0 || N == 0) return v;
+    return gemm_run(is_t(transA), is_t(transB), M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                    dtype, Batch{}, reinterpret_cast<hipStream_t>(stream));
+}
+
+int sg_gemm_noalloc(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
+                    const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                    int64_t ldc, int dtype, void* stream) {
+    const int v = check_gemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc, dtype);
+    if (v != 0 || M == 0 || N == 0) return v;
+    char* base = nullptr;
+    const hipError_t e = scratch_address(&base);
+    if (e != hipSuccess) return status_of(e);
+    FixedScratch fs{base, (size_t)SG_NOALLOC_SCRATCH_BYTES, false};
+    g_fixed = &fs;
+    const int st = gemm_run(is_t(transA), is_t(transB), M, N, K, alpha, A, lda, B, ldb, beta, C,
+                            ldc, dtype, Batch{}, reinterpret_cast<hipStream_t>(stream));
+    g_fixed = nullptr;
+    return fs.overflow ? SG_STATUS_SCRATCH_LIMIT : st;
 }
 
 int sg_gemm_ex(char transA, char transB, int64_t M, int64_t N, int64_t K, float alpha,
@@ -1222,6 +1292,8 @@ const char* sg_status_string(int status) {
         "invalid argument 14", "invalid argument 15", "invalid argument 16",
         "invalid argument 17", "invalid argument 18"};
     if (status <= 0 && status >= -18) return kArg[-status];
+    if (status == SG_STATUS_SCRATCH_LIMIT)
+        return "the problem needs more than the fixed no-allocation scratch buffer holds";
     if (status < 0) return "invalid argument";
     return hipGetErrorString(static_cast<hipError_t>(status));
 }
