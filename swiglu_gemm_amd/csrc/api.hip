@@ -172,7 +172,17 @@ struct Problem16 {
     bool ta, tb;          // transposes
     int esz;              // operand element size (2: fp16/bf16, 1: e4m3)
     int64_t batch = 1;    // problems of a strided batch (one launch, gridDim.z)
+    int64_t lda = 0, ldb = 0;   // leading dimensions (0: not known, no offset limit)
 };
+
+// The direct-to-LDS kernels address each lane's 16-byte chunk as a 32-bit offset from
+// the tile's base: the rows one tile spans (BM or BK of A, BK or BN of B) times the
+// leading dimension must stay below 2^31 bytes.
+bool offsets_fit(int rows_a, int rows_b, const Problem16& q) {
+    constexpr int64_t kLim = (int64_t)1 << 31;
+    return ((int64_t)rows_a * q.lda + 256) * q.esz < kLim &&
+           ((int64_t)rows_b * q.ldb + 256) * q.esz < kLim;
+}
 
 // A strided batch: n problems, operands sA / sB / sC bytes apart.
 struct Batch {
@@ -192,7 +202,7 @@ bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
     const int nw = c.dma == 2 ? 4 : c.WM * c.WN;     // ping-pong: group 0 issues the DMA
     if (!dma_tile_ok(!q.ta, c.BM, c.BK, q.esz, nw) || !dma_tile_ok(q.tb, c.BN, c.BK, q.esz, nw))
         return false;
-    return true;
+    return offsets_fit(q.ta ? c.BK : c.BM, q.tb ? c.BN : c.BK, q);
 }
 
 // K per split: the K tiles of depth bk dealt out as evenly as whole tiles allow
@@ -602,7 +612,7 @@ hipError_t gemm16(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha
     }
     p.vec_a = aligned(A, 16) && (lda % 8 == 0) && (bt.sA % 16 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 8 == 0) && (bt.sB % 16 == 0);
-    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 2, bt.n};
+    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 2, bt.n, lda, ldb};
     int splits = 1;
     float* ws = nullptr;
     hipError_t e = run16<DT>(ta, tb, ex.on ? EPI_GEMM_EX : EPI_GEMM, q, p, C,
@@ -640,7 +650,7 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
     }
     p.vec_a = aligned(A, 16) && (lda % 16 == 0) && (bt.sA % 16 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 16 == 0) && (bt.sB % 16 == 0);
-    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1, bt.n};
+    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1, bt.n, lda, ldb};
     int splits = 1;
     float* ws = nullptr;
     hipError_t e = run16<DT_E4M3>(ta, tb, ex.on ? EPI_GEMM_EX : EPI_GEMM, q, p, C,
@@ -780,7 +790,7 @@ bool seq_cfg_ok(const Cfg16& c, const Problem16& q_out) {
     if ((c.BN / c.WN / 32) % 2 != 0 || c.BN % 64 != 0) return false;
     const int nw = c.WM * c.WN;
     return dma_tile_ok(true, c.BM, c.BK, q_out.esz, nw) &&
-           dma_tile_ok(false, c.BN / 2, c.BK, q_out.esz, nw);
+           dma_tile_ok(false, c.BN / 2, c.BK, q_out.esz, nw) && offsets_fit(c.BM, c.BK, q_out);
 }
 
 // The Gate-then-Up configuration for q_out, or -1: 256-row tiles once they fill the
@@ -1093,7 +1103,7 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
     const int esz = dtype == SG_F8E4M3 ? 1 : 2;
     p.vec_a = aligned(A, 16) && ((K * esz) % 16 == 0);
     p.vec_b = aligned(Wfused, 16) && ((N2 * esz) % 16 == 0);
-    Problem16 q{M, N2, K, (bool)p.vec_a, (bool)p.vec_b, false, false, esz};
+    Problem16 q{M, N2, K, (bool)p.vec_a, (bool)p.vec_b, false, false, esz, 1, K, N2};
     // Y stores are 4 or 8 bytes wide depending on the kernel: require the stricter
     const bool yvec = aligned(Y, 8) && (N % 4 == 0);
     p.epi_flags = aligned(Y, 16) && N % 8 == 0 ? EPI_Y16 : 0;
@@ -1172,7 +1182,8 @@ int sg_swiglu_gemm_w12(const void* A, const void* W1, const void* W2, void* Y, i
     }
     if (K > 0) {
         Problem16 q{M, N, K, aligned(A, 16) && (K * esz) % 16 == 0,
-                    aligned(W1, 16) && aligned(W2, 16) && (N * esz) % 16 == 0, false, false, esz};
+                    aligned(W1, 16) && aligned(W2, 16) && (N * esz) % 16 == 0, false, false, esz,
+                    1, K, N};
         // the pages' dual-kernel choice: Gate then Up (Kernel-1) from kSeqMinRows rows,
         // Gate and Up side by side in one K loop below that (a forced configuration
         // of either kind selects its kernel)
