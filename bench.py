@@ -105,6 +105,47 @@ def time_steps(fn, steps, warmup, torch):
     return start.elapsed_time(stop) / steps          # ms per step
 
 
+def time_graph(fn, nsteps, replays, torch, check=None):
+    """GPU time per step of `fn`, captured into a HIP graph (nsteps steps per graph)
+    and replayed: the per-call host cost of an eager loop is gone, as in a serving
+    loop that replays a graph.  `check`, if given, is called after an eager step and
+    after each of three replays (with eager work and synchronisations between them)
+    and must return the same value each time."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(nsteps):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = check() if check else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(nsteps):
+            fn(i)
+    if check:
+        for _ in range(3):
+            fn(0)                      # eager work between the replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            if not check() == ref:
+                raise RuntimeError("graph replay result differs from the eager one")
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (replays * nsteps)
+    del g
+    return ms
+
+
 def to_dev(bits, dtype, torch):
     t = torch.from_numpy(np.ascontiguousarray(bits))
     if dtype == "e4m3":
@@ -224,8 +265,17 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True, k
         A, W1, W2, _, sa, sw = sets[i % ncold]
         sg.swiglu_gemm_w12(A, W1, W2, Y, sa, sw)
 
-    t_fused = time_steps(fused_over(sets), steps, warmup, torch)
+    t_fused_eager = time_steps(fused_over(sets), steps, warmup, torch)
     cfg = sg.last_config()
+    # the same steps replayed from a HIP graph: kernel time without the per-call host
+    # cost (the last step of each replay writes Y from the same copy of the weights)
+    nsteps = 2 * ncold
+    def y_bits():
+        v = Y.view(torch.int16).to(torch.int64)
+        return (v.sum().item(), (v * v).sum().item(), (v * torch.arange(
+            v.numel(), device=v.device, dtype=torch.int64).view_as(v)).sum().item())
+    replays = max(4, steps // nsteps + 1)
+    t_fused = time_graph(fused_over(sets), nsteps, replays, torch, check=y_bits)
     t_hot = time_steps(fused_over(base), steps, warmup, torch)
     t_w12 = time_steps(w12, steps, warmup, torch)
     cfg_w12 = sg.last_config()
@@ -239,7 +289,8 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True, k
         cfg_seq = sg.last_config()
     finally:
         os.environ.pop("SG_FORCE_CONFIG", None)
-    t_unfused = time_steps(unfused, steps, warmup, torch)
+    t_unfused_eager = time_steps(unfused, steps, warmup, torch)
+    t_unfused = time_graph(unfused, nsteps, replays, torch, check=y_bits)
     if keep is not None:
         A, W1, W2, Wf, sa, sw = base[0]
         sg.swiglu_gemm(A, Wf, Y, sa, sw)
@@ -249,14 +300,19 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True, k
         keep["problem"] = inputs.swiglu_problem(workload, M, N, K, dtype)
     flops = 4.0 * M * N * K
     nbytes = M * K * esz + K * 2 * N * esz + M * N * 2
-    tf = flops / (t_fused * 1e-3) / 1e12
-    gbs = nbytes / (t_fused * 1e-3) / 1e9
-    out = {"dtype": dtype, "M": M, "N": N, "K": K, "ms": round(t_fused, 5),
+    tf = flops / (t_fused_eager * 1e-3) / 1e12
+    gbs = nbytes / (t_fused_eager * 1e-3) / 1e9
+    out = {"dtype": dtype, "M": M, "N": N, "K": K, "ms": round(t_fused_eager, 5),
+           "ms_graph": round(t_fused, 5),
+           "timing": "eager loop of library calls (ms); the same steps replayed from a HIP graph "
+                     "(ms_graph, replays checked against the eager result)",
            "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK[dtype], 4),
            "hbm_gbs_algorithmic": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
            "weights": "cold: %d rotated copies, %.0f MB" % (ncold, ncold * per_set / 1e6),
            "ms_hot": round(t_hot, 5),
-           "unfused_ms": round(t_unfused, 5), "speedup_vs_unfused": round(t_unfused / t_fused, 3),
+           "unfused_ms": round(t_unfused_eager, 5), "unfused_ms_graph": round(t_unfused, 5),
+           "speedup_vs_unfused": round(t_unfused_eager / t_fused_eager, 3),
+           "speedup_vs_unfused_graph": round(t_unfused / t_fused, 3),
            "kernel_config": cfg,
            "w12_ms": round(t_w12, 5), "w12_kernel_config": cfg_w12,
            "seq_ms": round(t_seq, 5), "seq_kernel_config": cfg_seq}
@@ -266,7 +322,7 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True, k
             torch.nn.functional.silu(A @ W1) * (A @ W2)
         t_eager = time_steps(eager_fn, steps, warmup, torch)
         out["torch_eager_ms"] = round(t_eager, 5)
-        out["speedup_vs_torch_eager"] = round(t_eager / t_fused, 3)
+        out["speedup_vs_torch_eager"] = round(t_eager / t_fused_eager, 3)
     return out
 
 
@@ -415,6 +471,47 @@ def sclk_under_load(fn, torch, launches=1500):
     return samples or None
 
 
+def read_bandwidth(torch, nbytes=COPY_BYTES, reps=20):
+    """Streaming rate of a read-only kernel (the diagnostic library's stream_read:
+    16-byte loads, four in flight per thread) over two 512 MiB buffers in turn, so
+    the last-level cache holds neither: the practical HBM read ceiling, the yardstick
+    of the weight-streaming (skinny) shapes.  Best of three grid sizes; None if the
+    diagnostic library is not built."""
+    import ctypes
+    from swiglu_gemm_amd import build as b
+    if not os.path.exists(b.DIAG_LIB):
+        return None
+    lib = ctypes.CDLL(b.DIAG_LIB)
+    lib.sg_diag_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+    lib.sg_diag_stream_read.restype = ctypes.c_int
+    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0") for _ in range(2)]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = 0.0
+    for blocks in (1024, 2048, 4096):
+        out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda:0")
+
+        def run(i):
+            rc = lib.sg_diag_stream_read(ctypes.c_void_p(bufs[i % 2].data_ptr()), nbytes,
+                                         ctypes.c_void_p(out.data_ptr()), blocks, st)
+            assert rc == 0, rc
+        for i in range(4):
+            run(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(reps):
+            run(i)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / reps
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    del bufs
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
 def copy_bandwidth(torch, nbytes=COPY_BYTES, reps=20):
     """Streaming rate of a plain device-to-device copy (read + write bytes per
     second) over two buffer pairs, 2 GiB in all, so the last-level cache holds
@@ -472,6 +569,9 @@ def pmc_probe():
     for _ in range(3):
         sg.gemm(A, B, C)
     torch.cuda.synchronize()
+    for _ in range(3):                 # hipBLASLt on the same tensors: the yardstick
+        torch.mm(A, B, out=C)
+    torch.cuda.synchronize()
     print("pmc probe done: %s" % sg.last_config(), flush=True)
 
 
@@ -523,13 +623,19 @@ def pmc_summarize(fetch_csv, write_csv):
             raise SystemExit("counter file %s lacks the copy or GEMM dispatches" % path)
         copy_kib = max(copy)                     # the 512 MiB copy dominates
         factor = COPY_BYTES / (copy_kib * 1024.0)
+        blas = [v for n, v in d if n.startswith("Cijk") or "gemm" in n.lower() and "dma" not in n]
         out[counter] = {"gemm_kib_per_launch": sum(gemm) / len(gemm),
                         "copy_kib": copy_kib, "scale_factor": factor,
                         "gemm_bytes_per_launch": sum(gemm) / len(gemm) * 1024.0 * factor}
+        if blas:
+            out[counter]["hipblaslt_bytes_per_launch"] = sum(blas) / len(blas) * 1024.0 * factor
     total = out["FETCH_SIZE"]["gemm_bytes_per_launch"] + out["WRITE_SIZE"]["gemm_bytes_per_launch"]
     res = {"kernel_src_sha": kernel_source_hash(), "workload": "fp16 GEMM NN 8192^3",
            "algorithmic_bytes_per_launch": 3 * 8192 * 8192 * 2,
            "hbm_bytes_per_launch": total, "counters": out}
+    if all("hipblaslt_bytes_per_launch" in out[c] for c in out):
+        res["hipblaslt_hbm_bytes_per_launch"] = sum(out[c]["hipblaslt_bytes_per_launch"]
+                                                    for c in out)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
@@ -1082,6 +1188,7 @@ def main():
                        "sclk_mhz_under_load": sclk_load})
     print("bench: device copy bandwidth", file=sys.stderr, flush=True)
     out["env"]["copy_gbs"] = copy_bandwidth(torch)
+    out["env"]["read_gbs"] = read_bandwidth(torch)
     if not args.quick:
         print("bench: bf16 8192^3 GEMM and the ragged bf16 GEMMs", file=sys.stderr, flush=True)
         out["gemm_bf16_8192"] = bench_gemm_bf16_8192(torch, sg, max(10, args.steps // 2),
@@ -1103,6 +1210,10 @@ def main():
         sw.append(bench_swiglu(torch, sg, inputs, dt, m, n, k, max(10, args.steps // 2),
                                args.warmup, keep=kept if (dt, m) == ("bf16", 2048) else None))
         torch.cuda.empty_cache()
+    rb = out["env"].get("read_gbs")
+    for s in sw:                  # against what this board's HBM delivers to a plain read
+        if rb:
+            s["frac_of_read_bw"] = round(s["hbm_gbs_algorithmic"] / rb, 4)
     out["swiglu_m2048"] = [s for s in sw if s["dtype"] == "bf16" and s["M"] == 2048][0]
     if len(sw) > 1:
         out["swiglu_all"] = sw

@@ -114,13 +114,29 @@ def _check(status: int, what: str) -> None:
 # extent): the library sees bare pointers, so a short or mistyped tensor would
 # otherwise send the kernels past its allocation.  The device is checked last,
 # so that every other check can be exercised without a GPU.
+_TABLES = None
+
+
+def _tables():
+    """dtype -> code and code -> accepted output dtypes (built once: these checks run
+    on every call, so they avoid per-call allocations)."""
+    global _TABLES
+    if _TABLES is None:
+        import torch
+        code = {torch.float32: SG_F32, torch.float16: SG_F16, torch.bfloat16: SG_BF16,
+                torch.float8_e4m3fn: SG_F8E4M3, torch.uint8: SG_F8E4M3}
+        out = {SG_F32: (torch.float32,), SG_F16: (torch.float16,), SG_BF16: (torch.bfloat16,),
+               SG_F8E4M3: (torch.bfloat16,)}
+        _TABLES = (code, out, (torch.float8_e4m3fn, torch.uint8),
+                   (torch.float32, torch.float16, torch.bfloat16))
+    return _TABLES
+
+
 def _dtype_code(t) -> int:
-    import torch
-    m = {torch.float32: SG_F32, torch.float16: SG_F16, torch.bfloat16: SG_BF16,
-         torch.float8_e4m3fn: SG_F8E4M3, torch.uint8: SG_F8E4M3}
-    if t.dtype not in m:
+    code = _tables()[0].get(t.dtype)
+    if code is None:
         raise TypeError("unsupported dtype %s" % t.dtype)
-    return m[t.dtype]
+    return code
 
 
 # bytes per element of the operands and of the output, per dtype code
@@ -129,9 +145,7 @@ _IN_SIZE = {SG_F32: 4, SG_F16: 2, SG_BF16: 2, SG_F8E4M3: 1}
 
 def _out_dtypes(code: int):
     """torch dtypes accepted for C / Y when the operands have dtype code `code`."""
-    import torch
-    return {SG_F32: (torch.float32,), SG_F16: (torch.float16,), SG_BF16: (torch.bfloat16,),
-            SG_F8E4M3: (torch.bfloat16,)}[code]
+    return _tables()[1][code]
 
 
 def _stream(t):
@@ -159,6 +173,8 @@ def _avail(t) -> int:
 
 
 def _need(t, name: str, elems: int) -> None:
+    if elems <= t.numel() and t.is_contiguous():
+        return                    # the view itself covers the span
     if elems > _avail(t):
         raise ValueError("%s holds %d elements from its first one, the call needs %d"
                          % (name, _avail(t), elems))
@@ -177,24 +193,45 @@ def _on_gpu(*ts) -> None:
 
 
 def _contig(t, name: str, shape) -> None:
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
 
 
+def _view_ld(sh, st) -> int:
+    """Leading dimension of a 2-D (or batched) row-major view from its shape and strides."""
+    if len(sh) == 2 and sh[0] <= 1:
+        return max(sh[1], 1)
+    return max(st[-2], 1)
+
+
+def _need_span(t, sh, name: str, elems: int) -> None:
+    n = 1
+    for d in sh:
+        n *= d
+    if elems <= n and t.is_contiguous():
+        return                    # the view itself covers the span
+    if elems > _avail(t):
+        raise ValueError("%s holds %d elements from its first one, the call needs %d"
+                         % (name, _avail(t), elems))
+
+
 def _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc, c_dtypes, batch=1,
                strides=(0, 0, 0)):
-    """Sizes and leading dimensions of a GEMM call, checked against the tensors."""
+    """Sizes and leading dimensions of a GEMM call, checked against the tensors (each
+    tensor's shape and strides are read once: these checks run on every call)."""
     if ta not in ("N", "T") or tb not in ("N", "T"):
         raise ValueError("transA and transB must be 'N' or 'T'")
+    ash, bsh, csh = tuple(A.shape), tuple(B.shape), tuple(C.shape)
+    ast, bst, cst = A.stride(), B.stride(), C.stride()
     if M is None:
-        if A.dim() < 2 or B.dim() < 2:
+        if len(ash) < 2 or len(bsh) < 2:
             raise ValueError("A and B must have at least 2 dimensions")
-        M = A.size(-1) if ta == "T" else A.size(-2)
-        K = A.size(-2) if ta == "T" else A.size(-1)
-        N = B.size(-2) if tb == "T" else B.size(-1)
-        kb = B.size(-1) if tb == "T" else B.size(-2)
+        M = ash[-1] if ta == "T" else ash[-2]
+        K = ash[-2] if ta == "T" else ash[-1]
+        N = bsh[-2] if tb == "T" else bsh[-1]
+        kb = bsh[-1] if tb == "T" else bsh[-2]
         if kb != K:
             raise ValueError("op(A) is %d x %d but op(B) has %d rows" % (M, K, kb))
     elif N is None or K is None:
@@ -202,24 +239,31 @@ def _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc, c_dtypes, batch=1,
     M, N, K = int(M), int(N), int(K)
     if M < 0 or N < 0 or K < 0:
         raise ValueError("M, N and K must be >= 0")
-    lda = (_ld(A) if A.dim() == 2 else int(A.stride(-2))) if lda is None else int(lda)
-    ldb = (_ld(B) if B.dim() == 2 else int(B.stride(-2))) if ldb is None else int(ldb)
-    ldc = (_ld(C) if C.dim() == 2 else int(C.stride(-2))) if ldc is None else int(ldc)
-    _same_size(A, "A", code, "the operand dtype")
-    _same_size(B, "B", code, "the operand dtype")
+    for sh, st, name in ((ash, ast, "A"), (bsh, bst, "B"), (csh, cst, "C")):
+        if len(sh) >= 2 and sh[-1] > 1 and st[-1] != 1:
+            raise ValueError("%s: the last dimension must be contiguous (stride 1)" % name)
+    lda = (_view_ld(ash, ast) if len(ash) >= 2 else 1) if lda is None else int(lda)
+    ldb = (_view_ld(bsh, bst) if len(bsh) >= 2 else 1) if ldb is None else int(ldb)
+    ldc = (_view_ld(csh, cst) if len(csh) >= 2 else 1) if ldc is None else int(ldc)
+    want = _IN_SIZE[code]
+    if A.element_size() != want:
+        raise TypeError("A has %d-byte elements, the operand dtype needs %d"
+                        % (A.element_size(), want))
+    if B.element_size() != want:
+        raise TypeError("B has %d-byte elements, the operand dtype needs %d"
+                        % (B.element_size(), want))
     if C.dtype not in c_dtypes:
         raise TypeError("C has dtype %s, expected one of %s" % (C.dtype, c_dtypes))
-    for t, name in ((A, "A"), (B, "B"), (C, "C")):
-        if t.dim() >= 2 and t.size(-1) > 1 and t.stride(-1) != 1:
-            raise ValueError("%s: the last dimension must be contiguous (stride 1)" % name)
     sA, sB, sC = strides
     last = max(int(batch) - 1, 0)
     if M and K:
-        _need(A, "A", last * sA + (_span(K, M, lda) if ta == "T" else _span(M, K, lda)))
+        _need_span(A, ash, "A",
+                   last * sA + (_span(K, M, lda) if ta == "T" else _span(M, K, lda)))
     if N and K:
-        _need(B, "B", last * sB + (_span(N, K, ldb) if tb == "T" else _span(K, N, ldb)))
+        _need_span(B, bsh, "B",
+                   last * sB + (_span(N, K, ldb) if tb == "T" else _span(K, N, ldb)))
     if M and N:
-        _need(C, "C", last * sC + _span(M, N, ldc))
+        _need_span(C, csh, "C", last * sC + _span(M, N, ldc))
     return M, N, K, lda, ldb, ldc
 
 
@@ -248,15 +292,14 @@ def gemm_ex(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N",
     'none', 'relu', 'gelu', 'gelu_tanh' or 'silu'.  out_scale: None (C has gemm's
     output type) or the per-tensor scale of an e4m3 output (C an e4m3 / uint8
     tensor holding the codes of y / out_scale; beta must be 0)."""
-    import torch
     code = _dtype_code(A) if dtype is None else dtype
     ta, tb = transA.upper(), transB.upper()
-    c_dtypes = (torch.float8_e4m3fn, torch.uint8) if out_scale is not None else _out_dtypes(code)
+    c_dtypes = _tables()[2] if out_scale is not None else _out_dtypes(code)
     M, N, K, lda, ldb, ldc = _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc, c_dtypes)
     if activation not in ACTIVATIONS:
         raise ValueError("unknown activation %r" % activation)
     if bias is not None:
-        if bias.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        if bias.dtype not in _tables()[3]:
             raise TypeError("bias must be fp32, fp16 or bf16")
         if bias.dim() != 1 or not bias.is_contiguous() or bias.numel() < N:
             raise ValueError("bias must be a contiguous vector of at least N = %d values" % N)
@@ -300,7 +343,6 @@ def gemm_strided_batched(A, B, C, batch, strideA, strideB, strideC, alpha: float
 def _swiglu_args(A, W_list, Y, two_n: bool):
     """M, N, K of a SwiGLU call, with A [M, K], each weight [K, 2N] (two_n) or [K, N]
     and Y [M, N] contiguous; operands of one dtype, Y bf16 (fp16 for fp16 inputs)."""
-    import torch
     if A.dim() != 2 or any(w.dim() != 2 for w in W_list):
         raise ValueError("A and the weights must be 2-D")
     M, K = int(A.shape[0]), int(A.shape[1])

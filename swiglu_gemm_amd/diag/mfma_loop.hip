@@ -84,7 +84,106 @@ __global__ void __launch_bounds__(256) mfma_loop(const u32x4* src, int nsrc, int
     out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Streams n16 16-byte chunks of src through the vector memory path (four loads in
+// flight per thread per step, grid-stride) and folds them with XOR into one word
+// per thread, so the only work is reading: the HBM read ceiling of the board.
+__global__ void __launch_bounds__(256) stream_read(const u32x4* src, int64_t n16, uint32_t* out) {
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(src + i);
+        const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+        const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < n16; i += stride) acc ^= src[i];
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// Per-CU L2 -> CU throughput on a region small enough to stay in L2: each
+// work-group (256 threads, one per CU) reads `region` bytes `iters` times.
+// KIND 0: global_load_dwordx4 into registers (DEPTH loads in flight per thread,
+// XOR-folded); KIND 1: global_load_lds_dwordx4 into an LDS ring (DEPTH KiB-blocks of
+// each wave in flight, the ring 64 KiB).
+template <int KIND, int DEPTH>
+__global__ void __launch_bounds__(1024) l2_stream(const char* src, int64_t region, int iters,
+                                                  uint32_t* out) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nthr = blockDim.x;
+    const int64_t per_pass = (int64_t)nthr * 16;                // bytes per WG instruction round
+    const int64_t passes = region / per_pass;
+    if constexpr (KIND == 0) {
+        u32x4 acc = {0u, 0u, 0u, 0u};
+        for (int it = 0; it < iters; ++it) {
+            for (int64_t p = 0; p + DEPTH <= passes; p += DEPTH) {
+                u32x4 v[DEPTH];
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d)
+                    v[d] = *reinterpret_cast<const u32x4*>(src + (p + d) * per_pass +
+                                                           threadIdx.x * 16);
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) acc ^= v[d];
+            }
+        }
+        out[(int64_t)blockIdx.x * nthr + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    } else {
+        __shared__ __attribute__((aligned(1024))) char ring[65536];
+        // wave w's block for pass p: ring[((p % 4) * 16 + w) * 1024], 64 lanes x 16 B
+        int64_t issued = 0;
+        for (int it = 0; it < iters; ++it) {
+            for (int64_t p = 0; p < passes; ++p, ++issued) {
+                const uint32_t lds = (uint32_t)(uintptr_t)(
+                    (__attribute__((address_space(3))) char*)(ring + ((issued % 4) * 16 + wave) * 1024));
+                const char* g = src + p * per_pass + threadIdx.x * 16;
+                asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                             :: "s"(lds), "v"(g) : "memory", "m0");
+                if (issued >= DEPTH) __builtin_amdgcn_s_waitcnt((DEPTH & 15) | (7 << 4) | (15 << 8) | ((DEPTH >> 4) << 14));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        out[(int64_t)blockIdx.x * nthr + threadIdx.x] =
+            *reinterpret_cast<const uint32_t*>(ring + threadIdx.x * 4);
+    }
+}
+
 }  // namespace
+
+// Per-CU L2 -> CU throughput probe (see l2_stream): kind 0 registers, kind 1 LDS DMA;
+// depth in {4, 8, 16}; waves 1..16 per work-group; region (a multiple of waves*1024
+// bytes) read iters times by each of `blocks` work-groups; out: blocks*64*waves words.
+extern "C" int sg_diag_l2_stream(int kind, int depth, const void* src, int64_t region, int iters,
+                                 int blocks, int waves, void* out, void* stream) {
+    if (!src || !out || waves < 1 || waves > 16 || region < waves * 1024 ||
+        region % (waves * 1024) != 0 || blocks <= 0 || iters < 1)
+        return (int)hipErrorInvalidValue;
+    hipStream_t st = (hipStream_t)stream;
+    const char* s = (const char*)src;
+    uint32_t* o = (uint32_t*)out;
+#define L2S(K, D) hipLaunchKernelGGL((l2_stream<K, D>), dim3(blocks), dim3(64 * waves), 0, st, s, region, iters, o)
+    if (kind == 0 && depth == 4) L2S(0, 4);
+    else if (kind == 0 && depth == 8) L2S(0, 8);
+    else if (kind == 0 && depth == 16) L2S(0, 16);
+    else if (kind == 1 && depth == 4) L2S(1, 4);
+    else if (kind == 1 && depth == 8) L2S(1, 8);
+    else if (kind == 1 && depth == 16) L2S(1, 16);
+    else return (int)hipErrorInvalidValue;
+#undef L2S
+    return (int)hipGetLastError();
+}
+
+// Reads `bytes` (a multiple of 16) from the device buffer src with `blocks`
+// work-groups of 256 threads; out: blocks*256 words (device).  Returns a hipError_t.
+extern "C" int sg_diag_stream_read(const void* src, int64_t bytes, void* out, int blocks,
+                                   void* stream) {
+    if (!src || !out || bytes < 0 || bytes % 16 != 0 || blocks <= 0)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_read, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4*)src, bytes / 16, (uint32_t*)out);
+    return (int)hipGetLastError();
+}
 
 // Launches `blocks` work-groups of 4 waves.  src: nsrc 16-byte operand chunks
 // (device); out: blocks*256 floats (device).  Returns a hipError_t.  Work:
