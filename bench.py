@@ -755,7 +755,7 @@ def pmc_swiglu_summarize(fetch_csv, write_csv, sq_csv):
     print("\n".join(lines))
 
 
-SWEEP_CFGS = (10, 8, 34, 35, 9, 27, 5, 41, 3, 40, 19, 42, 13, 36, 37, 30, 38, 39, 6, 31)
+SWEEP_CFGS = (10, 8, 34, 35, 9, 27, 5, 41, 3, 40, 13, 36, 37, 30, 38, 39, 6, 31)
 
 
 def stage_sweep(steps):

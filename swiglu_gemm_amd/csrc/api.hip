@@ -147,11 +147,14 @@ hipError_t scratch_address(char** out) {
 }
 
 // ---------------------------------------------------------------- configs
+// SG_FORCE_CONFIG=<id>[,<splits>] (an id outside the table, e.g. -1, keeps the large-
+// tile choice but turns the decode kernels off); a retired id counts as no override.
 bool forced_config(int* cfg, int* splits) {
     const char* s = std::getenv("SG_FORCE_CONFIG");
     if (!s || !*s) return false;
     int c = -1, k = 0;
     if (std::sscanf(s, "%d,%d", &c, &k) < 1) return false;
+    if (c >= 0 && c < kNumCfg16 && !cfg_live(c)) return false;
     *cfg = c;
     *splits = k;
     return true;
@@ -194,12 +197,11 @@ struct Batch {
 // operands and rows (base pointers and ld) and DMA-compatible tiles.  Edge rows and
 // chunks are clamped in-kernel; a row-contiguous operand's row (M or N elements)
 // may end inside a chunk.  A K tail (K not a multiple of BK) is loaded through
-// registers by the one-stream kernel; the ping-pong kernel needs whole K tiles.
+// registers.
 bool dma_ok(const Cfg16& c, const Problem16& q, int64_t kps) {
-    if (!c.dma || c.dma == 3 || c.e4m3 != (q.esz == 1)) return false;
+    if (c.dma != 1 || c.e4m3 != (q.esz == 1)) return false;
     if (!q.vec_a || !q.vec_b || kps % c.BK != 0) return false;
-    if (c.dma == 2 && q.K % c.BK != 0) return false;
-    const int nw = c.dma == 2 ? 4 : c.WM * c.WN;     // ping-pong: group 0 issues the DMA
+    const int nw = c.WM * c.WN;
     if (!dma_tile_ok(!q.ta, c.BM, c.BK, q.esz, nw) || !dma_tile_ok(q.tb, c.BN, c.BK, q.esz, nw))
         return false;
     return offsets_fit(q.ta ? c.BK : c.BM, q.tb ? c.BN : c.BK, q);

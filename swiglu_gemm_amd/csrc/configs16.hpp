@@ -6,9 +6,9 @@ namespace sg {
 struct Cfg16 {
     int e4m3;           // 1: e4m3 operands (BK in bytes), 0: fp16 / bf16 operands
     int dma;            // 0: register-staged (gemm16.hpp), 1: direct global->LDS ring
-                        // (gemm16_dma.hpp), 2: the same ring with the 8-wave ping-pong
-                        // schedule (gemm_pingpong.hpp), 3: the direct ring for the
-                        // split-weight SwiGLU with Gate then Up (EPI_SWIGLU_SEQ only)
+                        // (gemm16_dma.hpp), 3: the direct ring for the split-weight
+                        // SwiGLU with Gate then Up (EPI_SWIGLU_SEQ only); -1: a retired
+                        // id, kept so that the others stay stable
     int BM, BN, BK, S;  // tile and LDS stages
     int WM, WN;         // waves along M and N
     const char* name;
@@ -35,18 +35,18 @@ constexpr Cfg16 kCfg16[] = {
     {1, 1, 128, 128, 128, 2, 2, 4, "e4m3 dma 128x128x128 s2 2x4w"},
     {1, 1, 32, 256, 128, 4, 1, 4, "e4m3 dma 32x256x128 s4 1x4w"},
     {1, 1, 32, 128, 128, 4, 1, 4, "e4m3 dma 32x128x128 s4 1x4w"},
-    {0, 2, 256, 256, 64, 2, 4, 2, "pp 256x256x64 s2 4x2w"},
-    {0, 2, 256, 256, 32, 4, 4, 2, "pp 256x256x32 s4 4x2w"},
-    {0, 2, 256, 256, 64, 2, 2, 4, "pp 256x256x64 s2 2x4w"},
-    {1, 2, 256, 256, 128, 2, 4, 2, "e4m3 pp 256x256x128 s2 4x2w"},
-    {0, 2, 128, 256, 64, 2, 2, 4, "pp 128x256x64 s2 2x4w"},
-    {1, 2, 128, 256, 128, 2, 2, 4, "e4m3 pp 128x256x128 s2 2x4w"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
     {0, 1, 256, 320, 64, 2, 4, 2, "dma 256x320x64 s2 4x2w"},
-    {0, 2, 256, 320, 64, 2, 4, 2, "pp 256x320x64 s2 4x2w"},
-    {0, 2, 256, 320, 32, 4, 4, 2, "pp 256x320x32 s4 4x2w"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
     {0, 1, 256, 256, 32, 5, 4, 2, "dma 256x256x32 s5 4x2w"},
     {0, 1, 256, 256, 32, 5, 2, 4, "dma 256x256x32 s5 2x4w"},
-    {0, 2, 256, 256, 32, 5, 4, 2, "pp 256x256x32 s5 4x2w"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
     {0, 1, 128, 128, 64, 5, 2, 4, "dma 128x128x64 s5 2x4w"},
     {0, 1, 128, 128, 32, 8, 2, 2, "dma 128x128x32 s8 2x2w"},
     {0, 1, 128, 256, 64, 3, 2, 4, "dma 128x256x64 s3 2x4w"},
@@ -60,7 +60,7 @@ constexpr Cfg16 kCfg16[] = {
     {0, 1, 128, 128, 32, 3, 2, 2, "sweep dma 128x128x32 s3 2x2w"},
     {0, 1, 256, 256, 32, 5, 2, 2, "sweep dma 256x256x32 s5 2x2w"},
     {0, 1, 256, 256, 32, 3, 2, 2, "sweep dma 256x256x32 s3 2x2w"},
-    {0, 2, 256, 256, 32, 5, 4, 2, "sweep pp 256x256x32 s5 4x2w"},
+    {0, -1, 0, 0, 0, 0, 0, 0, "retired"},
     // 64-row tiles: twice the work-groups of 128-row tiles for 65..128-row problems
     {0, 1, 64, 256, 64, 3, 1, 4, "dma 64x256x64 s3 1x4w"},
     {0, 1, 64, 128, 64, 4, 1, 4, "dma 64x128x64 s4 1x4w"},
@@ -77,8 +77,11 @@ constexpr Cfg16 kCfg16[] = {
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
+// Whether id names a configuration that is still built (in range, not retired).
+constexpr bool cfg_live(int id) { return id >= 0 && id < kNumCfg16 && kCfg16[id].dma >= 0; }
+
 constexpr int kFirstCfgE4M3 = 14;
-constexpr int kFirstSweepCfg = 34;   // ids 34..42: the fp16 NN pipeline-depth study
+constexpr int kFirstSweepCfg = 34;   // ids 34..41: the fp16 NN pipeline-depth study
 
 // Whether the direct-to-LDS kernel supports an operand tile: k-contiguous rows of
 // 64 or 128 bytes; row-contiguous rows of 128..1024 bytes made of an even number
@@ -108,16 +111,9 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(11, 1, 128, 256, 64, 2, 2, 2)    \
     X(12, 1, 256, 128, 64, 2, 2, 2)    \
     X(13, 1, 128, 128, 64, 2, 2, 4)     \
-    X(18, 2, 256, 256, 64, 2, 4, 2)    \
-    X(19, 2, 256, 256, 32, 4, 4, 2)    \
-    X(20, 2, 256, 256, 64, 2, 2, 4)    \
-    X(22, 2, 128, 256, 64, 2, 2, 4)    \
     X(24, 1, 256, 320, 64, 2, 4, 2)    \
-    X(25, 2, 256, 320, 64, 2, 4, 2)    \
-    X(26, 2, 256, 320, 32, 4, 4, 2)    \
     X(27, 1, 256, 256, 32, 5, 4, 2)    \
     X(28, 1, 256, 256, 32, 5, 2, 4)    \
-    X(29, 2, 256, 256, 32, 5, 4, 2)    \
     X(30, 1, 128, 128, 64, 5, 2, 4)    \
     X(31, 1, 128, 128, 32, 8, 2, 2)    \
     X(32, 1, 128, 256, 64, 3, 2, 4)    \
@@ -135,8 +131,7 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(38, 1, 128, 128, 32, 2, 2, 2)    \
     X(39, 1, 128, 128, 32, 3, 2, 2)    \
     X(40, 1, 256, 256, 32, 5, 2, 2)    \
-    X(41, 1, 256, 256, 32, 3, 2, 2)    \
-    X(42, 2, 256, 256, 32, 5, 4, 2)
+    X(41, 1, 256, 256, 32, 3, 2, 2)
 
 // the configurations the library chooses by itself, also compiled with the extra
 // epilogue steps (EPI_GEMM_EX); any other one maps to the nearest of these (the
@@ -172,8 +167,6 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(15, 1, 128, 128, 128, 2, 2, 4)   \
     X(16, 1, 32, 256, 128, 4, 1, 4)    \
     X(17, 1, 32, 128, 128, 4, 1, 4)    \
-    X(21, 2, 256, 256, 128, 2, 4, 2)   \
-    X(23, 2, 128, 256, 128, 2, 2, 4)   \
     X(33, 1, 128, 256, 128, 3, 2, 2)   \
     X(45, 1, 128, 256, 128, 3, 2, 4)   \
     X(47, 1, 128, 192, 128, 3, 4, 2)

@@ -39,8 +39,8 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 // EPI_GEMM_EX: y = act(alpha*acc + beta*C_old + bias[n]), stored in DT or, for an
 // e4m3 output, as the e4m3fn code of y * inv_scale.  This form serves the register-
-// staged and ping-pong kernels, and the direct-to-LDS kernel when C is not 16-byte
-// aligned or ldc is not a multiple of 8 (else epilogue_gemm_ex_rows_lds).  Each wave stages one 32 x 32
+// staged kernel, and the direct-to-LDS kernel when C is not 16-byte aligned or ldc
+// is not a multiple of 8 (else epilogue_gemm_ex_rows_lds).  Each wave stages one 32 x 32
 // fp32 fragment at a time in a region of the (by now idle) LDS ring of its own, and
 // a rolled loop then finishes four consecutive columns per lane (row-contiguous
 // stores).  The accumulator is only ever indexed by constants: with the

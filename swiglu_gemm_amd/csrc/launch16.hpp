@@ -8,7 +8,6 @@
 #include "configs16.hpp"
 #include "gemm16.hpp"
 #include "gemm16_dma.hpp"
-#include "gemm_pingpong.hpp"
 
 namespace sg {
 
@@ -27,7 +26,7 @@ inline hipError_t launch_grid(Kern k, const Gemm16Params& p, int splits, int thr
 template <int DT, bool TA, bool TB, int DMA, int BM, int BN, int BK, int WM, int WN>
 constexpr bool w12_ok() {
     constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
-    return (DMA == 1 || (DT == DT_E4M3 && DMA != 2)) && !TA && !TB && (BN / WN / 32) % 2 == 0 &&
+    return (DMA == 1 || DT == DT_E4M3) && !TA && !TB && (BN / WN / 32) % 2 == 0 &&
            BN % 64 == 0 && dma_tile_ok(true, BM, BK, ESZ, WM * WN) &&
            dma_tile_ok(false, BN / 2, BK, ESZ, WM * WN);
 }
@@ -38,12 +37,6 @@ inline hipError_t launch_one(const Gemm16Params& p, int splits, hipStream_t st) 
     if constexpr (EPI == EPI_SWIGLU_W12 || EPI == EPI_SWIGLU_SEQ) {
         if constexpr (w12_ok<DT, TA, TB, DMA, BM, BN, BK, WM, WN>())
             return launch_grid(gemm_dma_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
-                               64 * WM * WN, st);
-        else
-            return hipErrorInvalidValue;
-    } else if constexpr (DMA == 2) {
-        if constexpr (dma_tile_ok(!TA, BM, BK, ESZ, 4) && dma_tile_ok(TB, BN, BK, ESZ, 4))
-            return launch_grid(gemm_pp_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
                                64 * WM * WN, st);
         else
             return hipErrorInvalidValue;

@@ -14,8 +14,8 @@ from helpers import assert_close, bits_equal, from_dev, split_count, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-CFGS16 = list(range(14)) + [18, 19, 20, 22] + list(range(24, 33)) + [43, 44, 46, 48]   # every 16-bit id
-WIDE = [24, 25, 26]                # 320-column tiles (640-byte LDS rows)
+CFGS16 = list(range(14)) + [24] + list(range(27, 33)) + [43, 44, 46, 48]   # every 16-bit id
+WIDE = [24]                        # 320-column tiles (640-byte LDS rows)
 TRANS = ["NN", "NT", "TN", "TT"]
 
 
@@ -86,7 +86,7 @@ def test_output_rounding_bit_exact(cfg, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("cfg", [10, 24, 46, 48, 13, 30, 32, 43, 44, 5, 20])
+@pytest.mark.parametrize("cfg", [10, 24, 46, 48, 13, 30, 32, 43, 44, 5, 8])
 def test_output_rounding_bit_exact_many_tiles(cfg, dtype):
     """More work-groups than one round of the CUs: the row-staged epilogue of the
     direct-to-LDS kernels (full tiles) next to the register epilogue (edge tiles:
@@ -276,7 +276,7 @@ def test_wide_tiles_swiglu_and_identity(cfg):
     assert bits_equal(from_dev(C), Ab), desc
 
 
-@pytest.mark.parametrize("cfg", [34, 35, 36, 37, 38, 39, 40, 41, 42])
+@pytest.mark.parametrize("cfg", [34, 35, 36, 37, 38, 39, 40, 41])
 def test_pipeline_study_configs_fp16_nn(cfg):
     """The pipeline-depth study configurations (fp16 NN GEMM only) against the
     oracle, on a ragged shape that spans several tiles; other dtypes reject them."""
