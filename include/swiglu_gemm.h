@@ -106,14 +106,18 @@ typedef struct {
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  *
  * Arguments, semantics, kernels and results are those of sg_gemm (bit-identical
- * output for the same problem).  The split-K partial sums and the decode path's
- * partial sums, which sg_gemm keeps in library-allocated workspace, live here in a
- * fixed device array of SG_NOALLOC_SCRATCH_BYTES built into the library: every GPU
- * the library runs on holds one copy until the process ends.  No call allocates or
- * frees device memory (its device address is looked up once per device, on the
- * first call there).
+ * output for the same problem, with one exception below).  The split-K partial
+ * sums, the decode path's partial sums and the 16-byte-row copies of e4m3 operands
+ * whose rows are not 16-byte multiples, which sg_gemm keeps in library-allocated
+ * workspace, live here in a fixed device array of SG_NOALLOC_SCRATCH_BYTES built
+ * into the library: every GPU the library runs on holds one copy until the process
+ * ends.  No call allocates or frees device memory (its device address is looked up
+ * once per device, on the first call there).
  * - A problem whose chosen kernels need more scratch than that returns
  *   SG_STATUS_SCRATCH_LIMIT before enqueuing anything (C is untouched).
+ * - The exception: e4m3 operands whose copies would not fit run the one-thread-
+ *   per-output kernel instead of the tile kernels (same tolerance, different
+ *   summation order, so not the same bits as sg_gemm).
  * - Every call on one GPU shares that GPU's array, which keeps the last call's
  *   contents; nothing in it needs to start at zero (each partial sum is written
  *   before it is read).  Calls that overlap in time on one GPU (different streams,

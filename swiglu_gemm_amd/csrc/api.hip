@@ -74,8 +74,9 @@ struct Workspace {
 std::mutex g_ws_mu;
 // slot 0: split-K partials; slot 1: W_fused built from separate W1, W2 (the
 // split-weight SwiGLU's fallback for shapes its own kernel cannot take); slot 2:
-// partial sums of the decode path's split column tiles
-constexpr int kSlots = 3;
+// partial sums of the decode path's split column tiles; slot 3: e4m3 operands re-
+// laid with 16-byte rows
+constexpr int kSlots = 4;
 constexpr int kMaxDevices = 64;
 Workspace g_ws[kSlots][kMaxDevices];
 std::vector<void*> g_retired[kMaxDevices];
@@ -87,23 +88,35 @@ size_t ws_round(size_t bytes) {
 }
 
 // While sg_gemm_noalloc runs on a thread, its fixed scratch stands in for the
-// library-owned buffers: workspace() hands out the fixed buffer (or reports that
-// the problem needs more) and never allocates.  One call uses one buffer kind.
+// library-owned buffers: workspace() hands out consecutive 256-byte aligned pieces
+// of it, one per request of the call (or reports that the problem needs more),
+// and never allocates.
 struct FixedScratch {
     char* base;
     size_t cap;
     bool overflow;
+    size_t used = 0;
 };
 thread_local FixedScratch* g_fixed = nullptr;
+
+size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
+
+// Whether a workspace request of `bytes` can be met without failing the call: always
+// with library-owned buffers (an allocation failure is an error like any other),
+// within what is left of the fixed scratch otherwise.
+bool workspace_fits(size_t bytes) {
+    return !g_fixed || g_fixed->used + round256(bytes) <= g_fixed->cap;
+}
 
 hipError_t workspace(size_t bytes, float** out, int slot = 0) {
     if (g_fixed) {
         (void)slot;
-        if (bytes > g_fixed->cap) {
+        if (!workspace_fits(bytes)) {
             g_fixed->overflow = true;
             return hipErrorOutOfMemory;
         }
-        *out = reinterpret_cast<float*>(g_fixed->base);
+        *out = reinterpret_cast<float*>(g_fixed->base + g_fixed->used);
+        g_fixed->used += round256(bytes);
         return hipSuccess;
     }
     int dev = 0;
@@ -332,21 +345,27 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
             if (cfg < 0) cfg = cdiv(q.M, 256) * cdiv(q.N, 256) >= kNumCU ? 0 : 2;
         }
     }
-    if (splits <= 0) {
-        splits = pick_splits(kCfg16[cfg], q);
+    auto default_splits = [&](int id) {
+        int sp = pick_splits(kCfg16[id], q);
         // e4m3 above the decode sizes: the reduction launch costs more than split-K
         // returns unless the tiles fill under an eighth of the CUs (measured: 64 x 4096
         // x 4096 NT with 32 x 128 tiles, 10.4 us unsplit against 12.7 us with 2 splits)
-        if (e4m3 && !forced && q.M > 32 && splits > 1 &&
-            cdiv(q.M, kCfg16[cfg].BM) * cdiv(q.N, kCfg16[cfg].BN) * 8 > kNumCU)
-            splits = 1;
-    }
+        if (e4m3 && !forced && q.M > 32 && sp > 1 &&
+            cdiv(q.M, kCfg16[id].BM) * cdiv(q.N, kCfg16[id].BN) * 8 > kNumCU)
+            sp = 1;
+        return sp;
+    };
+    if (splits <= 0) splits = default_splits(cfg);
     if (!dma_ok(kCfg16[cfg], q, split_len(q.K, splits, kCfg16[cfg].BK))) {
         if (kCfg16[cfg].dma && !e4m3 && !kCfg16[cfg].e4m3) {
             cfg = kCfg16[cfg].BM >= 256 ? 0 : 2;
             if (!forced) splits = pick_splits(kCfg16[cfg], q);
         } else if (kCfg16[cfg].dma) {
-            cfg = -1;
+            // e4m3: the 128 x 128 tile, whose 128-byte rows also suit a transposed A
+            // (the 32-row tiles' rows of a transposed A are 32 bytes), else none
+            constexpr int kAlt = 15;
+            if (!forced) splits = default_splits(kAlt);
+            cfg = dma_ok(kCfg16[kAlt], q, split_len(q.K, splits, kCfg16[kAlt].BK)) ? kAlt : -1;
         }
     }
     *cfg_out = cfg;
@@ -358,6 +377,53 @@ unsigned grid_1d(int64_t total) {
     if (b > 8 * kNumCU * 4) b = 8 * kNumCU * 4;
     if (b < 1) b = 1;
     return (unsigned)b;
+}
+
+// An e4m3 operand: rows x cols bytes, row pitch ld, problems `stride` bytes apart
+// (0: one matrix shared by every problem); vec: the direct-to-LDS kernels can read
+// it as it is (16-byte aligned base, pitch and stride).
+struct Operand8 {
+    const void* ptr;
+    int64_t ld, stride, rows, cols;
+    bool vec;
+};
+
+// Copies the operands without `vec` to workspace slot 3 with 16-byte rows (pitch
+// cols rounded up to 16, zero padding), so the direct-to-LDS kernels take the
+// problem, and points ops at the copies.  *relaid stays false, with nothing
+// enqueued, when every operand is usable as it is or the copies would not fit the
+// fixed scratch of sg_gemm_noalloc.
+hipError_t relay_e4m3(Operand8 (&ops)[2], int64_t batch, hipStream_t st, bool* relaid) {
+    *relaid = false;
+    size_t off[2] = {0, 0}, total = 0;
+    for (int i = 0; i < 2; ++i) {
+        if (ops[i].vec) continue;
+        const int64_t ld = cdiv(ops[i].cols, 16) * 16;
+        off[i] = total;
+        total += round256((size_t)(ops[i].rows * ld * (ops[i].stride ? batch : 1)));
+    }
+    if (total == 0 || !workspace_fits(total)) return hipSuccess;
+    float* ws = nullptr;
+    hipError_t e = workspace(total, &ws, 3);
+    if (e != hipSuccess) return e;
+    for (int i = 0; i < 2; ++i) {
+        Operand8& o = ops[i];
+        if (o.vec) continue;
+        const int64_t ld = cdiv(o.cols, 16) * 16;
+        const int64_t nb = o.stride ? batch : 1, stride = o.stride ? o.rows * ld : 0;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(ws) + off[i];
+        hipLaunchKernelGGL(pack_rows_kernel, dim3(grid_1d(o.rows * ld / 16), 1, (unsigned)nb),
+                           dim3(256), 0, st, static_cast<const uint8_t*>(o.ptr), o.ld, o.stride,
+                           dst, ld, o.rows * ld, o.rows, o.cols);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        o.ptr = dst;
+        o.ld = ld;
+        o.stride = stride;
+        o.vec = true;
+    }
+    *relaid = true;
+    return hipSuccess;
 }
 
 void set_last(const char* what, int cfg, int splits) {
@@ -652,14 +718,30 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
     }
     p.vec_a = aligned(A, 16) && (lda % 16 == 0) && (bt.sA % 16 == 0);
     p.vec_b = aligned(B, 16) && (ldb % 16 == 0) && (bt.sB % 16 == 0);
-    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1, bt.n, lda, ldb};
+    if (!p.vec_a || !p.vec_b) {
+        Operand8 ops[2] = {{A, lda, bt.sA, ta ? K : M, ta ? M : K, (bool)p.vec_a},
+                           {B, ldb, bt.sB, tb ? N : K, tb ? K : N, (bool)p.vec_b}};
+        bool relaid = false;
+        const hipError_t r = relay_e4m3(ops, bt.n, st, &relaid);
+        if (r != hipSuccess) return r;
+        if (relaid) {
+            p.A = static_cast<const uint16_t*>(ops[0].ptr);
+            p.lda = ops[0].ld;
+            p.sA = ops[0].stride;
+            p.B = static_cast<const uint16_t*>(ops[1].ptr);
+            p.ldb = ops[1].ld;
+            p.sB = ops[1].stride;
+            p.vec_a = p.vec_b = 1;
+        }
+    }
+    Problem16 q{M, N, K, (bool)p.vec_a, (bool)p.vec_b, ta, tb, 1, bt.n, p.lda, p.ldb};
     int splits = 1;
     float* ws = nullptr;
     hipError_t e = run16<DT_E4M3>(ta, tb, ex.on ? EPI_GEMM_EX : EPI_GEMM, q, p, C,
                                   c_vec_ok(C, ldc, bt.sC, ex), "gemm8", st, &splits, &ws);
     if (e == hipErrorNotSupported) {
         std::snprintf(g_last_cfg, sizeof(g_last_cfg), "gemm8 generic splits=1");
-        for (int64_t z = 0; z < bt.n; ++z) {   // rare path (K tails, odd alignment)
+        for (int64_t z = 0; z < bt.n; ++z) {   // rare: see gemm_e4m3_generic
             hipLaunchKernelGGL(gemm_e4m3_generic, dim3(grid_1d(M * N)), dim3(256), 0, st,
                                (const uint8_t*)A + z * bt.sA, (const uint8_t*)B + z * bt.sB,
                                (void*)((char*)C + z * bt.sC), lda, ldb, ldc, (int)M, (int)N,
@@ -674,10 +756,12 @@ hipError_t gemm8(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alpha,
 }
 
 template <bool TA, bool TB>
-hipError_t launch_f32(const GemmF32Params& p, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB>),
-                       dim3((unsigned)(p.tiles_m * p.tiles_n), 1, (unsigned)(p.batch > 1 ? p.batch : 1)),
-                       dim3(256), 0, st, p);
+hipError_t launch_f32(const GemmF32Params& p, int wt, hipStream_t st) {
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n), 1, (unsigned)(p.batch > 1 ? p.batch : 1));
+    if (wt == 64)
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 64>), grid, dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, 32>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -701,13 +785,23 @@ hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alp
     p.K = (int)K;
     p.alpha = alpha;
     p.beta = beta;
-    p.tiles_m = (int)cdiv(M, 64);
-    p.tiles_n = (int)cdiv(N, 64);
-    std::snprintf(g_last_cfg, sizeof(g_last_cfg), "gemm_f32 64x64x16 mfma32x32x2 splits=1");
-    if (!ta && !tb) return launch_f32<false, false>(p, st);
-    if (!ta && tb) return launch_f32<false, true>(p, st);
-    if (ta && !tb) return launch_f32<true, false>(p, st);
-    return launch_f32<true, true>(p, st);
+    // 128 x 128 tiles once there are enough for the three work-groups per CU that fit
+    // at once, else 64 x 64 (four times the work-groups).  Measured on MI355X (NN,
+    // U[-1,1]): 64 x 64 ahead up to 3072^3 (96 against 86 TFLOP/s there; 2063 x 2100
+    // x 77: 18.6 against 26.2 us), 128 x 128 from 4096^3 (112 against 101, at 8192^3
+    // 120 against 102 TFLOP/s).
+    const int wt = cdiv(M, 128) * cdiv(N, 128) * bt.n >= 3 * kNumCU ? 64 : 32;
+    p.tiles_m = (int)cdiv(M, 2 * wt);
+    p.tiles_n = (int)cdiv(N, 2 * wt);
+    p.group_m = group_m();
+    p.vec_a = aligned(A, 16) && lda % 4 == 0 && bt.sA % 16 == 0;
+    p.vec_b = aligned(B, 16) && ldb % 4 == 0 && bt.sB % 16 == 0;
+    std::snprintf(g_last_cfg, sizeof(g_last_cfg), "gemm_f32 %dx%dx16 mfma32x32x2 splits=1",
+                  2 * wt, 2 * wt);
+    if (!ta && !tb) return launch_f32<false, false>(p, wt, st);
+    if (!ta && tb) return launch_f32<false, true>(p, wt, st);
+    if (ta && !tb) return launch_f32<true, false>(p, wt, st);
+    return launch_f32<true, true>(p, wt, st);
 }
 
 // ------------------------------------------------ split-weight SwiGLU (W1, W2)
@@ -1121,6 +1215,20 @@ int sg_swiglu_gemm(const void* A, const void* Wfused, void* Y, int64_t M, int64_
             d = try_decode<DT_BF16>(false, EPI_SWIGLU, A, K, Wfused, nullptr, N2, Y, N, M, N2, K,
                                     p.alpha, 0.0f, st);
         if (d != hipErrorNotSupported) return status_of(d);
+    }
+    if (dtype == SG_F8E4M3 && (!p.vec_a || !p.vec_b)) {
+        Operand8 ops[2] = {{A, K, 0, M, K, (bool)p.vec_a}, {Wfused, N2, 0, K, N2, (bool)p.vec_b}};
+        bool relaid = false;
+        const hipError_t r = relay_e4m3(ops, 1, st, &relaid);
+        if (r != hipSuccess) return status_of(r);
+        if (relaid) {
+            p.A = static_cast<const uint16_t*>(ops[0].ptr);
+            p.lda = q.lda = ops[0].ld;
+            p.B = static_cast<const uint16_t*>(ops[1].ptr);
+            p.ldb = q.ldb = ops[1].ld;
+            p.vec_a = p.vec_b = 1;
+            q.vec_a = q.vec_b = true;
+        }
     }
     int splits = 1;
     float* ws = nullptr;

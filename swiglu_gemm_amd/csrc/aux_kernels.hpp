@@ -8,10 +8,20 @@ namespace sg {
 
 // ---------------------------------------------------------------------------
 // fp32 GEMM: C = alpha*op(A)*op(B) + beta*C_old ("GEMM o Coração Matemático" §1)
-// with v_mfma_f32_32x32x2_f32 (fp32 products, fp32 accumulation).  64x64 tile,
-// BK = 16, four waves each owning one 32x32 accumulator.  Operands are staged in
-// LDS as [k][row] (row contiguous) so each lane's MFMA operand is one float.
-// Out-of-range elements are zero-filled; stores are predicated.
+// with v_mfma_f32_32x32x2_f32 (fp32 products, fp32 accumulation).
+//
+// A (2*WT) x (2*WT) tile per work-group of four waves (2 x 2), each wave a WT x WT
+// block of 32x32 accumulators; K in tiles of 16.  Both operand tiles sit in LDS
+// as [row][k] (k contiguous, rows padded to 20 floats: the eight 16-byte reads of
+// one LDS cycle land on distinct banks), so a lane's operands for four MFMAs are
+// one 16-byte read: in a group of 8 k, lane half h supplies k = 4h + s to MFMA
+// step s of A and B alike, which sums every k once.  An operand stored k-
+// contiguous is copied as 16-byte pieces of a row; one stored row-contiguous is
+// read as 16-byte pieces along the row and written to LDS one float per row.
+// Two LDS stages: the next K tile is loaded into registers while the current one
+// feeds the MFMAs, one barrier per K tile.  Out-of-range elements load as zero
+// and never dereference; vector loads only where the operand's base and ld allow
+// them and the whole piece is in range.
 // ---------------------------------------------------------------------------
 struct GemmF32Params {
     const float* A;
@@ -21,12 +31,26 @@ struct GemmF32Params {
     int M, N, K;
     float alpha, beta;
     int tiles_m, tiles_n;
+    int group_m;         // tile-rows walked together
+    int vec_a, vec_b;    // 16-byte aligned base, ld % 4 == 0 and batch stride % 16 == 0
     int batch;           // strided batch over gridDim.z
     int64_t sA, sB, sC;  // byte distance between consecutive problems
     EpiEx ex;            // bias / activation / e4m3 output (ex.on == 0: none)
 };
 
-template <bool TA, bool TB>
+// Four consecutive floats src[0..3] of which the first `left` exist (zeros past
+// them); `vec`: the 16-byte load is allowed when all four exist.
+__device__ __forceinline__ f32x4 load4_f32(const float* src, int left, bool vec) {
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (left <= 0) return v;
+    if (vec && left >= 4) return *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        if (c < left) v[c] = src[c];
+    return v;
+}
+
+template <bool TA, bool TB, int WT>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmF32Params p_) {
     GemmF32Params p = p_;
     {
@@ -35,57 +59,120 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const GemmF32Params p_) {
         p.B = reinterpret_cast<const float*>(reinterpret_cast<const char*>(p_.B) + z * p_.sB);
         p.C = reinterpret_cast<float*>(reinterpret_cast<char*>(p_.C) + z * p_.sC);
     }
-    constexpr int T = 64, BK = 16, PAD = 4;
-    __shared__ float As[BK][T + PAD];
-    __shared__ float Bs[BK][T + PAD];
+    constexpr int T = 2 * WT, BK = 16, LDR = BK + 4;
+    constexpr int NL = T / 64;    // 16-byte pieces per thread and operand per K tile
+    constexpr int FM = WT / 32;   // 32x32 accumulators per wave along each dimension
+    __shared__ __attribute__((aligned(16))) float As[2][T][LDR];
+    __shared__ __attribute__((aligned(16))) float Bs[2][T][LDR];
+
     const int nblk = p.tiles_m * p.tiles_n;
     const int lid = xcd_remap(blockIdx.x, nblk);
-    const int tmi = lid % p.tiles_m, tni = lid / p.tiles_m;
+    int tmi, tni;
+    tile_coords(lid, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
     const int m0 = tmi * T, n0 = tni * T;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave & 1, wn = wave >> 1;
-    f32x16 acc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    const bool va = p.vec_a != 0, vb = p.vec_b != 0;
 
-    for (int k0 = 0; k0 < p.K; k0 += BK) {
+    // piece e of a tile: k-contiguous operand: row e/4, k 4*(e%4); row-contiguous
+    // operand: k e%16, rows 4*(e/16) .. +3
+    auto load = [&](int k0, f32x4 (&ra)[NL], f32x4 (&rb)[NL]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NL; ++i) {
             const int e = tid + i * 256;
-            int m, k;
-            if (TA) { k = e >> 6; m = e & 63; }   // A stored K x M: m contiguous
-            else    { m = e >> 4; k = e & 15; }   // A stored M x K: k contiguous
-            float v = 0.0f;
-            if (m0 + m < p.M && k0 + k < p.K)
-                v = TA ? p.A[(int64_t)(k0 + k) * p.lda + (m0 + m)]
-                       : p.A[(int64_t)(m0 + m) * p.lda + (k0 + k)];
-            As[k][m] = v;
-            int n;
-            if (TB) { n = e >> 4; k = e & 15; }   // B stored N x K: k contiguous
-            else    { k = e >> 6; n = e & 63; }   // B stored K x N: n contiguous
-            float w = 0.0f;
-            if (n0 + n < p.N && k0 + k < p.K)
-                w = TB ? p.B[(int64_t)(n0 + n) * p.ldb + (k0 + k)]
-                       : p.B[(int64_t)(k0 + k) * p.ldb + (n0 + n)];
-            Bs[k][n] = w;
+            if (!TA) {
+                const int r = e >> 2, k = k0 + ((e & 3) << 2);
+                ra[i] = m0 + r < p.M ? load4_f32(p.A + (int64_t)(m0 + r) * p.lda + k, p.K - k, va)
+                                     : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            } else {
+                const int k = k0 + (e & 15), r = m0 + ((e >> 4) << 2);
+                ra[i] = k < p.K ? load4_f32(p.A + (int64_t)k * p.lda + r, p.M - r, va)
+                                : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            if (TB) {
+                const int r = e >> 2, k = k0 + ((e & 3) << 2);
+                rb[i] = n0 + r < p.N ? load4_f32(p.B + (int64_t)(n0 + r) * p.ldb + k, p.K - k, vb)
+                                     : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            } else {
+                const int k = k0 + (e & 15), r = n0 + ((e >> 4) << 2);
+                rb[i] = k < p.K ? load4_f32(p.B + (int64_t)k * p.ldb + r, p.N - r, vb)
+                                : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
         }
-        __syncthreads();
+    };
+    auto store = [&](int st, const f32x4 (&ra)[NL], const f32x4 (&rb)[NL]) {
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 2) {
-            const float a = As[kk + (lane >> 5)][wm * 32 + (lane & 31)];
-            const float b = Bs[kk + (lane >> 5)][wn * 32 + (lane & 31)];
-            // first operand: rows of A (i = lane%32), second: columns of B
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+        for (int i = 0; i < NL; ++i) {
+            const int e = tid + i * 256;
+            if (!TA) {
+                *reinterpret_cast<f32x4*>(&As[st][e >> 2][(e & 3) << 2]) = ra[i];
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) As[st][((e >> 4) << 2) + c][e & 15] = ra[i][c];
+            }
+            if (TB) {
+                *reinterpret_cast<f32x4*>(&Bs[st][e >> 2][(e & 3) << 2]) = rb[i];
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) Bs[st][((e >> 4) << 2) + c][e & 15] = rb[i][c];
+            }
         }
+    };
+
+    f32x16 acc[FM][FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int nkt = (p.K + BK - 1) / BK;
+    f32x4 ra[NL], rb[NL];
+    if (nkt > 0) {
+        load(0, ra, rb);
+        store(0, ra, rb);
+    }
+    __syncthreads();
+    const int h = lane >> 5, li = lane & 31;
+    for (int t = 0; t < nkt; ++t) {
+        const int st = t & 1;
+        if (t + 1 < nkt) load((t + 1) * BK, ra, rb);
+#pragma unroll
+        for (int g = 0; g < BK / 8; ++g) {
+            f32x4 a[FM], b[FM];
+#pragma unroll
+            for (int f = 0; f < FM; ++f) {
+                a[f] = *reinterpret_cast<const f32x4*>(&As[st][wm * WT + f * 32 + li][8 * g + 4 * h]);
+                b[f] = *reinterpret_cast<const f32x4*>(&Bs[st][wn * WT + f * 32 + li][8 * g + 4 * h]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s],
+                                                                          acc[i][j], 0, 0, 0);
+        }
+        // the other stage was last read before the previous barrier
+        if (t + 1 < nkt) store(st ^ 1, ra, rb);
         __syncthreads();
     }
-    // D[i][j]: j = lane%32, i = 8*(r/4) + 4*(lane/32) + r%4
-    const int n = n0 + wn * 32 + (lane & 31);
-    if (n >= p.N) return;
+    // D[i][j] of one accumulator: j = lane % 32, i = 8*(r/4) + 4*(lane/32) + r%4
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < p.M) store_elem<DT_F32>(p.C, (int64_t)m * p.ldc + n, n, p.alpha * acc[r], p.beta, p.ex);
+    for (int j = 0; j < FM; ++j) {
+        const int n = n0 + wn * WT + j * 32 + li;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * WT + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < p.M)
+                    store_elem<DT_F32>(p.C, (int64_t)m * p.ldc + n, n, p.alpha * acc[i][j][r],
+                                       p.beta, p.ex);
+            }
     }
 }
 
@@ -208,9 +295,34 @@ __global__ void __launch_bounds__(256) silu_mul_kernel(const uint16_t* G, const 
 namespace sg {
 
 // ---------------------------------------------------------------------------
-// Generic e4m3 kernels for shapes the direct-to-LDS kernel does not take (a K
-// tail, odd sizes or alignment): one thread per output, exact e4m3 -> fp32
-// decode, fp32 accumulation in k order, bf16 output.
+// Re-lays `rows` rows of `cols` bytes (src, row pitch lds, problem z at src + z*sS)
+// as rows of ldd bytes (ldd % 16 == 0, dst 16-byte aligned, problem z at dst +
+// z*sD), bytes [cols, ldd) of each row zero.  One 16-byte piece of dst per thread
+// and step; src is read byte by byte (any alignment).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) pack_rows_kernel(const uint8_t* src, int64_t lds,
+                                                        int64_t sS, uint8_t* dst, int64_t ldd,
+                                                        int64_t sD, int64_t rows, int64_t cols) {
+    src += (int64_t)blockIdx.z * sS;
+    dst += (int64_t)blockIdx.z * sD;
+    const int64_t per_row = ldd >> 4, total = rows * per_row;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * 256) {
+        const int64_t r = q / per_row, c0 = (q - r * per_row) << 4;
+        const uint8_t* s = src + r * lds + c0;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+            if (c0 + b < cols) w[b >> 2] |= (uint32_t)s[b] << (8 * (b & 3));
+        *reinterpret_cast<u32x4*>(dst + r * ldd + c0) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Generic e4m3 kernels for problems the direct-to-LDS kernel cannot take even
+// with re-laid operands (a tile's rows spanning 2^31 bytes or more, or no room in
+// the fixed scratch of sg_gemm_noalloc for the re-laid copies): one thread per
+// output, exact e4m3 -> fp32 decode, fp32 accumulation in k order, bf16 output.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float e4m3_to_f32(uint8_t q) {
     const int e = (q >> 3) & 15, f = q & 7;

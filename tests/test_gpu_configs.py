@@ -14,7 +14,7 @@ from helpers import assert_close, bits_equal, from_dev, split_count, to_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-CFGS16 = list(range(14)) + [24] + list(range(27, 33)) + [43, 44, 46, 48]   # every 16-bit id
+CFGS16 = list(range(14)) + [24, 27, 28, 30, 31, 32, 43, 44, 46, 48]   # every 16-bit id
 WIDE = [24]                        # 320-column tiles (640-byte LDS rows)
 TRANS = ["NN", "NT", "TN", "TT"]
 

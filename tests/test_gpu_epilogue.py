@@ -1,8 +1,8 @@
 """GPU parity of the fused GEMM epilogue (sg_gemm_ex: bias, activation, e4m3
 output quantisation) against the fp64 oracle, through the C ABI, on every kernel
 path that stores C: the direct-to-LDS tile kernels, the register-staged kernel
-(K tail), split-K with its reduction, the decode path, the generic e4m3 kernel,
-the fp32 kernel and the K == 0 quick return.  e4m3 outputs: bit-exact codes where
+(K tail), split-K with its reduction, the decode path, e4m3 operands re-laid
+with 16-byte rows, the fp32 kernel and the K == 0 quick return.  e4m3 outputs: bit-exact codes where
 the value before quantisation is exact (ties, subnormals, saturation), otherwise
 the code must be the rounding of a value within a tight bound of the oracle's.
 Also the two plain-GEMM uses of the pages' epilogue argument: attention scores
@@ -119,10 +119,13 @@ def check_ex(dtype, ta, tb, M, N, K, seed, act, bdt, beta=0.3, out8=False, ld_mo
 def test_epilogue_tile_kernels(dtype, act):
     """Multi-tile ragged shapes on the large-tile kernels (direct-to-LDS for the
     aligned 16-bit / e4m3 rows), bias in fp32 and in bf16; C rows of 522 elements
-    (ldc not a multiple of 8) take the quad-store form of the epilogue."""
+    (ldc not a multiple of 8) take the quad-store form of the epilogue; fp32 also on
+    its 128 x 128 tiles."""
     check_ex(dtype, "N", "N", 300, 520, 256, 400, act, "f32")
     check_ex(dtype, "N", "T", 257, 384, 512, 401, act, "bf16")
     check_ex(dtype, "N", "T", 300, 522, 256, 402, act, "f32", ld_mode="tight")
+    if dtype == "f32":
+        check_ex(dtype, "T", "N", 3600, 3500, 40, 403, act, "bf16", expect="128x128")
 
 
 @pytest.mark.parametrize("act", ACTS)
@@ -134,15 +137,16 @@ def test_epilogue_e4m3_output(dtype, act):
 @pytest.mark.parametrize("act", ["gelu", "silu"])
 def test_epilogue_other_paths(act):
     """Register-staged kernel (a leading dimension that is not a 16-byte multiple),
-    split-K + reduction, decode path, generic e4m3 kernel (K tail, odd rows), each
-    with bias and activation, 16-bit and e4m3 outputs."""
+    split-K + reduction, decode path, e4m3 operands with odd rows (re-laid with
+    16-byte rows for the tile kernels), each with bias and activation, 16-bit and
+    e4m3 outputs."""
     check_ex("bf16", "T", "N", 201, 300, 250, 420, act, "f32", expect=" reg ", ld_mode="tight")
     d = check_ex("f16", "N", "N", 64, 384, 8192, 421, act, "f16")
     assert split_count(d) > 1, d
     check_ex("bf16", "N", "T", 4, 1024, 2048, 422, act, "bf16", expect="decode")
     check_ex("bf16", "N", "T", 4, 1024, 2048, 423, act, "bf16", out8=True, expect="decode")
-    check_ex("e4m3", "N", "N", 37, 80, 70, 424, act, "f32", expect="generic")
-    check_ex("e4m3", "N", "N", 37, 80, 70, 425, act, "f32", out8=True, expect="generic")
+    check_ex("e4m3", "N", "N", 37, 80, 70, 424, act, "f32", expect="gemm8 cfg=")
+    check_ex("e4m3", "N", "N", 37, 80, 70, 425, act, "f32", out8=True, expect="gemm8 cfg=")
     d = check_ex("f16", "N", "N", 64, 384, 8192, 426, act, "bf16", out8=True)
     assert split_count(d) > 1, d
 

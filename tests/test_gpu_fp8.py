@@ -102,32 +102,64 @@ def test_gemm_e4m3_configs_and_transposes(cfg, tr):
         desc = sg.last_config()
     finally:
         os.environ.pop("SG_FORCE_CONFIG", None)
-    if cfg is not None and not (ta == "T" and cfg in (16, 17)):
-        assert "cfg=%d " % cfg in desc, desc
+    if cfg is not None:
+        # a transposed A has 32-byte rows in a 32-row tile: the 128 x 128 tile runs it
+        assert "cfg=%d " % (15 if ta == "T" and cfg in (16, 17) else cfg) in desc, desc
     ref = oracle.gemm(ta, tb, M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], 0.25, p["C"],
                       p["ldc"], "e4m3", c_dtype="bf16")
     assert_close(oracle.decode(from_dev(C), "bf16"), ref, "e4m3", K, desc)
 
 
-@pytest.mark.parametrize("shape", [(37, 50, 70), (1, 1, 1), (5, 300, 130)])
-def test_generic_e4m3_odd_shapes(shape):
-    """K tails and odd sizes take the generic e4m3 kernels."""
+@pytest.mark.parametrize("shape", [(37, 50, 70), (1, 1, 1), (5, 300, 130), (300, 1001, 1000)])
+def test_e4m3_odd_rows_relaid(shape):
+    """Rows that are not 16-byte multiples (odd K or N, tight leading dimensions):
+    the operands are copied with 16-byte rows and the tile kernels run, GEMM and
+    SwiGLU (whose W_fused rows of 2N bytes are then not 16-byte multiples either)."""
     import swiglu_gemm_amd as sg
     M, N, K = shape
     p = inputs.gemm_problem(91, "N", "N", M, N, K, "e4m3", "normal", c_dtype="bf16")
     A, B, C = to_dev(p["A"], "e4m3"), to_dev(p["B"], "e4m3"), to_dev(p["C"], "bf16")
-    sg.gemm(A, B, C, alpha=1.0, beta=0.0, M=M, N=N, K=K, lda=p["lda"], ldb=p["ldb"],
+    alpha = p["scale_a"] * p["scale_b"]          # the per-tensor scales: O(1) outputs
+    print("gemm e4m3 relaid M=%d N=%d K=%d" % (M, N, K), flush=True)
+    sg.gemm(A, B, C, alpha=alpha, beta=0.0, M=M, N=N, K=K, lda=p["lda"], ldb=p["ldb"],
             ldc=p["ldc"], dtype=3)
     torch.cuda.synchronize()
     desc = sg.last_config()
-    ref = oracle.gemm("N", "N", M, N, K, 1.0, p["A"], p["lda"], p["B"], p["ldb"], 0.0, p["C"],
+    assert "generic" not in desc, desc
+    ref = oracle.gemm("N", "N", M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], 0.0, p["C"],
                       p["ldc"], "e4m3", c_dtype="bf16")
     assert_close(oracle.decode(from_dev(C), "bf16"), ref, "e4m3", K, desc)
     pb = inputs.swiglu_problem(92, M, N, K, "e4m3")
     Wf = oracle.interleave(pb["W1"], pb["W2"])
     y, desc = run_swiglu8(pb, Wf, M, N, K)
+    assert "generic" not in desc, desc
     ref = oracle.swiglu(M, N, K, pb["A"], Wf, "e4m3", pb["scale_a"], pb["scale_w"])
     assert_close(oracle.decode(y, "bf16"), ref, "e4m3", K, desc)
+
+
+@pytest.mark.parametrize("tr", ["NN", "NT", "TN", "TT"])
+def test_e4m3_padded_ld_relaid(tr):
+    """Leading dimensions padded to 64k + 8 bytes (8 bytes off the 16-byte grid),
+    several tiles and a ragged edge: the re-laid copies feed the tile kernels;
+    every output against the oracle and the ld padding of C untouched."""
+    import swiglu_gemm_amd as sg
+    ta, tb = tr
+    M, N, K = 700, 900, 1000
+    p = inputs.gemm_problem(93, ta, tb, M, N, K, "e4m3", "normal", ld_mode="padded",
+                            c_dtype="bf16")
+    A, B, C = to_dev(p["A"], "e4m3"), to_dev(p["B"], "e4m3"), to_dev(p["C"], "bf16")
+    alpha = 0.7 * p["scale_a"] * p["scale_b"]
+    print("gemm e4m3 padded ld %s M=%d N=%d K=%d" % (tr, M, N, K), flush=True)
+    sg.gemm(A, B, C, alpha=alpha, beta=0.3, transA=ta, transB=tb, M=M, N=N, K=K, lda=p["lda"],
+            ldb=p["ldb"], ldc=p["ldc"], dtype=3)
+    torch.cuda.synchronize()
+    desc = sg.last_config()
+    assert "gemm8 cfg=" in desc, desc
+    got = from_dev(C)
+    ref = oracle.gemm(ta, tb, M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], 0.3, p["C"],
+                      p["ldc"], "e4m3", c_dtype="bf16")
+    assert_close(oracle.decode(got, "bf16")[:, :N], ref[:, :N], "e4m3", K, desc)
+    assert bits_equal(got[:, N:], p["C"][:, N:]), "ld padding of C was written"
 
 
 @pytest.mark.parametrize("M", [1, 16, 256])

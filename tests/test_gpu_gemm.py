@@ -96,6 +96,21 @@ def test_f32_transposes_64x48x32(tr):
     check_full(p, tr[0], tr[1], 64, 48, 32, 1.5, 0.5, "f32", "f32 64x48x32")
 
 
+@pytest.mark.parametrize("tr", TRANS)
+@pytest.mark.parametrize("shape,ld_mode,tile", [((3600, 3500, 129), "padded", 128),
+                                                ((3599, 3601, 77), "tight", 128),
+                                                ((1001, 1003, 517), "tight", 64)])
+def test_f32_multi_tile(tr, shape, ld_mode, tile):
+    """fp32 past one tile: 128 x 128 tiles (more than one round of them) and 64 x 64
+    tiles, ragged edges and K tails, 16-byte loads (padded leading dimensions) and
+    element loads (odd leading dimensions); every output against the oracle."""
+    import swiglu_gemm_amd as sg
+    M, N, K = shape
+    p = inputs.gemm_problem(3, tr[0], tr[1], M, N, K, "f32", "uniform", ld_mode=ld_mode)
+    check_full(p, tr[0], tr[1], M, N, K, 1.5, 0.5, "f32", "f32 %dx%dx%d" % shape)
+    assert "gemm_f32 %dx%dx16" % (tile, tile) in sg.last_config(), sg.last_config()
+
+
 # --------------------------------------------------------------------------
 # fp16
 # --------------------------------------------------------------------------

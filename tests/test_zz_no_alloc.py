@@ -1,8 +1,9 @@
 """sg_gemm_noalloc through the C ABI: the entry point for callers that cannot
 allocate device memory gives the same bits as sg_gemm on problems whose kernels
-use scratch memory (split-K partial sums; the decode path's partial sums), on two
-calls in a row with the second one smaller, and refuses a problem that needs more
-than its fixed scratch before enqueuing anything."""
+use scratch memory (split-K partial sums; the decode path's partial sums; e4m3
+operands re-laid with 16-byte rows), on two calls in a row with the second one
+smaller, and refuses a problem that needs more than its fixed scratch before
+enqueuing anything."""
 import ctypes
 import os
 
@@ -31,7 +32,7 @@ def L():
 
 def call(L, fn, p, ta, tb, M, N, K, alpha, beta, dtype, C):
     import swiglu_gemm_amd as sg
-    code = {"f16": 1, "bf16": 2}[dtype]
+    code = {"f16": 1, "bf16": 2, "e4m3": 3}[dtype]
     A, B = to_dev(p["A"], dtype), to_dev(p["B"], dtype)
     st = getattr(L, fn)(ta.encode(), tb.encode(), M, N, K, alpha, ctypes.c_void_p(A.data_ptr()),
                         p["lda"], ctypes.c_void_p(B.data_ptr()), p["ldb"], beta,
@@ -97,6 +98,48 @@ def test_too_large_is_refused_before_any_launch(L):
     C2 = to_dev(p["C"], "bf16")
     st3, desc3 = call(L, "sg_gemm", p, "N", "N", M, N, K, 1.0, 0.5, "bf16", C2)
     assert st3 == 0 and desc3 == desc and bits_equal(from_dev(C), from_dev(C2)), desc
+
+
+def e4m3_both(L, M, N, K, seed):
+    """One e4m3 problem with tight leading dimensions (rows off the 16-byte grid)
+    through sg_gemm_noalloc and sg_gemm; each output within tolerance of the oracle.
+    Returns both descriptions and outputs."""
+    p = inputs.gemm_problem(seed, "N", "N", M, N, K, "e4m3", "normal", ld_mode="tight",
+                            beta_zero=True, c_dtype="bf16")
+    alpha = p["scale_a"] * p["scale_b"]
+    ref = oracle.gemm("N", "N", M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], 0.0, p["C"],
+                      p["ldc"], "e4m3", c_dtype="bf16")
+    out = []
+    for fn in ("sg_gemm_noalloc", "sg_gemm"):
+        print("%s e4m3 M=%d N=%d K=%d" % (fn, M, N, K), flush=True)
+        C = to_dev(p["C"], "bf16")
+        st, desc = call(L, fn, p, "N", "N", M, N, K, alpha, 0.0, "e4m3", C)
+        assert st == 0, (fn, st, desc)
+        c = from_dev(C)
+        assert_close(oracle.decode(c, "bf16"), ref, "e4m3", K, "%s %s" % (fn, desc))
+        out.append((desc, c))
+    return out
+
+
+def test_e4m3_relaid_operands_twice_second_smaller(L):
+    """e4m3 rows off the 16-byte grid are re-laid in the fixed scratch next to the
+    split-K partial sums (two pieces of it in one call): same bits as sg_gemm."""
+    (d1, c1), (d2, c2) = e4m3_both(L, 40, 300, 4100, 705)
+    assert d1 == d2 and "gemm8 cfg=" in d1 and split_count(d1) > 1, (d1, d2)
+    assert bits_equal(c1, c2), d1
+    (d1, c1), (d2, c2) = e4m3_both(L, 37, 80, 70, 706)
+    assert d1 == d2 and "gemm8 cfg=" in d1, (d1, d2)
+    assert bits_equal(c1, c2), d1
+
+
+def test_e4m3_relay_beyond_scratch_takes_generic_kernel(L):
+    """A 4100 x 8200 e4m3 A with rows off the 16-byte grid needs a 33.7 MB copy,
+    more than the fixed scratch: sg_gemm_noalloc runs the generic kernel instead
+    (no failure), sg_gemm the tile kernels; both within tolerance of the oracle."""
+    assert 4100 * 8208 > SCRATCH_BYTES
+    (d1, _), (d2, _) = e4m3_both(L, 4100, 8, 8200, 707)
+    assert "generic" in d1, d1
+    assert "gemm8 cfg=" in d2, d2
 
 
 def test_argument_checks_match_sg_gemm(L):
