@@ -51,7 +51,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "TFLOPS & % of MFMA peak: fp16 8192³ GEMM; fused SwiGLU-GEMM at M=2048"
-PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0}   # MI355X dense MFMA TFLOP/s
+PEAK = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}   # MI355X dense MFMA TFLOP/s
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm16_f16_nn_8192.json")
 COPY_BYTES = 512 * 1024 * 1024          # calibration copy: reads and writes this many bytes
@@ -150,6 +150,8 @@ def to_dev(bits, dtype, torch):
     t = torch.from_numpy(np.ascontiguousarray(bits))
     if dtype == "e4m3":
         return t.view(torch.float8_e4m3fn).to("cuda:0")
+    if dtype == "f32":
+        return t.view(torch.float32).to("cuda:0")
     t = t.view(torch.int16).view(torch.float16 if dtype == "f16" else torch.bfloat16)
     return t.to("cuda:0")
 
@@ -358,6 +360,26 @@ def bench_gemm_bf16_8192(torch, sg, steps, warmup):
     tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 5), "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK["bf16"], 4),
             "kernel_config": sg.last_config()}
+
+
+def bench_gemm_f32(torch, sg, inputs, steps, warmup):
+    """fp32 GEMM: the 256^3 parity workload (alpha 1.5, beta 0.5, U[-1,1]; a latency
+    figure) and 4096^3 NN (alpha 1, beta 0) against the fp32 MFMA peak."""
+    out = []
+    for (M, alpha, beta) in ((256, 1.5, 0.5), (4096, 1.0, 0.0)):
+        p = inputs.gemm_problem(1, "N", "N", M, M, M, "f32", "uniform")
+        A, B, C = (to_dev(p["A"], "f32", torch), to_dev(p["B"], "f32", torch),
+                   to_dev(p["C"], "f32", torch))
+
+        def step(i):
+            sg.gemm(A, B, C, alpha=alpha, beta=beta, M=M, N=M, K=M, lda=p["lda"], ldb=p["ldb"],
+                    ldc=p["ldc"], dtype=0)
+        ms = time_steps(step, steps, warmup, torch)
+        tf = 2.0 * M ** 3 / (ms * 1e-3) / 1e12
+        out.append({"M": M, "N": M, "K": M, "alpha": alpha, "beta": beta, "us": round(ms * 1e3, 2),
+                    "tflops": round(tf, 2), "frac_of_fp32_mfma_peak": round(tf / PEAK["f32"], 4),
+                    "kernel_config": sg.last_config()})
+    return out
 
 
 def bench_gemm_ragged(torch, sg, inputs, steps, warmup):
@@ -1198,6 +1220,9 @@ def main():
         torch.cuda.empty_cache()
         print("bench: fused GEMM epilogue", file=sys.stderr, flush=True)
         out["gemm_epilogue"] = bench_epilogue(torch, sg, max(10, args.steps // 2), args.warmup)
+        torch.cuda.empty_cache()
+        print("bench: fp32 GEMM", file=sys.stderr, flush=True)
+        out["gemm_f32"] = bench_gemm_f32(torch, sg, inputs, 20, 3)
         torch.cuda.empty_cache()
     sizes = [("bf16", 2048, 4864, 896)]
     if not args.quick:

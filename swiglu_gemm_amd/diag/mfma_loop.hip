@@ -105,8 +105,10 @@ __global__ void __launch_bounds__(256) stream_read(const u32x4* src, int64_t n16
 // Per-CU L2 -> CU throughput on a region small enough to stay in L2: each
 // work-group (256 threads, one per CU) reads `region` bytes `iters` times.
 // KIND 0: global_load_dwordx4 into registers (DEPTH loads in flight per thread,
-// XOR-folded); KIND 1: global_load_lds_dwordx4 into an LDS ring (DEPTH KiB-blocks of
-// each wave in flight, the ring 64 KiB).
+// XOR-folded); KIND 1: global_load_lds_dwordx4 into an LDS ring (bursts of DEPTH
+// KiB-blocks per wave, the ring 64 KiB), 64-bit lane addresses; KIND 2: the same with
+// the compiler builtin; KIND 3: buffer_load_dwordx4 ... lds from a buffer resource
+// (compiler builtin); KIND 4: as 1 with a scalar base and 32-bit lane offsets.
 template <int KIND, int DEPTH>
 __global__ void __launch_bounds__(1024) l2_stream(const char* src, int64_t region, int iters,
                                                   uint32_t* out) {
@@ -130,16 +132,37 @@ __global__ void __launch_bounds__(1024) l2_stream(const char* src, int64_t regio
         out[(int64_t)blockIdx.x * nthr + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
     } else {
         __shared__ __attribute__((aligned(1024))) char ring[65536];
-        // wave w's block for pass p: ring[((p % 4) * 16 + w) * 1024], 64 lanes x 16 B
-        int64_t issued = 0;
+        // bursts of DEPTH loads per wave (unrolled, as a GEMM issues a K tile), then a
+        // wait until the previous burst has landed; wave w's block for load d of a
+        // burst: ring[((d % 4) * 16 + w) * 1024], 64 lanes x 16 B
+        const uint32_t voff = threadIdx.x * 16;
         for (int it = 0; it < iters; ++it) {
-            for (int64_t p = 0; p < passes; ++p, ++issued) {
-                const uint32_t lds = (uint32_t)(uintptr_t)(
-                    (__attribute__((address_space(3))) char*)(ring + ((issued % 4) * 16 + wave) * 1024));
-                const char* g = src + p * per_pass + threadIdx.x * 16;
-                asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                             :: "s"(lds), "v"(g) : "memory", "m0");
-                if (issued >= DEPTH) __builtin_amdgcn_s_waitcnt((DEPTH & 15) | (7 << 4) | (15 << 8) | ((DEPTH >> 4) << 14));
+            for (int64_t p = 0; p + DEPTH <= passes; p += DEPTH) {
+#pragma unroll
+                for (int d = 0; d < DEPTH; ++d) {
+                    const uint32_t lds = (uint32_t)(uintptr_t)(
+                        (__attribute__((address_space(3))) char*)(ring + ((d % 4) * 16 + wave) * 1024));
+                    const char* base = src + (p + d) * per_pass;
+                    if constexpr (KIND == 1) {
+                        const char* g = base + voff;
+                        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                                     :: "s"(lds), "v"(g) : "memory", "m0");
+                    } else if constexpr (KIND == 4) {
+                        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                                     :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+                    } else if constexpr (KIND == 2) {
+                        __builtin_amdgcn_global_load_lds(
+                            (const void*)(base + voff),
+                            (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, 0, 0);
+                    } else {
+                        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                            (void*)base, (short)0, (int)per_pass, 0x00020000);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff,
+                            0, 0, 0);
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt((DEPTH & 15) | (7 << 4) | (15 << 8) | ((DEPTH >> 4) << 14));
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -151,7 +174,7 @@ __global__ void __launch_bounds__(1024) l2_stream(const char* src, int64_t regio
 
 }  // namespace
 
-// Per-CU L2 -> CU throughput probe (see l2_stream): kind 0 registers, kind 1 LDS DMA;
+// Per-CU L2 -> CU throughput probe (see l2_stream): kind 0 registers, kinds 1-3 LDS DMA;
 // depth in {4, 8, 16}; waves 1..16 per work-group; region (a multiple of waves*1024
 // bytes) read iters times by each of `blocks` work-groups; out: blocks*64*waves words.
 extern "C" int sg_diag_l2_stream(int kind, int depth, const void* src, int64_t region, int iters,
@@ -169,6 +192,15 @@ extern "C" int sg_diag_l2_stream(int kind, int depth, const void* src, int64_t r
     else if (kind == 1 && depth == 4) L2S(1, 4);
     else if (kind == 1 && depth == 8) L2S(1, 8);
     else if (kind == 1 && depth == 16) L2S(1, 16);
+    else if (kind == 2 && depth == 4) L2S(2, 4);
+    else if (kind == 2 && depth == 8) L2S(2, 8);
+    else if (kind == 2 && depth == 16) L2S(2, 16);
+    else if (kind == 3 && depth == 4) L2S(3, 4);
+    else if (kind == 3 && depth == 8) L2S(3, 8);
+    else if (kind == 3 && depth == 16) L2S(3, 16);
+    else if (kind == 4 && depth == 4) L2S(4, 4);
+    else if (kind == 4 && depth == 8) L2S(4, 8);
+    else if (kind == 4 && depth == 16) L2S(4, 16);
     else return (int)hipErrorInvalidValue;
 #undef L2S
     return (int)hipGetLastError();
