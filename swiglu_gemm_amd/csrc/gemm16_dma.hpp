@@ -132,16 +132,17 @@ struct DmaStream {
     // The LDS-DMA reads M0 as its LDS address; a scalar write of M0 needs one wait
     // state before that read on this GPU family (the s_nop the compiler's hazard
     // recognizer would insert, which it cannot do inside an asm statement).
-    __device__ __forceinline__ void issue(char* stage, int t, int wave) const {
+    __device__ __forceinline__ void issue_one(char* stage, int t, int wave, int i) const {
         const char* bt = base + t * step;
+        const int b = wave + i * NWAVES;
+        const uint32_t lds = (uint32_t)(uintptr_t)(
+            (__attribute__((address_space(3))) char*)(stage + b * 1024));
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(lds), "v"(off[i]), "s"(bt) : "memory", "m0");
+    }
+    __device__ __forceinline__ void issue(char* stage, int t, int wave) const {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int b = wave + i * NWAVES;
-            const uint32_t lds = (uint32_t)(uintptr_t)(
-                (__attribute__((address_space(3))) char*)(stage + b * 1024));
-            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                         :: "s"(lds), "v"(off[i]), "s"(bt) : "memory", "m0");
-        }
+        for (int i = 0; i < NI; ++i) issue_one(stage, t, wave, i);
     }
     // A trailing partial K tile (the stream initialised at its first k), of which
     // only the first `kvalid` k belong to the problem: loaded through registers into
@@ -351,16 +352,60 @@ __device__ __forceinline__ void dma_mainloop(
         constexpr int NMF = FM * FN;
         constexpr int RD_KC = ESZ == 2 ? 1 : 2, RD_RC = ESZ == 2 ? 2 : 4;
         constexpr int NRD = (KCA ? RD_KC : RD_RC) * FM + (KCB ? RD_KC : RD_RC) * FN;
+        // One wave per SIMD: no second wave keeps the matrix core fed while this one
+        // issues the next tile's DMA, so the DMA is dealt out between the MFMAs, one
+        // slot after each fragment column q of the k-steps before the barrier; with 2
+        // stages (tile t+1 must land by the end of tile t) only the first k-step's.
+        // Measured on MI355X against the whole DMA at the top of the tile (fp16 8192^3,
+        // one run): 256x256x64 2 stages 937 -> 892 us, 256x256x32 4 stages 970 -> 925
+        // us, 128x128x64 3 stages 1302 -> 1257 us; the 8-wave tiles keep the burst.
+        // Dealing it over the k-step after the barrier as well was no better.
+        constexpr bool SPREAD = NW == 4 && !W12;
+        constexpr int NIA = DmaStream<KCA, BM, BK, ESZ, NW>::NI;
+        constexpr int NSLOT = (S >= 3 ? KS - 1 : 1) * FN;
+        // DMA slot j of tile u into stage memory st
+        auto slot_dma = [&](char* st, int u, int j) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                if (i * NSLOT / NL != j) continue;
+                if (i < NIA) da.issue_one(st, u, wave, i);
+                else db.issue_one(st + TA_::BYTES, u, wave, i - NIA);
+            }
+        };
+        // fragment column q of k-step s: its MFMAs on fragments (fa, fb)[s & 1], and the
+        // reads of k-step s2 of stage st2 into the other fragment set
+        auto column = [&](int s, int q, const char* st2, int s2) __attribute__((always_inline)) {
+#pragma unroll
+            for (int tm = q % FN; tm < FM; tm += FN)
+                fa[s2 & 1][tm] = read_frag<KCA, BM, BK, ESZ>(st2, wm * TM + tm * 32, s2, lane);
+            fb[s2 & 1][q] = read_frag<KCB, BN, BK, ESZ>(st2 + TA_::BYTES, wn * TN + q * 32, s2, lane);
+#pragma unroll
+            for (int tm = 0; tm < FM; ++tm)
+                acc[q][tm] = mfma_op<DT>(fb[s & 1][q], fa[s & 1][tm], acc[q][tm]);
+        };
         for (int t = 0; t < nkt; ++t) {
             const char* cur = smem + (t % S) * STAGE;
             const bool ahead = t + S - 1 < nkt;
-            if (ahead) issue(t + S - 1);
+            if constexpr (SPREAD) {
+                char* nxt = smem + ((t + S - 1) % S) * STAGE;
 #pragma unroll
-            for (int s = 0; s + 1 < KS; ++s) {
-                read_all(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-                mfma_all(fa[s & 1], fb[s & 1]);
-                sched_interleave<NMF, NRD, 0, 0>();
-                __builtin_amdgcn_sched_barrier(0);
+                for (int s = 0; s + 1 < KS; ++s) {
+#pragma unroll
+                    for (int q = 0; q < FN; ++q) {
+                        column(s, q, cur, s + 1);
+                        if (ahead) slot_dma(nxt, t + S - 1, s * FN + q);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            } else {
+                if (ahead) issue(t + S - 1);
+#pragma unroll
+                for (int s = 0; s + 1 < KS; ++s) {
+                    read_all(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+                    mfma_all(fa[s & 1], fb[s & 1]);
+                    sched_interleave<NMF, NRD, 0, 0>();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             // tile t+1 must have landed (own DMAs), then everyone's
             if (ahead) wait_vmcnt<(S - 2) * NL>();
