@@ -63,6 +63,30 @@ def test_swiglu_e4m3_full(M, weights):
                  report=True)
 
 
+@pytest.mark.parametrize("force", [("SG_FORCE_CONFIG", "17,2"), ("SG_FORCE_CONFIG", "17,4"),
+                                   ("SG_FORCE_CONFIG", "16,2"), ("SG_FORCE_DECODE", "5")])
+@pytest.mark.parametrize("M", [1, 16])
+def test_swiglu_e4m3_skinny_split_paths(M, force, weights):
+    """The skinny rows of the e4m3 SwiGLU workload (K = 4096, N = 11008) on the paths
+    that split K -- split-K with the fp32 reduction, and the stream-K decode kernel
+    with its fix-up -- every output against the oracle."""
+    N, K = 11008, 4096
+    wb, Wf = weights
+    pb = inputs.swiglu_problem(5, M, N, K, "e4m3")
+    var, val = force
+    os.environ[var] = val
+    try:
+        y, desc = run_swiglu8(pb, Wf, M, N, K)
+    finally:
+        os.environ.pop(var, None)
+    if var == "SG_FORCE_DECODE":
+        assert "decode" in desc and "fixup" in desc, desc
+    else:
+        assert split_count(desc) == int(val.split(",")[1]), desc
+    ref = oracle.swiglu(M, N, K, pb["A"], Wf, "e4m3", pb["scale_a"], pb["scale_w"])
+    assert_close(oracle.decode(y, "bf16"), ref, "e4m3", K, desc)
+
+
 @pytest.mark.parametrize("splits", [1, 2])
 @pytest.mark.parametrize("cfg", E4M3_CFGS)
 def test_swiglu_e4m3_every_config(cfg, splits):
