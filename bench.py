@@ -38,7 +38,6 @@ from __future__ import annotations
 
 import argparse
 import csv
-import hashlib
 import json
 import os
 import sys
@@ -58,12 +57,9 @@ COPY_BYTES = 512 * 1024 * 1024          # calibration copy: reads and writes thi
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "swiglu_gemm_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
-    return h.hexdigest()[:16]
+    """The library's source hash (the one built into it, see sg_build_info)."""
+    from swiglu_gemm_amd import build
+    return build.source_hash()
 
 
 def measured_traffic():

@@ -265,6 +265,12 @@ int sg_silu_mul(const void* G, const void* U, void* Y, int64_t M, int64_t N,
 /* Text for a status code returned by any sg_* call (static storage). */
 const char* sg_status_string(int status);
 
+/* Identifies the build (static storage): "swiglu_gemm source <hash> gfx950", where
+ * <hash> is 16 hex digits of the SHA-256 over the library's kernel and ABI sources
+ * (swiglu_gemm_amd/build.py, source_hash).  The Python binding compares it with the
+ * sources beside the library and refuses a library built from other sources. */
+const char* sg_build_info(void);
+
 /*
  * Describes the kernel configuration chosen by the most recent successful
  * sg_gemm / sg_swiglu_gemm call on the calling thread (tile, split count; for a

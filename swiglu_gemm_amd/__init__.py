@@ -79,8 +79,31 @@ def lib() -> ctypes.CDLL:
         L.sg_last_config.restype = ctypes.c_int
         L.sg_release.argtypes = []
         L.sg_release.restype = None
+        L.sg_build_info.argtypes = []
+        L.sg_build_info.restype = ctypes.c_char_p
+        _check_build(L)
         _lib = L
         return L
+
+
+def _check_build(L) -> None:
+    """Refuse a library built from sources other than the ones beside it (a stale
+    build would run kernels that the sources and tests no longer describe)."""
+    from . import build
+    if not os.path.isdir(build.CSRC):
+        return                      # a library shipped without its sources
+    info = L.sg_build_info().decode()
+    want = build.source_hash()
+    if want not in info.split():
+        raise SwigluGemmError(
+            "libswiglu_gemm.so (%s) was built from other sources than %s (source %s); "
+            "rebuild with __graft_entry__.build() or python -m swiglu_gemm_amd.build"
+            % (info, build.CSRC, want))
+
+
+def build_info() -> str:
+    """The loaded library's build identity (see sg_build_info)."""
+    return lib().sg_build_info().decode()
 
 
 def declared_symbols() -> list:

@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -30,6 +31,19 @@ def hipcc() -> str:
     return "hipcc"
 
 
+def source_hash() -> str:
+    """16 hex digits of the SHA-256 over the library's sources (kernel and ABI files,
+    name and contents, in name order).  Built into the library (sg_build_info) so
+    that the binding can tell a library built from other sources."""
+    h = hashlib.sha256()
+    for d, exts in ((CSRC, (".hip", ".hpp")), (INCLUDE, (".h",))):
+        for f in sorted(os.listdir(d)):
+            if f.endswith(exts):
+                with open(os.path.join(d, f), "rb") as fh:
+                    h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
 def _flags() -> list:
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             # packed-fp32 VALU ops are kept out of the generated code on purpose
@@ -43,9 +57,12 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
 
+    ident = ["-DSG_SOURCE_HASH=\"%s\"" % source_hash()]
+
     def one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + _flags() + (ident if src == "api.hip" else []) + \
+            ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1404,6 +1404,12 @@ int sg_silu_mul(const void* G, const void* U, void* Y, int64_t M, int64_t N, int
     return status_of(hipGetLastError());
 }
 
+#ifndef SG_SOURCE_HASH
+#define SG_SOURCE_HASH "unknown"
+#endif
+
+const char* sg_build_info(void) { return "swiglu_gemm source " SG_SOURCE_HASH " gfx950"; }
+
 const char* sg_status_string(int status) {
     static const char* const kArg[] = {
         "success",         "invalid argument 1", "invalid argument 2",  "invalid argument 3",

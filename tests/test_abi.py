@@ -167,6 +167,20 @@ def test_status_strings(L):
     assert isinstance(sg.last_config(), str)
 
 
+def test_library_built_from_these_sources(L):
+    """The loaded library carries the hash of the sources beside it (a stale build is
+    refused by the binding)."""
+    info = sg.build_info()
+    assert info.startswith("swiglu_gemm source ") and info.endswith(" gfx950"), info
+    assert sgbuild.source_hash() in info.split(), (info, sgbuild.source_hash())
+
+
+def test_stale_library_is_refused(monkeypatch):
+    monkeypatch.setattr(sgbuild, "source_hash", lambda: "0123456789abcdef")
+    with pytest.raises(sg.SwigluGemmError, match="other sources"):
+        sg._check_build(sg.lib())
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(sg, "_lib", None)
     monkeypatch.setattr(sg, "LIB_PATH", str(tmp_path / "nope.so"))
