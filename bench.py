@@ -278,9 +278,10 @@ def bench_swiglu(torch, sg, inputs, dtype, M, N, K, steps, warmup, eager=True, k
     t_w12 = time_steps(w12, steps, warmup, torch)
     cfg_w12 = sg.last_config()
     # Gate then Up (Kernel-1 of the SwiGLU page) on the same split weights, its tile
-    # chosen as the library does (256-row tiles once they fill the CUs)
+    # chosen as the library does (256-row tiles once they fill the CUs, else 128-row
+    # tiles with the loads in producer waves)
     big = -(-M // 256) * -(-2 * N // 256) >= 256
-    seq_cfg = (51 if big else 52) if dtype == "e4m3" else (49 if big else 50)
+    seq_cfg = (51 if big else 54) if dtype == "e4m3" else (49 if big else 53)
     os.environ["SG_FORCE_CONFIG"] = "%d,1" % seq_cfg
     try:
         t_seq = time_steps(w12, steps, warmup, torch)

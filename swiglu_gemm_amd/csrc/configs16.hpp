@@ -7,8 +7,10 @@ struct Cfg16 {
     int e4m3;           // 1: e4m3 operands (BK in bytes), 0: fp16 / bf16 operands
     int dma;            // 0: register-staged (gemm16.hpp), 1: direct global->LDS ring
                         // (gemm16_dma.hpp), 3: the direct ring for the split-weight
-                        // SwiGLU with Gate then Up (EPI_SWIGLU_SEQ only); -1: a retired
-                        // id, kept so that the others stay stable
+                        // SwiGLU with Gate then Up (EPI_SWIGLU_SEQ only), 4: the same
+                        // with the ring driven by separate producer waves
+                        // (gemm_ws_kernel); -1: a retired id, kept so that the others
+                        // stay stable
     int BM, BN, BK, S;  // tile and LDS stages
     int WM, WN;         // waves along M and N
     const char* name;
@@ -74,6 +76,10 @@ constexpr Cfg16 kCfg16[] = {
     {0, 3, 128, 256, 64, 4, 2, 2, "seq 128x256x64 s4 2x2w"},
     {1, 3, 256, 256, 128, 3, 4, 2, "e4m3 seq 256x256x128 s3 4x2w"},
     {1, 3, 128, 256, 128, 4, 2, 2, "e4m3 seq 128x256x128 s4 2x2w"},
+    // the same with 4 producer waves beside the 2x2 consumer waves (Kernel-1's
+    // producer / consumer split)
+    {0, 4, 128, 256, 64, 4, 2, 2, "seq-ws 128x256x64 s4 2x2w+4p"},
+    {1, 4, 128, 256, 128, 4, 2, 2, "e4m3 seq-ws 128x256x128 s4 2x2w+4p"},
 };
 constexpr int kNumCfg16 = sizeof(kCfg16) / sizeof(kCfg16[0]);
 
@@ -155,11 +161,13 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
 // the split-weight SwiGLU with Gate then Up (EPI_SWIGLU_SEQ, NN only)
 #define SG_CONFIGS_SEQ(X)              \
     X(49, 1, 256, 256, 64, 3, 4, 2)    \
-    X(50, 1, 128, 256, 64, 4, 2, 2)
+    X(50, 1, 128, 256, 64, 4, 2, 2)    \
+    X(53, 4, 128, 256, 64, 4, 2, 2)
 
 #define SG_CONFIGS_E4M3_SEQ(X)         \
     X(51, 1, 256, 256, 128, 3, 4, 2)   \
-    X(52, 1, 128, 256, 128, 4, 2, 2)
+    X(52, 1, 128, 256, 128, 4, 2, 2)   \
+    X(54, 4, 128, 256, 128, 4, 2, 2)
 
 // the same for every e4m3 row (all direct-to-LDS)
 #define SG_CONFIGS_E4M3(X)             \

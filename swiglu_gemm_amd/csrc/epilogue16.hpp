@@ -580,10 +580,13 @@ __device__ __forceinline__ float swiglu_pair(float g, float u, float s) {
     return SCALED ? silu(s * g) * (s * u) : silu(g) * u;
 }
 
+// has_acc == false: a wave without accumulators (a producer wave of the wave-
+// specialised kernel) takes part in the barriers and the stores but stages nothing.
 template <int DT, int FM, int FN, int BM, int BN, int NT, bool W12, bool SCALED, bool PRE = false>
 __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
                                                     f32x16 (&acc)[FN][FM], char* smem, int m0,
-                                                    int n0, int rb, int cb, int lane) {
+                                                    int n0, int rb, int cb, int lane,
+                                                    bool has_acc = true) {
     constexpr int ROW = BN + 8;        // bytes per staged row: BN/2 outputs of 2 bytes + pad
     constexpr int CPR = BN / 16;       // 16-byte pieces (8 outputs) per row
     constexpr int WMS = BM / (32 * FM);            // wave rows of the tile
@@ -598,7 +601,8 @@ __device__ __forceinline__ void epilogue_swiglu_lds(const Gemm16Params& p,
 #pragma unroll
     for (int tm = 0; tm < FM; ++tm) {
         char* row = smem + (rb + tm * 32 + lm) * ROW;
-        if constexpr (W12) {
+        if (!has_acc) {
+        } else if constexpr (W12) {
 #pragma unroll
             for (int tn = 0; tn < FN / 2; ++tn) {
 #pragma unroll

@@ -558,6 +558,135 @@ __device__ __forceinline__ void dma_mainloop_seq(
     phase(std::integral_constant<int, FH>{}, nkt, T);
 }
 
+// Kernel-1 with its loads and its MFMAs in separate wave groups ("Resumo Técnico:
+// Sobreposição de Ativação em Nível de Tile ...", Metodologia / Kernel-1: producer
+// warps load the tiles, consumer warps compute, SiLU(Gate) overlapping the Up
+// loads).  The work-group holds WM x WN consumer waves (the accumulators and MFMAs
+// of dma_mainloop_seq) and kWsProducers producer waves that only drive the S-stage
+// direct-to-LDS ring: they issue tile t+S-1, wait for their own loads of tile t+1
+// and meet the consumers at the one barrier per tile.  Both groups run the same
+// loops, so they pass the same barriers; while the consumers evaluate SiLU(s*gate)
+// the producers are already issuing the first Up tiles.  Products and K order are
+// those of dma_mainloop_seq (bit-identical output).
+constexpr int kWsProducers = 4;
+
+template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
+__device__ __forceinline__ void ws_mainloop_seq(
+    const Gemm16Params& p, char* smem, int m0, int n0, int nkt,
+    typename DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>::Acc& acc, int wave, int lane) {
+    using D = DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>;
+    static_assert(D::SEQ, "sequential SwiGLU only");
+    constexpr int ESZ = D::ESZ, FM = D::FM, FN = D::FN, KS = D::KS, TM = D::TM, TN = D::TN;
+    constexpr int BNS = D::BNS, NW = D::NW, STAGE = D::STAGE, FH = FN / 2;
+    constexpr int NP = kWsProducers;
+    using TA_ = typename D::TA_;
+    using Frag = typename D::Frag;
+    using SA = DmaStream<true, BM, BK, ESZ, NP>;
+    using SB = DmaStream<false, BNS, BK, ESZ, NP>;
+    constexpr int NLP = SA::NI + SB::NI;           // loads per producer thread and tile
+    static_assert((S - 2) * NLP < 64, "vmcnt range");
+    const bool producer = wave >= NW;              // wave-uniform
+    const int pw = producer ? wave - NW : 0;
+    const int wm = wave % WM, wn = (wave / WM) % WN;
+    const int T = 2 * nkt;
+
+    SA da;
+    SB d1, d2;
+    if (producer) {
+        da.init(p.A, p.lda, m0, p.M, 0, pw, lane);
+        d1.init(p.B, p.ldb, n0 / 2, p.N / 2, 0, pw, lane);
+        d2.init(p.B2, p.ldb, n0 / 2, p.N / 2, 0, pw, lane);
+    }
+    auto issue = [&](int t) {
+        char* st = smem + (t % S) * STAGE;
+        if (t < nkt) {
+            da.issue(st, t, pw);
+            d1.issue(st + TA_::BYTES, t, pw);
+        } else {
+            da.issue(st, t - nkt, pw);
+            d2.issue(st + TA_::BYTES, t - nkt, pw);
+        }
+    };
+    if (nkt <= 0) return;
+    if (producer) {
+        // one barrier after the first tile has landed, then one per tile: the loads of
+        // tile t+S-1, then tile t+1 must have landed (the consumers' barrier count)
+#pragma unroll
+        for (int i = 0; i < S - 1; ++i)
+            if (i < T) issue(i);
+        if (T >= S - 1) wait_vmcnt<(S - 2) * NLP>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        for (int t = 0; t < T; ++t) {
+            if (t + S - 1 < T) {
+                issue(t + S - 1);
+                wait_vmcnt<(S - 2) * NLP>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            __builtin_amdgcn_s_barrier();
+        }
+        return;
+    }
+
+    Frag fa[2][FM], fb[2][FH];
+    auto read_all = [&](const char* st, int s, Frag (&af)[FM], Frag (&bf)[FH]) {
+#pragma unroll
+        for (int tm = 0; tm < FM; ++tm)
+            af[tm] = read_frag<true, BM, BK, ESZ>(st, wm * TM + tm * 32, s, lane);
+#pragma unroll
+        for (int tn = 0; tn < FH; ++tn)
+            bf[tn] = read_frag<false, BNS, BK, ESZ>(st + TA_::BYTES, wn * (TN / 2) + tn * 32, s,
+                                                   lane);
+    };
+    constexpr int NMF = FM * FH;
+    constexpr int RD_RC = ESZ == 2 ? 2 : 4, RD_KC = ESZ == 2 ? 1 : 2;
+    constexpr int NRD = RD_KC * FM + RD_RC * FH;
+    // consumers: tiles [t0, t1) into the accumulator fragments OFF .. OFF + FH - 1,
+    // one barrier per tile
+    auto phase = [&](auto off, int t0, int t1) __attribute__((always_inline)) {
+        constexpr int OFF = decltype(off)::value;
+        auto mfma_all = [&](const Frag (&af)[FM], const Frag (&bf)[FH]) {
+#pragma unroll
+            for (int tn = 0; tn < FH; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < FM; ++tm)
+                    acc[OFF + tn][tm] = mfma_op<DT>(bf[tn], af[tm], acc[OFF + tn][tm]);
+        };
+        for (int t = t0; t < t1; ++t) {
+            const char* cur = smem + (t % S) * STAGE;
+#pragma unroll
+            for (int s = 0; s + 1 < KS; ++s) {
+                read_all(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+                mfma_all(fa[s & 1], fb[s & 1]);
+                sched_interleave<NMF, NRD, 0, 0>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // the next tile's first fragments (on the last tile: a stale stage, unused)
+            read_all(smem + ((t + 1) % S) * STAGE, 0, fa[0], fb[0]);
+            mfma_all(fa[1], fb[1]);
+            sched_interleave<NMF, NRD, 0, 0>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_all(smem, 0, fa[0], fb[0]);
+    phase(std::integral_constant<int, 0>{}, 0, nkt);
+    // SiLU(s * gate) while the producers issue the first Up tiles
+    const float sc = DT == DT_E4M3 ? p.alpha : 1.0f;
+#pragma unroll
+    for (int tn = 0; tn < FH; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < FM; ++tm)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[tn][tm][e] = silu(sc * acc[tn][tm][e]);
+    __builtin_amdgcn_sched_barrier(0);
+    phase(std::integral_constant<int, FH>{}, nkt, T);
+}
+
 // The epilogue of one finished output tile (every thread of the work-group).
 template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
 __device__ __forceinline__ void dma_epilogue(
@@ -658,6 +787,41 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_dma_kernel(const Gemm16P
         dma_mainloop<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, smem, m0, n0, kbeg, nkt, ktail,
                                                              acc, wave, lane);
     dma_epilogue<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, acc, smem, m0, n0, wave, lane);
+}
+
+// The wave-specialised Kernel-1 (ws_mainloop_seq): WM x WN consumer waves and
+// kWsProducers producer waves per work-group; all of them take part in the staged
+// epilogue's barriers and stores, the producers with no accumulators to stage.
+template <int DT, bool TA, bool TB, int EPI, int BM, int BN, int BK, int S, int WM, int WN>
+__global__ void __launch_bounds__(64 * (WM * WN + kWsProducers), 1)
+    gemm_ws_kernel(const Gemm16Params p_) {
+    using D = DmaShape<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>;
+    static_assert(D::SEQ, "the wave-specialised kernel runs Kernel-1 only");
+    const Gemm16Params p = batch_item(p_);
+    __shared__ __attribute__((aligned(1024))) char smem[D::LDS];
+
+    const int nblk = p.tiles_m * p.tiles_n;
+    const int lid = xcd_remap(blockIdx.x, nblk);
+    int tmi, tni;
+    tile_coords(lid, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+    const int nkt = p.K / BK;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const bool consumer = wave < D::NW;
+
+    typename D::Acc acc;
+#pragma unroll
+    for (int i = 0; i < D::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < D::FM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    ws_mainloop_seq<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>(p, smem, m0, n0, nkt, acc, wave, lane);
+    static_assert(BM * (BN + 8) <= D::LDS, "staged SwiGLU tile fits the LDS ring");
+    const int wm = wave % WM, wn = (wave / WM) % WN;
+    epilogue_swiglu_lds<D::DT_OUT, D::FM, D::FN, BM, BN, 64 * (WM * WN + kWsProducers), true,
+                        DT == DT_E4M3, true>(p, acc, smem, m0, n0, wm * D::TM, wn * (D::TN / 2),
+                                             lane, consumer);
 }
 
 }  // namespace sg

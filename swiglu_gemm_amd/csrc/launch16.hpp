@@ -34,7 +34,16 @@ constexpr bool w12_ok() {
 template <int DT, bool TA, bool TB, int EPI, int DMA, int BM, int BN, int BK, int S, int WM, int WN>
 inline hipError_t launch_one(const Gemm16Params& p, int splits, hipStream_t st) {
     constexpr int ESZ = DT == DT_E4M3 ? 1 : 2;
-    if constexpr (EPI == EPI_SWIGLU_W12 || EPI == EPI_SWIGLU_SEQ) {
+    if constexpr (EPI == EPI_SWIGLU_SEQ && DMA == 4) {
+        // Kernel-1 with producer waves: the loads split over kWsProducers waves
+        if constexpr (!TA && !TB && (BN / WN / 32) % 2 == 0 && BN % 64 == 0 &&
+                      dma_tile_ok(true, BM, BK, ESZ, kWsProducers) &&
+                      dma_tile_ok(false, BN / 2, BK, ESZ, kWsProducers))
+            return launch_grid(gemm_ws_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
+                               64 * (WM * WN + kWsProducers), st);
+        else
+            return hipErrorInvalidValue;
+    } else if constexpr (EPI == EPI_SWIGLU_W12 || EPI == EPI_SWIGLU_SEQ) {
         if constexpr (w12_ok<DT, TA, TB, DMA, BM, BN, BK, WM, WN>())
             return launch_grid(gemm_dma_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
                                64 * WM * WN, st);

@@ -133,8 +133,8 @@ def test_w12_one_hot_bit_exact(dtype):
 # Gate then Up (Kernel-1 of the SwiGLU page): SiLU(Gate) computed between the two
 # K loops while the first Up tiles load
 # --------------------------------------------------------------------------
-SEQ_CFGS16 = [49, 50]
-SEQ_CFGS8 = [51, 52]
+SEQ_CFGS16 = [49, 50, 53]        # 53: loads in 4 producer waves beside 4 consumer waves
+SEQ_CFGS8 = [51, 52, 54]
 
 
 def run_forced(pb, M, N, K, dtype, cfg):
@@ -174,7 +174,7 @@ def test_seq_e4m3(cfg, M):
     assert_close(oracle.decode(y, "bf16"), reference(pb, M, N, K, "e4m3"), "e4m3", K, desc)
 
 
-@pytest.mark.parametrize("dtype,cfg", [("bf16", 49), ("e4m3", 51)])
+@pytest.mark.parametrize("dtype,cfg", [("bf16", 49), ("e4m3", 51), ("bf16", 53), ("e4m3", 54)])
 def test_seq_one_hot_bit_exact(dtype, cfg):
     M, N, K = 256, 512, 1024
     gen = np.random.default_rng(8)
@@ -208,7 +208,8 @@ def test_split_weight_default_path_full(dtype, M):
 
 
 @pytest.mark.parametrize("dtype,M,cfg", [("bf16", 2048, 49), ("bf16", 8192, 49),
-                                         ("e4m3", 4096, 51), ("e4m3", 256, 52)])
+                                         ("e4m3", 4096, 51), ("e4m3", 256, 52),
+                                         ("bf16", 2048, 53), ("e4m3", 16, 54)])
 def test_seq_workload_sizes_full(dtype, M, cfg):
     """Gate then Up forced at the SwiGLU workloads' full sizes: every output."""
     N, K = (4864, 896) if dtype == "bf16" else (11008, 4096)
