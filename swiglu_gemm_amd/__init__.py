@@ -307,6 +307,25 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N", tran
     return C
 
 
+def gemm_noalloc(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N",
+                 transB: str = "N", dtype: int | None = None, M=None, N=None, K=None, lda=None,
+                 ldb=None, ldc=None):
+    """gemm() through sg_gemm_noalloc: the same result with no device allocation (its
+    scratch is a fixed array of the library), for code under HIP graph capture.  A
+    problem that needs more scratch raises (SG_STATUS_SCRATCH_LIMIT) with C untouched."""
+    code = _dtype_code(A) if dtype is None else dtype
+    ta, tb = transA.upper(), transB.upper()
+    M, N, K, lda, ldb, ldc = _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc,
+                                        _out_dtypes(code))
+    _on_gpu(A, B, C)
+    st = lib().sg_gemm_noalloc(ta.encode(), tb.encode(), M, N, K, float(alpha),
+                               ctypes.c_void_p(A.data_ptr()), lda, ctypes.c_void_p(B.data_ptr()),
+                               ldb, float(beta), ctypes.c_void_p(C.data_ptr()), ldc, code,
+                               _stream(C))
+    _check(st, "sg_gemm_noalloc")
+    return C
+
+
 def gemm_ex(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N",
             transB: str = "N", bias=None, activation: str = "none", out_scale=None,
             dtype: int | None = None, M=None, N=None, K=None, lda=None, ldb=None, ldc=None):

@@ -30,6 +30,14 @@ def test_gemm_well_formed_reaches_the_device_check():
            t(16, 4, dtype=torch.float8_e4m3fn), t(8, 4))
 
 
+def test_gemm_noalloc_checks_like_gemm():
+    raises(ValueError, ON_GPU, sg.gemm_noalloc, t(8, 16), t(16, 4), t(8, 4))
+    raises(ValueError, "rows", sg.gemm_noalloc, t(8, 16), t(15, 4), t(8, 4))
+    raises(ValueError, "C holds", sg.gemm_noalloc, t(8, 16), t(16, 4), t(7, 4))
+    raises(TypeError, "C has dtype", sg.gemm_noalloc, t(8, 16), t(16, 4),
+           t(8, 4, dtype=torch.float16))
+
+
 def test_gemm_inner_dimensions_must_agree():
     raises(ValueError, "rows", sg.gemm, t(8, 16), t(15, 4), t(8, 4))
     raises(ValueError, "rows", sg.gemm, t(8, 16), t(4, 15), t(8, 4), transB="T")
