@@ -172,7 +172,56 @@ __global__ void __launch_bounds__(1024) l2_stream(const char* src, int64_t regio
     }
 }
 
+// LDS read throughput: each wave reads its own 16 KiB of a 128 KiB buffer (so at most
+// 8 waves), 16 distinct reads per loop trip, addresses rotating with the trip so no
+// read can be hoisted.  KIND 0: ds_read_b128 (a wave reads 1 KiB of consecutive
+// 16-byte pieces: no bank conflict); KIND 1: the transposing ds_read_b64_tr_b16 (512
+// bytes per wave read).
+typedef short i16x4_d __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_d lds_i16x4_d;
+
+template <int KIND>
+__global__ void __launch_bounds__(512) lds_read(int iters, uint32_t* out) {
+    __shared__ __attribute__((aligned(1024))) char buf[131072];
+    for (int i = threadIdx.x; i < 131072 / 4; i += blockDim.x)
+        reinterpret_cast<uint32_t*>(buf)[i] = (uint32_t)i * 2654435761u;
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int base = (wave & 7) * 16384;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if constexpr (KIND == 0) {
+                const int off = base + (((j + it) & 15) << 10) + lane * 16;
+                acc ^= *reinterpret_cast<const u32x4*>(buf + off);
+            } else {
+                const int off = base + (((j + it) & 15) << 9) + lane * 8;
+                const i16x4_d v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_d*)(buf + off));
+                acc.x ^= (uint32_t)(uint16_t)v.x | ((uint32_t)(uint16_t)v.y << 16);
+                acc.y ^= (uint32_t)(uint16_t)v.z | ((uint32_t)(uint16_t)v.w << 16);
+            }
+        }
+    }
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
+
+// LDS read throughput probe (see lds_read): kind 0 ds_read_b128, kind 1
+// ds_read_b64_tr_b16; `blocks` work-groups of `waves` (1..8) waves, each wave making
+// iters*16 reads; out: blocks*64*waves words (device).  Returns a hipError_t.
+extern "C" int sg_diag_lds_read(int kind, int blocks, int waves, int iters, void* out,
+                                void* stream) {
+    if (!out || blocks <= 0 || waves < 1 || waves > 8 || iters < 1 || kind < 0 || kind > 1)
+        return (int)hipErrorInvalidValue;
+    hipStream_t st = (hipStream_t)stream;
+    if (kind == 0)
+        hipLaunchKernelGGL(lds_read<0>, dim3(blocks), dim3(64 * waves), 0, st, iters, (uint32_t*)out);
+    else
+        hipLaunchKernelGGL(lds_read<1>, dim3(blocks), dim3(64 * waves), 0, st, iters, (uint32_t*)out);
+    return (int)hipGetLastError();
+}
 
 // Per-CU L2 -> CU throughput probe (see l2_stream): kind 0 registers, kinds 1-3 LDS DMA;
 // depth in {4, 8, 16}; waves 1..16 per work-group; region (a multiple of waves*1024
