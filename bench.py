@@ -19,8 +19,12 @@ pair); the fused SwiGLU-GEMM (bf16: A[M x 896], W_fused[896 x 9728], M in {128,
 M in {1, 16, 256, 4096}) with cold weights (copies rotated past the last-level
 cache) and hot, against this library's unfused path (two sg_gemm calls writing
 Gate and Up, then sg_silu_mul), the split-weight entry point (separate W1, W2:
-w12_ms) and torch eager as context; and the fp64 CPU oracle timed on a bounded
-sample of the GEMM rows.
+w12_ms), Kernel-1's Gate-then-Up schedule on the same split weights (seq_ms), HIP
+graph replays of the fused and unfused steps, and torch eager as context; the fused
+bias + GELU GEMM epilogue; the fp32 GEMM (256^3 and 4096^3); the clock before,
+after and under load and the board's read / copy bandwidth; and the fp64 CPU oracle
+timed on a bounded sample of the GEMM rows, whose outputs double as an every-element
+check of those rows (numerics).
 
 Prints ONE JSON line.
 
