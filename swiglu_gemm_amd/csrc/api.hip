@@ -426,9 +426,29 @@ hipError_t relay_e4m3(Operand8 (&ops)[2], int64_t batch, hipStream_t st, bool* r
     return hipSuccess;
 }
 
-void set_last(const char* what, int cfg, int splits) {
-    std::snprintf(g_last_cfg, sizeof(g_last_cfg), "%s cfg=%d %s splits=%d", what, cfg,
-                  cfg >= 0 && cfg < kNumCfg16 ? kCfg16[cfg].name : "-", splits);
+void set_last(const char* what, int cfg, int splits, int warm = 0) {
+    const int n = std::snprintf(g_last_cfg, sizeof(g_last_cfg), "%s cfg=%d %s splits=%d", what,
+                                cfg, cfg >= 0 && cfg < kNumCfg16 ? kCfg16[cfg].name : "-", splits);
+    if (warm > 0 && n > 0 && n < (int)sizeof(g_last_cfg))
+        std::snprintf(g_last_cfg + n, sizeof(g_last_cfg) - n, " l2warm=%d", warm);
+}
+
+// The L2 warm-up of gemm_dma_kernel (warm_l2 in gemm16_dma.hpp): a single round of
+// fewer tiles than CUs, B row-major, and each XCD's share of B (plus A, which every
+// XCD reads whole) well inside its 4 MB L2 -- then the idle CUs become warm-up
+// blocks and the grid is one block per CU.  Returns that grid size, or 0.
+// SG_NO_WARM=1 turns it off (tuning, tests).
+constexpr int64_t kWarmMaxBytes = (int64_t)7 << 19;     // 3.5 MiB per XCD
+int warm_grid(const Problem16& q, const Cfg16& c, bool tb, int epi, const Gemm16Params& p) {
+    if (tb || c.dma != 1 || p.batch > 1) return 0;
+    if (epi != EPI_GEMM && epi != EPI_GEMM_EX && epi != EPI_SWIGLU) return 0;
+    const char* off = std::getenv("SG_NO_WARM");
+    if (off && *off == '1') return 0;
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles < 8 || tiles > kNumCU - 16 || p.tiles_m > p.group_m) return 0;
+    if (q.K < 4 * (int64_t)c.BK) return 0;                  // nothing to run ahead of
+    const int64_t per_xcd = q.K * q.N * q.esz / 8 + q.M * q.K * q.esz;
+    return per_xcd <= kWarmMaxBytes ? kNumCU : 0;
 }
 
 // The configuration compiled with the extra epilogue steps (EPI_GEMM_EX) that is
@@ -535,7 +555,8 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
             if (e != hipSuccess) return e;
             return launch16_dt<DT>(ta, tb, epi, cs.cfg_tail, pt, 1, st);
         }
-        set_last(what, cfg, 1);
+        p.warm_grid = warm_grid(q, c, tb, epi, p);
+        set_last(what, cfg, 1, p.warm_grid > 0 ? p.warm_grid - p.tiles_m * p.tiles_n : 0);
         return launch16_dt<DT>(ta, tb, epi, cfg, p, 1, st);
     }
     float* ws = nullptr;

@@ -13,8 +13,9 @@ namespace sg {
 
 template <typename Kern>
 inline hipError_t launch_grid(Kern k, const Gemm16Params& p, int splits, int threads,
-                              hipStream_t st) {
-    dim3 grid((unsigned)(p.tiles_m * p.tiles_n), (unsigned)splits,
+                              hipStream_t st, bool warm = false) {
+    const int tiles = p.tiles_m * p.tiles_n;
+    dim3 grid((unsigned)(warm && p.warm_grid > tiles ? p.warm_grid : tiles), (unsigned)splits,
               (unsigned)(p.batch > 1 ? p.batch : 1));
     hipLaunchKernelGGL(k, grid, dim3(threads), 0, st, p);
     return hipGetLastError();
@@ -50,9 +51,11 @@ inline hipError_t launch_one(const Gemm16Params& p, int splits, hipStream_t st) 
         else
             return hipErrorInvalidValue;
     } else if constexpr (DMA || DT == DT_E4M3) {
+        // only this kernel has work for blocks past the tiles (the L2 warm-up), and
+        // only with row-major B, one split and one problem (the host checks the same)
         if constexpr (dma_tile_ok(!TA, BM, BK, ESZ, WM * WN) && dma_tile_ok(TB, BN, BK, ESZ, WM * WN))
             return launch_grid(gemm_dma_kernel<DT, TA, TB, EPI, BM, BN, BK, S, WM, WN>, p, splits,
-                               64 * WM * WN, st);
+                               64 * WM * WN, st, !TB && splits == 1 && p.batch <= 1);
         else
             return hipErrorInvalidValue;
     } else

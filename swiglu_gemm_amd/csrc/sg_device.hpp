@@ -167,6 +167,8 @@ struct Gemm16Params {
     int tiles_m, tiles_n, group_m;
     int k_per_split;    // a multiple of 64; gridDim.y splits
     int epi_flags;      // EPI_SWIGLU: EPI_Y16 (Y rows allow 16-byte stores)
+    int warm_grid;      // gemm_dma_kernel with row-major B: gridDim.x when larger than
+                        // tiles_m*tiles_n; the extra work-groups warm L2 (warm_l2)
     int batch;          // strided batch: gridDim.z problems (0 or 1: one problem)
     int64_t sA, sB, sC; // byte distance between consecutive problems' A, B, C
     EpiEx ex;           // EPI_GEMM_EX: bias / activation / e4m3 output
