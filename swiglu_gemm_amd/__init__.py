@@ -44,6 +44,8 @@ class SwigluGemmError(RuntimeError):
 def lib() -> ctypes.CDLL:
     """Load libswiglu_gemm.so (raises if it is not built)."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -171,9 +173,19 @@ def _out_dtypes(code: int):
     return _tables()[1][code]
 
 
+_RAW_STREAM = None
+
+
 def _stream(t):
-    import torch
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    """Handle (an int) of torch's current HIP stream on t's device.  torch's raw-stream
+    query skips building a Stream object (about 2 us a call); older builds without it
+    take the public route."""
+    global _RAW_STREAM
+    if _RAW_STREAM is None:
+        import torch
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None) or \
+            (lambda d: torch.cuda.current_stream(d).cuda_stream)
+    return _RAW_STREAM(t.get_device())
 
 
 def _ld(t) -> int:
@@ -246,7 +258,7 @@ def _gemm_args(A, B, C, ta, tb, code, M, N, K, lda, ldb, ldc, c_dtypes, batch=1,
     tensor's shape and strides are read once: these checks run on every call)."""
     if ta not in ("N", "T") or tb not in ("N", "T"):
         raise ValueError("transA and transB must be 'N' or 'T'")
-    ash, bsh, csh = tuple(A.shape), tuple(B.shape), tuple(C.shape)
+    ash, bsh, csh = A.shape, B.shape, C.shape
     ast, bst, cst = A.stride(), B.stride(), C.stride()
     if M is None:
         if len(ash) < 2 or len(bsh) < 2:
@@ -301,8 +313,8 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N", tran
                                         _out_dtypes(code))
     _on_gpu(A, B, C)
     st = lib().sg_gemm(ta.encode(), tb.encode(), M, N, K, float(alpha),
-                       ctypes.c_void_p(A.data_ptr()), lda, ctypes.c_void_p(B.data_ptr()),
-                       ldb, float(beta), ctypes.c_void_p(C.data_ptr()), ldc, code, _stream(C))
+                       A.data_ptr(), lda, B.data_ptr(),
+                       ldb, float(beta), C.data_ptr(), ldc, code, _stream(C))
     _check(st, "sg_gemm")
     return C
 
@@ -319,8 +331,8 @@ def gemm_noalloc(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "
                                         _out_dtypes(code))
     _on_gpu(A, B, C)
     st = lib().sg_gemm_noalloc(ta.encode(), tb.encode(), M, N, K, float(alpha),
-                               ctypes.c_void_p(A.data_ptr()), lda, ctypes.c_void_p(B.data_ptr()),
-                               ldb, float(beta), ctypes.c_void_p(C.data_ptr()), ldc, code,
+                               A.data_ptr(), lda, B.data_ptr(),
+                               ldb, float(beta), C.data_ptr(), ldc, code,
                                _stream(C))
     _check(st, "sg_gemm_noalloc")
     return C
@@ -351,8 +363,8 @@ def gemm_ex(A, B, C, alpha: float = 1.0, beta: float = 0.0, transA: str = "N",
                    SG_F8E4M3 if out_scale is not None else -1,
                    float(out_scale) if out_scale is not None else 1.0)
     st = lib().sg_gemm_ex(ta.encode(), tb.encode(), M, N, K, float(alpha),
-                          ctypes.c_void_p(A.data_ptr()), lda, ctypes.c_void_p(B.data_ptr()),
-                          ldb, float(beta), ctypes.c_void_p(C.data_ptr()), ldc, code,
+                          A.data_ptr(), lda, B.data_ptr(),
+                          ldb, float(beta), C.data_ptr(), ldc, code,
                           ctypes.byref(epi), _stream(C))
     _check(st, "sg_gemm_ex")
     return C
@@ -374,9 +386,9 @@ def gemm_strided_batched(A, B, C, batch, strideA, strideB, strideC, alpha: float
                                         strides=(int(strideA), int(strideB), int(strideC)))
     _on_gpu(A, B, C)
     st = lib().sg_gemm_strided_batched(ta.encode(), tb.encode(), M, N, K,
-                                       float(alpha), ctypes.c_void_p(A.data_ptr()), lda,
-                                       int(strideA), ctypes.c_void_p(B.data_ptr()), ldb,
-                                       int(strideB), float(beta), ctypes.c_void_p(C.data_ptr()),
+                                       float(alpha), A.data_ptr(), lda,
+                                       int(strideA), B.data_ptr(), ldb,
+                                       int(strideB), float(beta), C.data_ptr(),
                                        ldc, int(strideC), int(batch), code, _stream(C))
     _check(st, "sg_gemm_strided_batched")
     return C
@@ -384,24 +396,36 @@ def gemm_strided_batched(A, B, C, batch, strideA, strideB, strideC, alpha: float
 
 def _swiglu_args(A, W_list, Y, two_n: bool):
     """M, N, K of a SwiGLU call, with A [M, K], each weight [K, 2N] (two_n) or [K, N]
-    and Y [M, N] contiguous; operands of one dtype, Y bf16 (fp16 for fp16 inputs)."""
-    if A.dim() != 2 or any(w.dim() != 2 for w in W_list):
+    and Y [M, N] contiguous; operands of one dtype, Y bf16 (fp16 for fp16 inputs).
+    Each tensor attribute is read once (these checks run on every call)."""
+    ash = A.shape
+    wshapes = [w.shape for w in W_list]
+    if len(ash) != 2 or any(len(sh) != 2 for sh in wshapes):
         raise ValueError("A and the weights must be 2-D")
-    M, K = int(A.shape[0]), int(A.shape[1])
-    W0 = W_list[0]
-    if two_n and W0.shape[1] % 2:
+    M, K = ash
+    ncols = wshapes[0][1]
+    if two_n and ncols % 2:
         raise ValueError("Wfused must have an even number of columns (gate, up pairs)")
-    N = int(W0.shape[1]) // 2 if two_n else int(W0.shape[1])
-    code = _dtype_code(A)
+    N = ncols // 2 if two_n else ncols
+    codes = _tables()[0]
+    code = codes.get(A.dtype)
+    if code is None:
+        raise TypeError("unsupported dtype %s" % A.dtype)
     if code == SG_F32:
         raise TypeError("SwiGLU takes bf16, fp16 or e4m3 operands")
-    _contig(A, "A", (M, K))
-    for i, w in enumerate(W_list):
-        _contig(w, "weight %d" % i, (K, 2 * N if two_n else N))
-        if _dtype_code(w) != code or w.element_size() != A.element_size():
+    if not A.is_contiguous():
+        raise ValueError("A must be contiguous")
+    want = (K, ncols)
+    for i, (w, sh) in enumerate(zip(W_list, wshapes)):
+        if sh != want:
+            raise ValueError("weight %d has shape %s, expected %s" % (i, tuple(sh), want))
+        if not w.is_contiguous():
+            raise ValueError("weight %d must be contiguous" % i)
+        if codes.get(w.dtype) != code:
             raise TypeError("the weights must have A's dtype")
-    if Y.dtype not in _out_dtypes(code):
-        raise TypeError("Y has dtype %s, expected %s" % (Y.dtype, _out_dtypes(code)[0]))
+    outs = _tables()[1][code]
+    if Y.dtype not in outs:
+        raise TypeError("Y has dtype %s, expected %s" % (Y.dtype, outs[0]))
     _contig(Y, "Y", (M, N))
     return M, N, K, code
 
@@ -411,8 +435,8 @@ def swiglu_gemm(A, Wfused, Y, scale_a: float = 1.0, scale_w: float = 1.0):
     (s = scale_a*scale_w); A [M, K], Y [M, N], all contiguous."""
     M, N, K, code = _swiglu_args(A, [Wfused], Y, True)
     _on_gpu(A, Wfused, Y)
-    st = lib().sg_swiglu_gemm(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(Wfused.data_ptr()),
-                              ctypes.c_void_p(Y.data_ptr()), M, N, K, code, float(scale_a),
+    st = lib().sg_swiglu_gemm(A.data_ptr(), Wfused.data_ptr(),
+                              Y.data_ptr(), M, N, K, code, float(scale_a),
                               float(scale_w), _stream(Y))
     _check(st, "sg_swiglu_gemm")
     return Y
@@ -423,8 +447,8 @@ def swiglu_gemm_w12(A, W1, W2, Y, scale_a: float = 1.0, scale_w: float = 1.0):
     A [M, K], Y [M, N], all contiguous."""
     M, N, K, code = _swiglu_args(A, [W1, W2], Y, False)
     _on_gpu(A, W1, W2, Y)
-    st = lib().sg_swiglu_gemm_w12(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(W1.data_ptr()),
-                                  ctypes.c_void_p(W2.data_ptr()), ctypes.c_void_p(Y.data_ptr()),
+    st = lib().sg_swiglu_gemm_w12(A.data_ptr(), W1.data_ptr(),
+                                  W2.data_ptr(), Y.data_ptr(),
                                   M, N, K, code, float(scale_a), float(scale_w), _stream(Y))
     _check(st, "sg_swiglu_gemm_w12")
     return Y
@@ -446,8 +470,8 @@ def interleave_gate_up(W1, W2, out=None):
     if out.element_size() != W1.element_size():
         raise TypeError("out must have W1's element size")
     _on_gpu(W1, W2, out)
-    st = lib().sg_interleave_gate_up(ctypes.c_void_p(W1.data_ptr()), ctypes.c_void_p(W2.data_ptr()),
-                                     ctypes.c_void_p(out.data_ptr()), K, N,
+    st = lib().sg_interleave_gate_up(W1.data_ptr(), W2.data_ptr(),
+                                     out.data_ptr(), K, N,
                                      _dtype_code(W1), _stream(out))
     _check(st, "sg_interleave_gate_up")
     return out
@@ -466,7 +490,7 @@ def silu_mul(G, U, Y):
         if t.dtype != G.dtype:
             raise TypeError("G, U and Y must have one dtype")
     _on_gpu(G, U, Y)
-    st = lib().sg_silu_mul(ctypes.c_void_p(G.data_ptr()), ctypes.c_void_p(U.data_ptr()),
-                           ctypes.c_void_p(Y.data_ptr()), M, N, _dtype_code(G), _stream(Y))
+    st = lib().sg_silu_mul(G.data_ptr(), U.data_ptr(),
+                           Y.data_ptr(), M, N, _dtype_code(G), _stream(Y))
     _check(st, "sg_silu_mul")
     return Y
