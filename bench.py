@@ -669,6 +669,7 @@ SWIGLU_COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_swiglu_kernels.m
 SWIGLU_PROBES = [("e4m3 SwiGLU M=1", "e4m3", 1, 11008, 4096),
                  ("e4m3 SwiGLU M=16", "e4m3", 16, 11008, 4096),
                  ("e4m3 SwiGLU M=256", "e4m3", 256, 11008, 4096),
+                 ("bf16 SwiGLU M=128", "bf16", 128, 4864, 896),
                  ("bf16 SwiGLU M=512", "bf16", 512, 4864, 896),
                  ("bf16 SwiGLU M=2048", "bf16", 2048, 4864, 896)]
 
@@ -755,7 +756,9 @@ def pmc_swiglu_summarize(fetch_csv, write_csv, sq_csv):
              "kernel times are in the bench line and bench_default_kernel_stats.md), so rates are "
              "not derived from them; the clock is not given for these short launches (the "
              "GRBM-based estimate is not meaningful below ~100 us); MFMA busy shares that "
-             "denominator and so understates them.", "",
+             "denominator and so understates them. Where the launch adds L2 warm-up work-groups "
+             "(one per idle CU; bf16 M=128 and 512), the HBM bytes include their loads and the "
+             "per-work-group LDS figure counts them among the work-groups.", "",
              "| workload | kernel | HBM read MB | HBM write MB | algorithmic MB | read / algorithmic | "
              "MFMA busy | LDS bank-conflict cycles per work-group |",
              "|---|---|---|---|---|---|---|---|"]
