@@ -535,6 +535,49 @@ def read_bandwidth(torch, nbytes=COPY_BYTES, reps=20):
     return round(best, 1)
 
 
+def read_same_bytes_ms(torch, nbytes, reps=40):
+    """Time of the diagnostic library's plain read kernel over nbytes (rounded down to
+    16) with the data cold in HBM (buffers of that size rotated through > 512 MiB, as
+    the SwiGLU weights are), an eager loop of launches as in the SwiGLU timing; best of
+    four grid sizes.  The floor for a kernel that must stream the same bytes once,
+    launch and ramp included.  None if the diagnostic library is not built."""
+    import ctypes
+    from swiglu_gemm_amd import build as b
+    if not os.path.exists(b.DIAG_LIB):
+        return None
+    lib = ctypes.CDLL(b.DIAG_LIB)
+    lib.sg_diag_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+    lib.sg_diag_stream_read.restype = ctypes.c_int
+    nbytes -= nbytes % 16
+    nbuf = max(4, -(-COLD_BYTES // nbytes))
+    bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0") for _ in range(nbuf)]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for blocks in (256, 512, 1024, 2048):
+        out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda:0")
+
+        def run(i):
+            rc = lib.sg_diag_stream_read(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nbytes,
+                                         ctypes.c_void_p(out.data_ptr()), blocks, st)
+            assert rc == 0, rc
+        for i in range(2 * nbuf):
+            run(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(reps):
+            run(i)
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / reps
+        best = ms if best is None else min(best, ms)
+    del bufs
+    torch.cuda.empty_cache()
+    return round(best, 5)
+
+
 def copy_bandwidth(torch, nbytes=COPY_BYTES, reps=20):
     """Streaming rate of a plain device-to-device copy (read + write bytes per
     second) over two buffer pairs, 2 GiB in all, so the last-level cache holds
@@ -1243,6 +1286,14 @@ def main():
     for s in sw:                  # against what this board's HBM delivers to a plain read
         if rb:
             s["frac_of_read_bw"] = round(s["hbm_gbs_algorithmic"] / rb, 4)
+        if (s["dtype"], s["M"]) in (("e4m3", 1), ("e4m3", 16), ("bf16", 128)):
+            # the weight-streaming rows: a plain read of the same bytes, cold, same timing
+            esz = 1 if s["dtype"] == "e4m3" else 2
+            nb = (s["M"] * s["K"] + 2 * s["K"] * s["N"]) * esz + s["M"] * s["N"] * 2
+            t = read_same_bytes_ms(torch, nb)
+            if t:
+                s["plain_read_same_bytes_ms"] = t
+                s["frac_of_plain_read_same_bytes"] = round(t / s["ms"], 4)
     out["swiglu_m2048"] = [s for s in sw if s["dtype"] == "bf16" and s["M"] == 2048][0]
     if len(sw) > 1:
         out["swiglu_all"] = sw
