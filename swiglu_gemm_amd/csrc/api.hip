@@ -249,7 +249,11 @@ int pick_splits(const Cfg16& c, const Problem16& q) {
 // 192: fp16 4096 x {3072, 6144} x 4096 and 8192 x 3072 x 4096, one and two full
 // rounds, 101.7, 186.1 and 184.5 us against 119.8, 210.8 and 209.8 us for the
 // previous choice; 128 x 192: bf16 SwiGLU M = 512, fused width 9728, one round of
-// 204 tiles, 15.7-16.0 us against 17.6 us for 152 tiles of 128 x 256.)
+// 204 tiles, 15.7-16.0 us against 17.6 us for 152 tiles of 128 x 256.  Its ring
+// has 4 stages, the whole LDS: the loads of these short-K shapes run about as long
+// as the MFMAs, and a third tile in flight hides more of their latency (measured,
+// alternating builds: SwiGLU M = 512 16.6 -> 15.3 us, M = 640 17.9 -> 16.9 us, GEMM
+// 512 x 9728 x 896 19.9 -> 17.4 us against 3 stages; bit-identical).)
 struct Cand16 {
     int id;
     double tf_per_cu;

@@ -70,7 +70,7 @@ constexpr Cfg16 kCfg16[] = {
     // 192-column tiles: one full round where 256 columns leave CUs idle (N = 3072)
     {0, 1, 256, 192, 64, 2, 4, 2, "dma 256x192x64 s2 4x2w"},
     {1, 1, 128, 192, 128, 3, 4, 2, "e4m3 dma 128x192x128 s3 4x2w"},
-    {0, 1, 128, 192, 64, 3, 4, 2, "dma 128x192x64 s3 4x2w"},
+    {0, 1, 128, 192, 64, 4, 4, 2, "dma 128x192x64 s4 4x2w"},
     // split-weight SwiGLU, Gate then Up (BN: the fused width, BN/2 outputs)
     {0, 3, 256, 256, 64, 3, 4, 2, "seq 256x256x64 s3 4x2w"},
     {0, 3, 128, 256, 64, 4, 2, 2, "seq 128x256x64 s4 2x2w"},
@@ -126,7 +126,7 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(43, 1, 64, 256, 64, 3, 1, 4)     \
     X(44, 1, 64, 128, 64, 4, 1, 4)     \
     X(46, 1, 256, 192, 64, 2, 4, 2)    \
-    X(48, 1, 128, 192, 64, 3, 4, 2)
+    X(48, 1, 128, 192, 64, 4, 4, 2)
 
 // the pipeline-depth study rows, instantiated for fp16 NN EPI_GEMM only
 #define SG_CONFIGS_SWEEP(X)            \
