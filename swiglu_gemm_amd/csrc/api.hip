@@ -309,7 +309,9 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
                 // ... and 128 x 192 where 128 x 256 leaves over a quarter of the CUs
                 // idle and the narrower tiles still fit one round (GEMM 256 x 11008 x
                 // 4096 NT: 24.4 against 29.1 us; SwiGLU M = 160, 256: 34.3, 35.6
-                // against 36.2, 36.7 us)
+                // against 36.2, 36.7 us); its ring has 4 stages (the whole LDS: GEMM
+                // 1024 x 4096 x 4096 and 256 x 11008 x 4096 NN 29.7, 26.3 -> 26.9, 24.0
+                // us against 3 stages, the SwiGLU rows unchanged; bit-identical)
                 cfg = mid > kNumCU ? 15
                       : (4 * mid <= 3 * kNumCU && cdiv(q.M, 128) * cdiv(q.N, 192) <= kNumCU) ? 47
                                                                                           : 45;

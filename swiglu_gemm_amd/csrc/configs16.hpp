@@ -69,7 +69,7 @@ constexpr Cfg16 kCfg16[] = {
     {1, 1, 128, 256, 128, 3, 2, 4, "e4m3 dma 128x256x128 s3 2x4w"},
     // 192-column tiles: one full round where 256 columns leave CUs idle (N = 3072)
     {0, 1, 256, 192, 64, 2, 4, 2, "dma 256x192x64 s2 4x2w"},
-    {1, 1, 128, 192, 128, 3, 4, 2, "e4m3 dma 128x192x128 s3 4x2w"},
+    {1, 1, 128, 192, 128, 4, 4, 2, "e4m3 dma 128x192x128 s4 4x2w"},
     {0, 1, 128, 192, 64, 4, 4, 2, "dma 128x192x64 s4 4x2w"},
     // split-weight SwiGLU, Gate then Up (BN: the fused width, BN/2 outputs)
     {0, 3, 256, 256, 64, 3, 4, 2, "seq 256x256x64 s3 4x2w"},
@@ -177,6 +177,6 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(17, 1, 32, 128, 128, 4, 1, 4)    \
     X(33, 1, 128, 256, 128, 3, 2, 2)   \
     X(45, 1, 128, 256, 128, 3, 2, 4)   \
-    X(47, 1, 128, 192, 128, 3, 4, 2)
+    X(47, 1, 128, 192, 128, 4, 4, 2)
 
 }  // namespace sg
