@@ -4,8 +4,8 @@ and other eager work of the library runs on the same stream (so a replay that le
 the output untouched, or a captured buffer that eager work overwrote, would show).
 Covers the paths a serving loop would capture: the 8-wave tile GEMM, split-K and
 the decode kernels through the entry point that allocates nothing, the fused
-SwiGLU-GEMM (bf16 and e4m3), the fp32 GEMM and e4m3 operands re-laid with 16-byte
-rows.  Workspace the library owns is grown by the eager call before capture."""
+SwiGLU-GEMM (bf16 and e4m3; bf16 at 128 tokens with the L2 warm-up blocks), the fp32
+GEMM and e4m3 operands re-laid with 16-byte rows.  Workspace the library owns is grown by the eager call before capture."""
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -111,4 +111,8 @@ def test_swiglu_graph_replay(dtype, M):
     Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")
     s = 1.0 if dtype == "bf16" else 0.01
     call = lambda: sg.swiglu_gemm(A, W, Y, s, s)
+    if (dtype, M) == ("bf16", 128):
+        call()                       # this size launches the L2 warm-up blocks too
+        torch.cuda.synchronize()
+        assert "l2warm=" in sg.last_config(), sg.last_config()
     replay_matches_eager(call, Y, other_work())
