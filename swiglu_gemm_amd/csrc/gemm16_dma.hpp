@@ -299,6 +299,32 @@ __device__ __forceinline__ void dma_mainloop(
     using TB_ = typename D::TB_;
     using Frag = typename D::Frag;
     const int wm = wave % WM, wn = wave / WM;
+    // One wave per SIMD: no second wave keeps the matrix core fed while this one
+    // issues the next tile's DMA, so the DMA is dealt out between the MFMAs, one
+    // slot after each fragment column q of the k-steps before the barrier; with 2
+    // stages (tile t+1 must land by the end of tile t) only the first k-step's.
+    // Measured on MI355X against the whole DMA at the top of the tile (fp16 8192^3,
+    // one run): 256x256x64 2 stages 937 -> 892 us, 256x256x32 4 stages 970 -> 925
+    // us, 128x128x64 3 stages 1302 -> 1257 us; the 8-wave tiles keep the burst.
+    // Dealing it over the k-step after the barrier as well was no better.
+    constexpr bool SPREAD = NW == 4 && !W12;
+    // Two-stage rings of 16-bit operands run unrolled by two tiles, so each stage is
+    // a compile-time constant; with the stages laid out [A0 A1 | B0 B1] every stage
+    // offset is below 64 KiB and folds into the LDS reads' immediate field, and the
+    // per-read address adds of a run-time stage go away (NT main loop per two tiles:
+    // 60 -> 9 VALU instructions).  Measured on MI355X, alternating builds, bit-
+    // identical: fp16 8192^3 NN 873.8 -> 864.7 us, NT 889.1 -> 881.5 us, bf16 NN
+    // 836.9 -> 825.9 us, bf16 8192 x 4096 x 4096 NT 216.6 -> 213.2 us.  e4m3
+    // fragments are twice as wide: the hoisted addresses there pushed the 256x256
+    // tile past 256 registers into scratch (4.6x slower), so 8-bit rings keep the
+    // interleaved layout and the rolled loop, and so do waves of more than 8
+    // fragments (the 256x320 tile spilled 16-32 bytes).  Other rings: [A0 B0 | A1
+    // B1 | ..].
+    constexpr bool SPLIT = S == 2 && !W12 && !SPREAD && ESZ == 2 && FM * FN <= 8;
+    auto stA = [&](int st) -> char* { return SPLIT ? smem + st * TA_::BYTES : smem + st * STAGE; };
+    auto stB = [&](int st) -> char* {
+        return SPLIT ? smem + S * TA_::BYTES + st * TB_::BYTES : smem + st * STAGE + TA_::BYTES;
+    };
 
     DmaStream<KCA, BM, BK, ESZ, NW> da;
     DmaStream<KCB, BNS, BK, ESZ, NW> db, db2;
@@ -311,32 +337,34 @@ __device__ __forceinline__ void dma_mainloop(
     }
 
     Frag fa[2][FM], fb[2][FN];
-    auto read_all = [&](const char* st, int s, Frag (&af)[FM], Frag (&bf)[FN]) {
+    auto read_all = [&](int sti, int s, Frag (&af)[FM], Frag (&bf)[FN]) __attribute__((always_inline)) {
+        const char* sa = stA(sti);
+        const char* sb = stB(sti);
 #pragma unroll
         for (int tm = 0; tm < FM; ++tm)
-            af[tm] = read_frag<KCA, BM, BK, ESZ>(st, wm * TM + tm * 32, s, lane);
+            af[tm] = read_frag<KCA, BM, BK, ESZ>(sa, wm * TM + tm * 32, s, lane);
 #pragma unroll
         for (int tn = 0; tn < FN; ++tn) {
             if constexpr (W12) {
                 constexpr int FH = FN / 2;
-                const char* half = st + TA_::BYTES + (tn / FH) * TB_::BYTES;
+                const char* half = sb + (tn / FH) * TB_::BYTES;
                 bf[tn] = read_frag<KCB, BNS, BK, ESZ>(half, wn * (TN / 2) + (tn % FH) * 32, s, lane);
             } else {
-                bf[tn] = read_frag<KCB, BN, BK, ESZ>(st + TA_::BYTES, wn * TN + tn * 32, s, lane);
+                bf[tn] = read_frag<KCB, BN, BK, ESZ>(sb, wn * TN + tn * 32, s, lane);
             }
         }
     };
-    auto mfma_all = [&](const Frag (&af)[FM], const Frag (&bf)[FN]) {
+    auto mfma_all = [&](const Frag (&af)[FM], const Frag (&bf)[FN]) __attribute__((always_inline)) {
 #pragma unroll
         for (int tn = 0; tn < FN; ++tn)
 #pragma unroll
             for (int tm = 0; tm < FM; ++tm) acc[tn][tm] = mfma_op<DT>(bf[tn], af[tm], acc[tn][tm]);
     };
     auto issue = [&](int t) {
-        char* st = smem + (t % S) * STAGE;
-        da.issue(st, t, wave);
-        db.issue(st + TA_::BYTES, t, wave);
-        if constexpr (W12) db2.issue(st + TA_::BYTES + TB_::BYTES, t, wave);
+        const int sti = t % S;
+        da.issue(stA(sti), t, wave);
+        db.issue(stB(sti), t, wave);
+        if constexpr (W12) db2.issue(stB(sti) + TB_::BYTES, t, wave);
     };
 
     if (nkt > 0) {
@@ -347,53 +375,47 @@ __device__ __forceinline__ void dma_mainloop(
         else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        read_all(smem, 0, fa[0], fb[0]);
+        read_all(0, 0, fa[0], fb[0]);
 
         constexpr int NMF = FM * FN;
         constexpr int RD_KC = ESZ == 2 ? 1 : 2, RD_RC = ESZ == 2 ? 2 : 4;
         constexpr int NRD = (KCA ? RD_KC : RD_RC) * FM + (KCB ? RD_KC : RD_RC) * FN;
-        // One wave per SIMD: no second wave keeps the matrix core fed while this one
-        // issues the next tile's DMA, so the DMA is dealt out between the MFMAs, one
-        // slot after each fragment column q of the k-steps before the barrier; with 2
-        // stages (tile t+1 must land by the end of tile t) only the first k-step's.
-        // Measured on MI355X against the whole DMA at the top of the tile (fp16 8192^3,
-        // one run): 256x256x64 2 stages 937 -> 892 us, 256x256x32 4 stages 970 -> 925
-        // us, 128x128x64 3 stages 1302 -> 1257 us; the 8-wave tiles keep the burst.
-        // Dealing it over the k-step after the barrier as well was no better.
-        constexpr bool SPREAD = NW == 4 && !W12;
         constexpr int NIA = DmaStream<KCA, BM, BK, ESZ, NW>::NI;
         constexpr int NSLOT = (S >= 3 ? KS - 1 : 1) * FN;
-        // DMA slot j of tile u into stage memory st
-        auto slot_dma = [&](char* st, int u, int j) __attribute__((always_inline)) {
+        // DMA slot j of tile u into stage sti
+        auto slot_dma = [&](int sti, int u, int j) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < NL; ++i) {
                 if (i * NSLOT / NL != j) continue;
-                if (i < NIA) da.issue_one(st, u, wave, i);
-                else db.issue_one(st + TA_::BYTES, u, wave, i - NIA);
+                if (i < NIA) da.issue_one(stA(sti), u, wave, i);
+                else db.issue_one(stB(sti), u, wave, i - NIA);
             }
         };
         // fragment column q of k-step s: its MFMAs on fragments (fa, fb)[s & 1], and the
         // reads of k-step s2 of stage st2 into the other fragment set
-        auto column = [&](int s, int q, const char* st2, int s2) __attribute__((always_inline)) {
+        auto column = [&](int s, int q, int st2, int s2) __attribute__((always_inline)) {
 #pragma unroll
             for (int tm = q % FN; tm < FM; tm += FN)
-                fa[s2 & 1][tm] = read_frag<KCA, BM, BK, ESZ>(st2, wm * TM + tm * 32, s2, lane);
-            fb[s2 & 1][q] = read_frag<KCB, BN, BK, ESZ>(st2 + TA_::BYTES, wn * TN + q * 32, s2, lane);
+                fa[s2 & 1][tm] = read_frag<KCA, BM, BK, ESZ>(stA(st2), wm * TM + tm * 32, s2, lane);
+            fb[s2 & 1][q] = read_frag<KCB, BN, BK, ESZ>(stB(st2), wn * TN + q * 32, s2, lane);
 #pragma unroll
             for (int tm = 0; tm < FM; ++tm)
                 acc[q][tm] = mfma_op<DT>(fb[s & 1][q], fa[s & 1][tm], acc[q][tm]);
         };
-        for (int t = 0; t < nkt; ++t) {
-            const char* cur = smem + (t % S) * STAGE;
+        // One K tile: its k-steps (with the DMA of tile t+S-1 dealt between the MFMAs
+        // for one wave per SIMD, or issued at the top), the wait and barrier for tile
+        // t+1, then tile t+1's first fragments under tile t's last MFMAs.  sc, sn:
+        // the stages of tiles t and t+1.
+        auto tile = [&](int t, int sc, int sn) __attribute__((always_inline)) {
             const bool ahead = t + S - 1 < nkt;
             if constexpr (SPREAD) {
-                char* nxt = smem + ((t + S - 1) % S) * STAGE;
+                const int sx = (t + S - 1) % S;
 #pragma unroll
                 for (int s = 0; s + 1 < KS; ++s) {
 #pragma unroll
                     for (int q = 0; q < FN; ++q) {
-                        column(s, q, cur, s + 1);
-                        if (ahead) slot_dma(nxt, t + S - 1, s * FN + q);
+                        column(s, q, sc, s + 1);
+                        if (ahead) slot_dma(sx, t + S - 1, s * FN + q);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -401,7 +423,7 @@ __device__ __forceinline__ void dma_mainloop(
                 if (ahead) issue(t + S - 1);
 #pragma unroll
                 for (int s = 0; s + 1 < KS; ++s) {
-                    read_all(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+                    read_all(sc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
                     mfma_all(fa[s & 1], fb[s & 1]);
                     sched_interleave<NMF, NRD, 0, 0>();
                     __builtin_amdgcn_sched_barrier(0);
@@ -414,10 +436,20 @@ __device__ __forceinline__ void dma_mainloop(
             __builtin_amdgcn_sched_barrier(0);
             // last k-step of tile t overlaps the first fragments of tile t+1 (on
             // the last tile this reads a stale stage whose values are never used)
-            read_all(smem + ((t + 1) % S) * STAGE, 0, fa[0], fb[0]);
+            read_all(sn, 0, fa[0], fb[0]);
             mfma_all(fa[1], fb[1]);
             sched_interleave<NMF, NRD, 0, 0>();
             __builtin_amdgcn_sched_barrier(0);
+        };
+        if constexpr (SPLIT) {
+            int t = 0;
+            for (; t + 1 < nkt; t += 2) {
+                tile(t, 0, 1);
+                tile(t + 1, 1, 0);
+            }
+            if (t < nkt) tile(t, 0, 1);
+        } else {
+            for (int t = 0; t < nkt; ++t) tile(t, t % S, (t + 1) % S);
         }
     }
     if (ktail > 0) {
@@ -432,22 +464,22 @@ __device__ __forceinline__ void dma_mainloop(
         {
             DmaStream<KCA, BM, BK, ESZ, NW> ta;
             ta.init(p.A, p.lda, m0, p.M, kt, wave, ln);
-            ta.load_tail(smem, ktail, wave, ln);
+            ta.load_tail(stA(0), ktail, wave, ln);
         }
         if constexpr (W12) {
             DmaStream<KCB, BNS, BK, ESZ, NW> tb, tb2;
             tb.init(p.B, p.ldb, n0 / 2, p.N / 2, kt, wave, ln);
-            tb.load_tail(smem + TA_::BYTES, ktail, wave, ln);
+            tb.load_tail(stB(0), ktail, wave, ln);
             tb2.init(p.B2, p.ldb, n0 / 2, p.N / 2, kt, wave, ln);
-            tb2.load_tail(smem + TA_::BYTES + TB_::BYTES, ktail, wave, ln);
+            tb2.load_tail(stB(0) + TB_::BYTES, ktail, wave, ln);
         } else {
             DmaStream<KCB, BNS, BK, ESZ, NW> tb;
             tb.init(p.B, p.ldb, n0, p.N, kt, wave, ln);
-            tb.load_tail(smem + TA_::BYTES, ktail, wave, ln);
+            tb.load_tail(stB(0), ktail, wave, ln);
         }
         __syncthreads();
         for (int s = 0; s < KS && s * D::KSTEP < ktail; ++s) {   // k-steps past K add 0
-            read_all(smem, s, fa[0], fb[0]);
+            read_all(0, s, fa[0], fb[0]);
             mfma_all(fa[0], fb[0]);
         }
     }
