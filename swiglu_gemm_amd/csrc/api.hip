@@ -479,11 +479,19 @@ int ex_cfg(int cfg, const Problem16& q, int64_t kps) {
 
 // Column split of a problem whose 256-row tiles take more than one round and
 // leave the last round at most half full: the chosen tile runs over the leading
-// columns that fill whole rounds and the 128 x 128 tile (two work-groups per CU)
-// over the remaining column strip -- two launches with disjoint outputs.  Measured
-// on MI355X: e4m3 4096 x 22016 x 4096 with 256 x 256 tiles (5.4 rounds) 394-423 us
-// in one launch, 375-378 us split at column 20480.  Not for split-K, batches, the
-// extra epilogue steps or a forced configuration.
+// columns that fill whole rounds and a smaller tile over the remaining column
+// strip -- two launches with disjoint outputs.  The strip takes the 128 x 128 tile
+// (two work-groups per CU); for e4m3 it takes the 4-stage 128 x 192 tile instead
+// when those tiles fit one round.  Measured on MI355X: e4m3 4096 x 22016 x 4096
+// with 256 x 256 tiles (5.4 rounds) 394-423 us in one launch, 375-378 us split at
+// column 20480; with the 128 x 192 strip (256 tiles, one per CU, instead of 384 of
+// 128 x 128) the GEMM 326 -> 322 us and the SwiGLU at M = 4096 319 -> 309 us
+// (alternating builds, bit-identical).  Not for split-K, batches, the extra
+// epilogue steps or a forced configuration.
+constexpr int kE4m3WideTail = 47;          // e4m3 dma 128x192x128, 4 stages, 4x2 waves
+static_assert(kCfg16[kE4m3WideTail].e4m3 == 1 && kCfg16[kE4m3WideTail].BM == 128 &&
+                  kCfg16[kE4m3WideTail].BN == 192 && kCfg16[kE4m3WideTail].S == 4,
+              "the e4m3 column-split strip tile");
 struct ColSplit {
     int64_t n1 = 0;      // columns of the first launch (0: no split)
     int cfg_tail = -1;
@@ -501,10 +509,16 @@ ColSplit plan_col_split(const Problem16& q, int cfg, int splits, int epi) {
     if (tm * tn <= kNumCU || rest == 0 || 2 * rest > kNumCU) return s;
     const int64_t strip = cdiv(rest, tm);                // column tiles moved to the tail
     if (strip >= tn) return s;
-    const int tail = q.esz == 1 ? 15 : 13;
-    const Cfg16& t = kCfg16[tail];
     Problem16 qt = q;
     qt.N = q.N - (tn - strip) * c.BN;
+    int tail = q.esz == 1 ? 15 : 13;
+    if (q.esz == 1) {
+        const Cfg16& w = kCfg16[kE4m3WideTail];
+        if (cdiv(q.M, w.BM) * cdiv(qt.N, w.BN) <= kNumCU &&
+            dma_ok(w, qt, split_len(q.K, 1, w.BK)))
+            tail = kE4m3WideTail;
+    }
+    const Cfg16& t = kCfg16[tail];
     if (!dma_ok(t, qt, split_len(q.K, 1, t.BK))) return s;
     if (cdiv(q.M, t.BM) * cdiv(qt.N, t.BN) > 2 * kNumCU) return s;   // one go, 2 per CU
     s.n1 = (tn - strip) * c.BN;

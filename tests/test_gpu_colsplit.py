@@ -1,7 +1,9 @@
 """The column split: a problem whose 256-row tiles take more than one round of the
 CUs and leave the last round at most half full runs as two launches -- the chosen
-tile over the leading columns that fill whole rounds, the 128 x 128 tile over the
-remaining column strip.  GEMM (B stored K x N and N x K, 16-bit and e4m3 operands,
+tile over the leading columns that fill whole rounds, a smaller tile over the
+remaining column strip (16-bit: 128 x 128; e4m3: 128 x 192, configuration 47, when
+its tiles fit one round, which they do here: 32 x 2 tiles over a 256-column strip,
+the second one ragged).  GEMM (B stored K x N and N x K, 16-bit and e4m3 operands,
 alpha and beta) and the fused SwiGLU against the fp64 oracle on every output (both
 launches and the seam between them), the routing itself, and no split under a
 forced configuration."""
@@ -21,6 +23,7 @@ pytestmark = pytest.mark.gpu
 # 16 x 33 = 528) or to 3/8 (bf16, 256 x 320 tiles: 32 x 27 = 864)
 SHAPES = {"bf16": (8192, 8448, 256), "e4m3": (4096, 8448, 256)}
 SEAM = {"bf16": 7680, "e4m3": 8192}     # first column of the tail launch
+TAIL = {"bf16": 13, "e4m3": 47}         # configuration of the tail launch
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -62,7 +65,7 @@ def run_gemm(dtype, tb, forced=None):
 @pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
 def test_gemm_column_split(dtype, tb):
     desc = run_gemm(dtype, tb)
-    assert "tail cfg=" in desc and "columns 0..%d," % SEAM[dtype] in desc, desc
+    assert ("tail cfg=%d " % TAIL[dtype]) in desc and "columns 0..%d," % SEAM[dtype] in desc, desc
 
 
 def test_forced_config_is_not_split():
@@ -84,7 +87,7 @@ def test_swiglu_column_split(dtype):
     sg.swiglu_gemm(A, W, Y, sa, sw)
     torch.cuda.synchronize()
     desc = sg.last_config()
-    assert "tail cfg=" in desc and "columns 0..%d," % SEAM[dtype] in desc, desc
+    assert ("tail cfg=%d " % TAIL[dtype]) in desc and "columns 0..%d," % SEAM[dtype] in desc, desc
     got = oracle.decode(from_dev(Y), "bf16")
     assert np.all(np.isfinite(got)), desc           # every output written
     ref = oracle.swiglu(M, N, K, pb["A"], Wf, dtype, sa, sw)
