@@ -149,7 +149,9 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(13, 1, 128, 128, 64, 2, 2, 4)    \
     X(24, 1, 256, 320, 64, 2, 4, 2)    \
     X(30, 1, 128, 128, 64, 5, 2, 4)    \
-    X(32, 1, 128, 256, 64, 3, 2, 4)
+    X(32, 1, 128, 256, 64, 3, 2, 4)    \
+    X(46, 1, 256, 192, 64, 2, 4, 2)    \
+    X(48, 1, 128, 192, 64, 4, 4, 2)
 
 #define SG_CONFIGS_E4M3_EX(X)          \
     X(14, 1, 256, 256, 128, 2, 4, 2)   \

@@ -134,6 +134,24 @@ def test_epilogue_e4m3_output(dtype, act):
     check_ex(dtype, "N", "N", 300, 512, 256, 410, act, "bf16", out8=True)
 
 
+EX16 = [2, 6, 10, 13, 24, 30, 32, 46, 48]     # 16-bit configurations with the extra steps
+
+
+@pytest.mark.parametrize("tr", ["NN", "NT", "TN", "TT"])
+@pytest.mark.parametrize("cfg", EX16)
+def test_epilogue_every_config(cfg, tr):
+    """Each 16-bit configuration compiled with the extra epilogue steps, forced, in
+    every transpose: bias (fp32) + GELU with beta on a ragged multi-tile shape whose
+    sizes are multiples of 8 (so every direct-to-LDS ring is eligible), against the
+    oracle."""
+    os.environ["SG_FORCE_CONFIG"] = "%d,1" % cfg
+    try:
+        check_ex("bf16", tr[0], tr[1], 296, 520, 256, 470 + cfg, "gelu", "f32", ld_mode="tight",
+                 expect="cfg=%d " % cfg)
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+
+
 @pytest.mark.parametrize("act", ["gelu", "silu"])
 def test_epilogue_other_paths(act):
     """Register-staged kernel (a leading dimension that is not a 16-byte multiple),
