@@ -461,13 +461,16 @@ int warm_grid(const Problem16& q, const Cfg16& c, bool tb, int epi, const Gemm16
 // nearest to cfg: the same kernel family and tile size where possible, else the
 // register-staged kernel (any shape); -1 for e4m3 without one (generic kernel).
 int ex_cfg(int cfg, const Problem16& q, int64_t kps) {
-    // the SG_CONFIGS_EX / SG_CONFIGS_E4M3_EX rows.  The 256 x 192 and 4-stage 128 x 192
-    // tiles, which the chooser takes where 256 columns would leave CUs idle, are among
-    // them: measured on MI355X with bias + GELU (bf16 2048 x 4864 x 896 36.6 -> 30.9
-    // us, fp16 4096 x 6144 x 4096 213 -> 191 us, bf16 8192 x 3072 x 4096 204 -> 180
-    // us, against their mapping to the 256 x 256 tile; bit-identical)
-    static const int k16[] = {2, 6, 10, 13, 24, 30, 32, 46, 48};
-    static const int k8[] = {14, 15, 16, 17, 33};
+    // the SG_CONFIGS_EX / SG_CONFIGS_E4M3_EX rows: every tile the chooser returns.
+    // Measured on MI355X with bias + GELU against the mapping these tiles had before
+    // they were compiled with the extra steps (bit-identical): 256 x 192 and 4-stage
+    // 128 x 192 instead of 256 x 256, bf16 2048 x 4864 x 896 36.6 -> 30.9 us, fp16
+    // 4096 x 6144 x 4096 213 -> 191 us, bf16 8192 x 3072 x 4096 204 -> 180 us; 64 x 128
+    // instead of 128 x 128, bf16 1024^3 13.9 -> 12.9 us; e4m3 128 x 192 instead of the
+    // 4-wave 128 x 256, 256 x 11008 x 4096 and 192 x 14336 x 4096 (B stored N x K)
+    // 47.7 -> 27.0 us.
+    static const int k16[] = {2, 6, 10, 13, 24, 30, 32, 46, 48, 44};
+    static const int k8[] = {14, 15, 16, 17, 33, 45, 47};
     const bool e4m3 = q.esz == 1;
     const int* list = e4m3 ? k8 : k16;
     const int n = e4m3 ? (int)(sizeof(k8) / sizeof(k8[0])) : (int)(sizeof(k16) / sizeof(k16[0]));

@@ -151,14 +151,17 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(30, 1, 128, 128, 64, 5, 2, 4)    \
     X(32, 1, 128, 256, 64, 3, 2, 4)    \
     X(46, 1, 256, 192, 64, 2, 4, 2)    \
-    X(48, 1, 128, 192, 64, 4, 4, 2)
+    X(48, 1, 128, 192, 64, 4, 4, 2)    \
+    X(44, 1, 64, 128, 64, 4, 1, 4)
 
 #define SG_CONFIGS_E4M3_EX(X)          \
     X(14, 1, 256, 256, 128, 2, 4, 2)   \
     X(15, 1, 128, 128, 128, 2, 2, 4)   \
     X(16, 1, 32, 256, 128, 4, 1, 4)    \
     X(17, 1, 32, 128, 128, 4, 1, 4)    \
-    X(33, 1, 128, 256, 128, 3, 2, 2)
+    X(33, 1, 128, 256, 128, 3, 2, 2)   \
+    X(45, 1, 128, 256, 128, 3, 2, 4)   \
+    X(47, 1, 128, 192, 128, 4, 4, 2)
 
 // the split-weight SwiGLU with Gate then Up (EPI_SWIGLU_SEQ, NN only)
 #define SG_CONFIGS_SEQ(X)              \

@@ -134,7 +134,8 @@ def test_epilogue_e4m3_output(dtype, act):
     check_ex(dtype, "N", "N", 300, 512, 256, 410, act, "bf16", out8=True)
 
 
-EX16 = [2, 6, 10, 13, 24, 30, 32, 46, 48]     # 16-bit configurations with the extra steps
+EX16 = [2, 6, 10, 13, 24, 30, 32, 44, 46, 48]     # configurations with the extra steps
+EX8 = [14, 15, 16, 17, 33, 45, 47]
 
 
 @pytest.mark.parametrize("tr", ["NN", "NT", "TN", "TT"])
@@ -147,6 +148,20 @@ def test_epilogue_every_config(cfg, tr):
     os.environ["SG_FORCE_CONFIG"] = "%d,1" % cfg
     try:
         check_ex("bf16", tr[0], tr[1], 296, 520, 256, 470 + cfg, "gelu", "f32", ld_mode="tight",
+                 expect="cfg=%d " % cfg)
+    finally:
+        os.environ.pop("SG_FORCE_CONFIG", None)
+
+
+@pytest.mark.parametrize("tb", ["N", "T"])
+@pytest.mark.parametrize("cfg", EX8)
+def test_epilogue_every_config_e4m3(cfg, tb):
+    """The same for each e4m3 configuration with the extra steps, B stored either way
+    (A untransposed: the 32-row tiles take a transposed A through the re-laid path):
+    bias (bf16) + GELU with beta, bf16 output, on a ragged shape of multiples of 16."""
+    os.environ["SG_FORCE_CONFIG"] = "%d,1" % cfg
+    try:
+        check_ex("e4m3", "N", tb, 304, 528, 256, 490 + cfg, "gelu", "bf16",
                  expect="cfg=%d " % cfg)
     finally:
         os.environ.pop("SG_FORCE_CONFIG", None)
