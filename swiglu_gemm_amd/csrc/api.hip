@@ -457,6 +457,22 @@ int warm_grid(const Problem16& q, const Cfg16& c, bool tb, int epi, const Gemm16
     return per_xcd <= kWarmMaxBytes ? kNumCU : 0;
 }
 
+// Whether a configuration is compiled with the extra epilogue steps (EPI_GEMM_EX).
+#define SG_IS(ID, DMA, BM, BN, BK, S, WM, WN) id == ID ||
+constexpr bool has_ex16(int id) { return SG_CONFIGS_EX(SG_IS) false; }
+constexpr bool has_ex8(int id) { return SG_CONFIGS_E4M3_EX(SG_IS) false; }
+#undef SG_IS
+// Every tile the 16-bit chooser weighs has them (a fused epilogue on a tile without
+// them ran on a neighbouring tile, up to 1.8x slower).  The e4m3 chooser returns 14,
+// 15, 16, 17, 45 and 47; the one-round 128 x 128 choice is 30.
+constexpr bool cands_have_ex() {
+    for (const Cand16& c : kCand16)
+        if (!has_ex16(c.id)) return false;
+    return has_ex16(30) && has_ex8(14) && has_ex8(15) && has_ex8(16) && has_ex8(17) &&
+           has_ex8(45) && has_ex8(47);
+}
+static_assert(cands_have_ex(), "a chosen tile lacks the fused-epilogue instances");
+
 // The configuration compiled with the extra epilogue steps (EPI_GEMM_EX) that is
 // nearest to cfg: the same kernel family and tile size where possible, else the
 // register-staged kernel (any shape); -1 for e4m3 without one (generic kernel).
@@ -469,13 +485,8 @@ int ex_cfg(int cfg, const Problem16& q, int64_t kps) {
     // instead of 128 x 128, bf16 1024^3 13.9 -> 12.9 us; e4m3 128 x 192 instead of the
     // 4-wave 128 x 256, 256 x 11008 x 4096 and 192 x 14336 x 4096 (B stored N x K)
     // 47.7 -> 27.0 us.
-    static const int k16[] = {2, 6, 10, 13, 24, 30, 32, 46, 48, 44};
-    static const int k8[] = {14, 15, 16, 17, 33, 45, 47};
+    if (q.esz == 1 ? has_ex8(cfg) : has_ex16(cfg)) return cfg;
     const bool e4m3 = q.esz == 1;
-    const int* list = e4m3 ? k8 : k16;
-    const int n = e4m3 ? (int)(sizeof(k8) / sizeof(k8[0])) : (int)(sizeof(k16) / sizeof(k16[0]));
-    for (int i = 0; i < n; ++i)
-        if (list[i] == cfg) return cfg;
     const Cfg16& c = kCfg16[cfg];
     int alt;
     if (e4m3) alt = c.BM >= 256 ? 14 : 33;

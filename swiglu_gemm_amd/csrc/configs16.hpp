@@ -184,4 +184,34 @@ constexpr bool dma_tile_ok(bool kc, int rows, int bk, int esz, int nwaves) {
     X(45, 1, 128, 256, 128, 3, 2, 4)   \
     X(47, 1, 128, 192, 128, 4, 4, 2)
 
+// Every row of the lists above is the kCfg16 row of its id.  The lists' DMA field
+// is the kernel family (0 register-staged, 1 direct ring, 4 producer waves); a
+// Gate-then-Up row's family 1 is kCfg16's dma 3.
+constexpr bool row_is(int id, int e4m3, int fam, int bm, int bn, int bk, int s, int wm, int wn,
+                      bool seq) {
+    return cfg_live(id) && kCfg16[id].e4m3 == e4m3 &&
+           kCfg16[id].dma == (seq && fam == 1 ? 3 : fam) && kCfg16[id].BM == bm &&
+           kCfg16[id].BN == bn && kCfg16[id].BK == bk && kCfg16[id].S == s &&
+           kCfg16[id].WM == wm && kCfg16[id].WN == wn;
+}
+#define SG_ROW16(ID, DMA, BM, BN, BK, S, WM, WN) \
+    static_assert(row_is(ID, 0, DMA, BM, BN, BK, S, WM, WN, false), "16-bit row " #ID);
+#define SG_ROW8(ID, DMA, BM, BN, BK, S, WM, WN) \
+    static_assert(row_is(ID, 1, DMA, BM, BN, BK, S, WM, WN, false), "e4m3 row " #ID);
+#define SG_ROW16_SEQ(ID, DMA, BM, BN, BK, S, WM, WN) \
+    static_assert(row_is(ID, 0, DMA, BM, BN, BK, S, WM, WN, true), "Gate-then-Up row " #ID);
+#define SG_ROW8_SEQ(ID, DMA, BM, BN, BK, S, WM, WN) \
+    static_assert(row_is(ID, 1, DMA, BM, BN, BK, S, WM, WN, true), "e4m3 Gate-then-Up row " #ID);
+SG_CONFIGS(SG_ROW16)
+SG_CONFIGS_SWEEP(SG_ROW16)
+SG_CONFIGS_EX(SG_ROW16)
+SG_CONFIGS_SEQ(SG_ROW16_SEQ)
+SG_CONFIGS_E4M3(SG_ROW8)
+SG_CONFIGS_E4M3_EX(SG_ROW8)
+SG_CONFIGS_E4M3_SEQ(SG_ROW8_SEQ)
+#undef SG_ROW16
+#undef SG_ROW8
+#undef SG_ROW16_SEQ
+#undef SG_ROW8_SEQ
+
 }  // namespace sg
