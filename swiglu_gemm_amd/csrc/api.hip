@@ -253,12 +253,17 @@ int pick_splits(const Cfg16& c, const Problem16& q) {
 // has 4 stages, the whole LDS: the loads of these short-K shapes run about as long
 // as the MFMAs, and a third tile in flight hides more of their latency (measured,
 // alternating builds: SwiGLU M = 512 16.6 -> 15.3 us, M = 640 17.9 -> 16.9 us, GEMM
-// 512 x 9728 x 896 19.9 -> 17.4 us against 3 stages; bit-identical).)
+// 512 x 9728 x 896 19.9 -> 17.4 us against 3 stages; bit-identical).)  The 256 x 320
+// and 256 x 256 rates were raised from 5.0 and 4.7 after every candidate was forced
+// on 46 shapes: the new rates change five decisions to 256 x 320 (fp16 and bf16
+// 4096 x 9216 x 4096 286 -> 263 and 272 -> 248 us, 6144^3 409 -> 382 and 403 -> 371
+// us, bf16 8192 x 14336 x 4096 758 -> 750 us) and one to 256 x 256 (fp16 6144 x 4096 x
+// 4096 205 -> 194 us), and none for the worse.
 struct Cand16 {
     int id;
     double tf_per_cu;
 };
-constexpr Cand16 kCand16[] = {{10, 4.7}, {24, 5.0}, {46, 4.6}, {13, 3.6},
+constexpr Cand16 kCand16[] = {{10, 4.8}, {24, 5.3}, {46, 4.6}, {13, 3.6},
                                {32, 3.6}, {48, 3.0}, {6, 3.4}, {44, 2.43}};
 constexpr double kTileOverheadUs = 3.0;   // pipeline fill + epilogue per tile
 constexpr double kSplitBytesPerUs = 4e6;  // fp32 partials: written, then read back
