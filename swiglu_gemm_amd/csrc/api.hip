@@ -189,6 +189,7 @@ struct Problem16 {
     int esz;              // operand element size (2: fp16/bf16, 1: e4m3)
     int64_t batch = 1;    // problems of a strided batch (one launch, gridDim.z)
     int64_t lda = 0, ldb = 0;   // leading dimensions (0: not known, no offset limit)
+    bool swiglu = false;        // the fused SwiGLU epilogue (N: fused width)
 };
 
 // The direct-to-LDS kernels address each lane's 16-byte chunk as a 32-bit offset from
@@ -265,6 +266,8 @@ struct Cand16 {
 };
 constexpr Cand16 kCand16[] = {{10, 4.8}, {24, 5.3}, {46, 4.6}, {13, 3.6},
                                {32, 3.6}, {48, 3.0}, {6, 3.4}, {44, 2.43}};
+// e4m3 above 256 rows (rates fitted to forced runs of every e4m3 candidate)
+constexpr Cand16 kCand8Wide[] = {{14, 10.9}, {45, 9.8}, {47, 10.0}};
 constexpr double kTileOverheadUs = 3.0;   // pipeline fill + epilogue per tile
 constexpr double kSplitBytesPerUs = 4e6;  // fp32 partials: written, then read back
 constexpr double kSplitLaunchUs = 5.0;    // the reduction kernel
@@ -292,21 +295,47 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
         splits = 0;
         if (e4m3) {
             // measured on MI355X (weights cold in HBM; these shapes are bound by how
-            // fast each CU pulls its operand tiles, so more busy CUs and waves win):
-            // 256x256 tiles once there are >= 2 full rounds of them, and above 256 rows
-            // while they fill between half and all of one round (SwiGLU, fused width
-            // 22016, K = 4096, M = 384, 512: 57, 59 us against 62, 72 us for 128x128);
-            // 32-row tiles while two work-groups per CU hold them all (GEMM 256 x 4096
-            // x 4096: 14.3 us against 24.8 us for 128x256 with split-K); above 128
-            // rows, 8-wave 128x256 tiles while they fit one round (SwiGLU M = 192, 256:
-            // 34, 36 us against 40, 39 us with 4 waves and 52 us with 32-row tiles),
-            // else 128x128; up to 128 rows, 32-row tiles: 128 wide while one work-group
-            // per CU holds them, else 256 wide if that is one round (SwiGLU M = 64: 27.6
-            // against 33.0 us with 344 work-groups of 32 x 128), else 128 wide
+            // fast each CU pulls its operand tiles, so more busy CUs and waves win).
+            // At any size, 32-row tiles while two work-groups per CU hold them all (GEMM
+            // 256 x 4096 x 4096: 14.3 us against 24.8 us for 128x256 with split-K).  Up
+            // to 256 rows otherwise (and for the fused SwiGLU up to 512): 256x256 tiles
+            // once there are >= 2 full rounds of them, and above 256 rows while they fill
+            // between half and all of one round (SwiGLU, fused width 22016, K = 4096, M =
+            // 384, 512: 57, 59 us against 62, 72 us for 128x128); above 128 rows, 8-wave 128x256 tiles while they fit one round
+            // (SwiGLU M = 192, 256: 34, 36 us against 40, 39 us with 4 waves and 52 us
+            // with 32-row tiles), else 128x128; up to 128 rows, 32-row tiles: 128 wide
+            // while one work-group per CU holds them, else 256 wide if that is one round
+            // (SwiGLU M = 64: 27.6 against 33.0 us with 344 work-groups of 32 x 128),
+            // else 128 wide.
+            //
+            // Above 256 rows, where 32-row tiles no longer fit two per CU, the cost model
+            // of the 16-bit tiles over the 256 x 256, 8-wave 128 x 256 and 128 x 192
+            // tiles (kCand8Wide).  Forcing every e4m3 candidate on 58 GEMM shapes (M =
+            // 384..4096, N = 4096..28672, K = 2048..8192) put the rules these rows had
+            // before at 1.032 and 1.077 of the per-shape best on two disjoint sets; the
+            // model, fitted on the first set, at 1.007 and 1.015 (e.g. 512 x 22016 x 4096
+            // 67.1 -> 51.2 us, 2048 x 14336 x 4096 120.4 -> 102.1 us).
             const int64_t big = cdiv(q.M, 256) * cdiv(q.N, 256);
             const int64_t mid = cdiv(q.M, 128) * cdiv(q.N, 256);
             const int64_t thin = cdiv(q.M, 32) * cdiv(q.N, 128);
-            if (big >= 2 * kNumCU || (q.M > 256 && big <= kNumCU && 2 * big > kNumCU))
+            // The fused SwiGLU up to 512 rows keeps the 256 x 256 tiles of the rule
+            // below: with its weights cold it ran M = 384, 512 (fused width 22016) in
+            // 56.3, 59.0 us on them against 59.0, 60.3 us on the 128 x 192 tiles the
+            // model picks (the GEMM of the same shape: 68.0 against 53.1 us).
+            const bool model = q.M > 256 && thin > 2 * kNumCU && !(q.swiglu && q.M <= 512);
+            if (model) {
+                double best = 0.0;
+                for (const Cand16& cand : kCand8Wide) {
+                    const Cfg16& c = kCfg16[cand.id];
+                    if (!dma_ok(c, q, split_len(q.K, 1, c.BK))) continue;
+                    const double t = est_us(c, q, 1, cand.tf_per_cu);
+                    if (cfg < 0 || t < best) {
+                        cfg = cand.id;
+                        best = t;
+                    }
+                }
+                if (cfg < 0) cfg = 14;       // none fits: the fallback below takes over
+            } else if (big >= 2 * kNumCU || (q.M > 256 && big <= kNumCU && 2 * big > kNumCU))
                 cfg = 14;
             else if (q.M > 128 && thin <= 2 * kNumCU)
                 cfg = 17;
@@ -559,6 +588,7 @@ hipError_t run16(bool ta, bool tb, int epi, Problem16 q, Gemm16Params p, void* o
                  float** ws_used) {
     if (!p.A || !p.B || !out) return hipErrorInvalidValue;           // never launch on NULL
     int cfg = 0, splits = 1;
+    q.swiglu = epi == EPI_SWIGLU;
     choose16(q, &cfg, &splits);
     if (cfg >= 0 && epi == EPI_GEMM_EX && splits <= 1)
         cfg = ex_cfg(cfg, q, split_len(q.K, 1, kCfg16[cfg].BK));
