@@ -352,7 +352,12 @@ void choose16(const Problem16& q, int* cfg_out, int* splits_out) {
             else if (cdiv(q.M, 32) * cdiv(q.N, 128) <= kNumCU)
                 cfg = 17;
             else
-                cfg = cdiv(q.M, 32) * cdiv(q.N, 256) <= kNumCU ? 16 : 17;
+                // 256 wide only for B stored K x N (the SwiGLU weight's layout): with B
+                // stored N x K the 32 x 128 tiles were faster on every shape measured (48
+                // to 128 rows, N = 11008..28672, K = 2048..8192: 3.6-28 %, e.g. 96 x 11008
+                // x 4096 17.0 -> 13.3 us); with K x N the 32 x 256 tiles (64 x 22016 x 4096
+                // 23.5 against 26.1 us, 128 x 14336 x 4096 19.2 against 22.0 us)
+                cfg = !q.tb && cdiv(q.M, 32) * cdiv(q.N, 256) <= kNumCU ? 16 : 17;
         } else {
             double best = 0.0;
             for (const Cand16& cand : kCand16) {
