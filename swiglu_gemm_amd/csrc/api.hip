@@ -907,7 +907,11 @@ hipError_t gemm_f32(bool ta, bool tb, int64_t M, int64_t N, int64_t K, float alp
 // ------------------------------------------------ split-weight SwiGLU (W1, W2)
 // Configurations that can run it (see w12_ok in launch16.hpp): 16-bit candidates
 // weighed with the same cost model as the interleaved kernel; e4m3 by rows.
-constexpr Cand16 kCandW12[] = {{10, 4.7}, {8, 4.7}, {32, 3.6}, {6, 3.4}};
+// (The 128 x 128 tile is the 64-deep 3-stage ring: against the 32-deep 4-stage one it
+// ran M = 128 and 256 (N = 4864, K = 896) in 13.1, 13.05 us instead of 17.0, 16.4 us,
+// 128 x 11008 x 4096 in 48.5 instead of 63.9 us, and as the column-split tail M = 2048
+// in 42.2 instead of 43.8 us.)
+constexpr Cand16 kCandW12[] = {{10, 4.7}, {8, 4.7}, {32, 3.6}, {7, 3.4}};
 // Rows from which the split-weight SwiGLU runs Gate then Up (Kernel-1).  Measured
 // on MI355X with the weights cold (bf16 K = 896, N = 4864, M = 128..8192; e4m3 K =
 // 4096, N = 11008, M = 1..4096) it was 1.15-1.9x slower than Gate and Up side by
@@ -965,7 +969,7 @@ ColSplit plan_w12_split(const Problem16& q_out, int cfg) {
     if (tm * tn <= kNumCU || rest == 0 || 2 * rest > kNumCU) return s;
     const int64_t strip = cdiv(rest, tm);
     if (strip >= tn) return s;
-    const int tail = q_out.esz == 1 ? 45 : 6;
+    const int tail = q_out.esz == 1 ? 45 : 7;
     const Cfg16& t = kCfg16[tail];
     Problem16 qt = q_out;
     qt.N = q_out.N - (tn - strip) * c.BN / 2;
