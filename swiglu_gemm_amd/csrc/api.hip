@@ -693,10 +693,15 @@ hipError_t try_decode(bool tb, int epi, const void* A, int64_t lda, const void* 
         // kernel streams the weight faster (measured on MI355X, weights cold: 14.2
         // vs 16.7 us for 1 x 4096 x 4096 bf16, 33.1 vs 41.2 us for 16 x 8192 x
         // 8192).  Where the large-tile path runs as one kernel it is the faster one
-        // (e4m3 SwiGLU 1 x 4096 x 2*11008: 19.3 vs 23.6 us).
+        // (e4m3 SwiGLU 1 x 4096 x 2*11008: 19.3 vs 23.6 us).  Not so for the e4m3
+        // split-weight SwiGLU, which cannot use that path's 32 x 128 tile (an odd
+        // number of fragments per wave) and ran 1, 16, 32 x 4096 x 2*11008 on 32 x 256
+        // tiles in 27.3, 28.1, 29.2 us against 25.2, 24.2, 25.6 us here; the 16-bit one
+        // keeps its tiles (bf16 1 x 896 x 2*4864: 11.7 us, 14.9 us here).
         int oc = -1, os = 1;
         choose16(Problem16{M, N, K, true, true, false, tb, esz}, &oc, &os);
-        if (oc >= 0 && os <= 1) return hipErrorNotSupported;
+        const bool w12_e4m3 = epi == EPI_SWIGLU_W12 && esz == 1;
+        if (!w12_e4m3 && oc >= 0 && os <= 1) return hipErrorNotSupported;
         cfg = choose_decode(epi);
     }
     if (ex.on) cfg = 5;                         // the tile compiled with the extra steps
